@@ -1,0 +1,285 @@
+/*
+ * Reference oracle for the quantized prefill GEMM path -- TEST INFRASTRUCTURE.
+ *
+ * Plain, slow, obviously correct CPU code in fp64.  Only the tests, the
+ * smoke check and the CPU-baseline leg of the benchmark may load it; the
+ * HIP library never does, and the two share no code, header or table.
+ *
+ * What it computes (the plain definition the method reaches up to rounding):
+ *   1. decode every weight of the canonical codec bytes exactly in fp64;
+ *   2. ref[m][n] = sum_k x[m][k] * w[n][k], k ascending, one fp64 accumulator
+ *      (Y = X * W^T with fp16 activations X [M,K] and weights W [N,K]);
+ *   3. for the fused gate/up projection: out = g / (1 + exp(-g)) * u, fp64.
+ *
+ * Sources on the pages (m4-prefill-engine):
+ *   - releases page, v0.3.0, "PrismML Q2_0 Ternary Codec": 128-weight block of
+ *     34 bytes (fp16 scale then 32 bytes of 2-bit codes), w = (q - 1) * d with
+ *     the reserved code q = 3 giving +2d.
+ *   - project index, Table B: block_q4_0 (GGUF Q4_0) and block_mlx_4bit weights.
+ *   - comparison page, section 2.2: SwiGLU is SiLU(Gate) x Up on one input X.
+ *   - releases page, v0.2 "Honest Verification Labeling": the check is a CPU
+ *     double-precision gold computation.
+ * Q4_0 w = (q - 8) * d over 32-weight blocks and MLX w = q * s + b over
+ * 64-weight groups are the formulas of the workloads this path is measured on.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - Q4_0 byte order: GGUF convention, fp16 d first, then byte j holds weight
+ *     j (low nibble) and weight j + 16 (high nibble).
+ *   - MLX4 codes: little-endian uint32 words of 8 codes, element 0 in the low
+ *     nibble; scales and biases are fp16; one group per 64 weights along K.
+ *   - Q2_0 code order: weight i sits in byte i / 4 of the code field at bit
+ *     2 * (i % 4); q = 3 is applied without clamping.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fopenmp -fPIC -shared -lm
+ * (no fast-math: every operation is a correctly rounded IEEE fp64 operation).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_Q4_0 1
+#define ORC_MLX4_G64 2
+#define ORC_Q2_0 3
+
+/* ---------------------------------------------------------------- fp16 --- */
+
+/* IEEE binary16 bit pattern -> exact fp64 value (sign, 5-bit exponent with
+ * bias 15, 10-bit fraction; exponent 0 is subnormal, 31 is Inf/NaN). */
+double orc_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);                 /* f * 2^-10 * 2^-14 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);     /* (1 + f/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* fp64 -> nearest binary16, ties to even, correctly rounded in one step
+ * (no detour through fp32, which would round twice).  Overflow gives +-Inf,
+ * NaN stays NaN. */
+uint16_t orc_f64_to_f16(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(x))
+        return 0x7E00;
+    if (isinf(a))
+        return sign | 0x7C00;
+    if (a == 0.0)
+        return sign;
+    int e2;
+    frexp(a, &e2);                 /* a = m * 2^e2, m in [0.5, 1) */
+    int e = e2 - 1;                /* a in [2^e, 2^(e+1)) */
+    if (e < -14)
+        e = -14;                   /* subnormal range: fixed quantum 2^-24 */
+    /* quantum of the binary16 grid around a is 2^(e-10) */
+    double scaled = ldexp(a, 10 - e);   /* exact: power-of-two scaling */
+    double fl = floor(scaled);
+    double rem = scaled - fl;           /* exact */
+    double q = fl;
+    if (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0))
+        q = fl + 1.0;
+    /* q * 2^(e-10) is the rounded magnitude; q in [1024, 2048] for normals,
+     * [0, 1024] for subnormals. */
+    double r = ldexp(q, e - 10);
+    if (r > 65504.0)               /* rounds past the largest finite value */
+        return sign | 0x7C00;
+    if (r < ldexp(1.0, -14)) {
+        /* subnormal (or rounded up to the smallest normal, q == 1024) */
+        uint16_t fbits = (uint16_t)q;      /* value = q * 2^-24 */
+        return sign | fbits;              /* q == 1024 encodes 2^-14 exactly */
+    }
+    int ee;
+    double mm = frexp(r, &ee);          /* r = mm * 2^ee, mm in [0.5,1) */
+    int exp16 = ee - 1 + 15;
+    uint16_t frac = (uint16_t)(ldexp(mm, 11) - 1024.0);
+    return sign | (uint16_t)(exp16 << 10) | frac;
+}
+
+void orc_f16_to_f64_array(const uint16_t *h, double *out, int64_t count)
+{
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = orc_f16_to_f64(h[i]);
+}
+
+void orc_f64_to_f16_array(const double *x, uint16_t *out, int64_t count)
+{
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = orc_f64_to_f16(x[i]);
+}
+
+static uint16_t rd_u16le(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+static uint32_t rd_u32le(const uint8_t *p)
+{
+    return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+}
+
+/* ------------------------------------------------------------ geometry --- */
+
+/* Weights per block and canonical bytes per block of a codec; 0 on error.
+ * Q2_0: 128 weights in 34 bytes = 2.125 bits per weight (releases page,
+ * v0.3.0).  MLX4-G64 has no interleaved block in canonical form; the value
+ * returned is the per-group byte budget (32 code bytes + fp16 s + fp16 b). */
+int orc_block_geometry(int codec, int64_t *weights, int64_t *bytes)
+{
+    switch (codec) {
+    case ORC_Q4_0:     *weights = 32;  *bytes = 18; return 1;
+    case ORC_MLX4_G64: *weights = 64;  *bytes = 36; return 1;
+    case ORC_Q2_0:     *weights = 128; *bytes = 34; return 1;
+    default: return 0;
+    }
+}
+
+/* -------------------------------------------------------------- decode --- */
+
+/* Q4_0: per 32-weight block, d = fp16 at bytes 0-1; weight j (0..15) is the
+ * low nibble of byte 2 + j, weight j + 16 the high nibble; w = (q - 8) * d.
+ * Exact in fp64 (a 5-bit integer times an 11-bit significand). */
+static void decode_q4_0_row(const uint8_t *row, int64_t k, double *w)
+{
+    for (int64_t b = 0; b < k / 32; ++b) {
+        const uint8_t *blk = row + b * 18;
+        double d = orc_f16_to_f64(rd_u16le(blk));
+        for (int j = 0; j < 16; ++j) {
+            int lo = blk[2 + j] & 0x0F;
+            int hi = blk[2 + j] >> 4;
+            w[b * 32 + j] = (double)(lo - 8) * d;
+            w[b * 32 + j + 16] = (double)(hi - 8) * d;
+        }
+    }
+}
+
+/* Q2_0: per 128-weight block (34 bytes), d = fp16 at bytes 0-1; weight i has
+ * q = (byte[2 + i/4] >> (2 * (i % 4))) & 3 and w = (q - 1) * d, so the four
+ * codes give -d, 0, +d and (reserved code 3) +2d.  Exact in fp64. */
+static void decode_q2_0_row(const uint8_t *row, int64_t k, double *w)
+{
+    for (int64_t b = 0; b < k / 128; ++b) {
+        const uint8_t *blk = row + b * 34;
+        double d = orc_f16_to_f64(rd_u16le(blk));
+        for (int i = 0; i < 128; ++i) {
+            int q = (blk[2 + i / 4] >> (2 * (i % 4))) & 3;
+            w[b * 128 + i] = (double)(q - 1) * d;
+        }
+    }
+}
+
+/* MLX4-G64 row n: q = (word[n][k/8] >> 4*(k%8)) & 15, g = k / 64,
+ * w = q * s[n][g] + b[n][g].  Exact in fp64: q*s has at most 15 significant
+ * bits and the sum of two fp16-derived values spans far fewer than 53. */
+static void decode_mlx4_row(const uint8_t *codes, const uint8_t *scales,
+                            const uint8_t *biases, int64_t n_idx, int64_t k,
+                            double *w)
+{
+    const uint8_t *crow = codes + n_idx * (k / 2);
+    const uint8_t *srow = scales + n_idx * (k / 64) * 2;
+    const uint8_t *brow = biases + n_idx * (k / 64) * 2;
+    for (int64_t kk = 0; kk < k; ++kk) {
+        uint32_t word = rd_u32le(crow + (kk / 8) * 4);
+        int q = (int)((word >> (4 * (kk % 8))) & 0xF);
+        double s = orc_f16_to_f64(rd_u16le(srow + (kk / 64) * 2));
+        double b = orc_f16_to_f64(rd_u16le(brow + (kk / 64) * 2));
+        w[kk] = (double)q * s + b;
+    }
+}
+
+/* Decode rows [row0, row0 + nrows) of an [n, k] weight matrix held in the
+ * canonical bytes `canon` into w[nrows][k].  The MLX stream is codes
+ * (n*k/2 bytes), then scales (n*k/64 fp16), then biases (same).
+ * Returns 0 on success, -1 on a bad codec or shape. */
+int orc_decode_rows(int codec, const uint8_t *canon, int64_t n, int64_t k,
+                    int64_t row0, int64_t nrows, double *w)
+{
+    int64_t bw, bb;
+    if (!orc_block_geometry(codec, &bw, &bb) || k <= 0 || k % bw || row0 < 0 ||
+        nrows < 0 || row0 + nrows > n)
+        return -1;
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t nn = row0 + r;
+        double *wr = w + r * k;
+        if (codec == ORC_Q4_0)
+            decode_q4_0_row(canon + nn * (k / 32) * 18, k, wr);
+        else if (codec == ORC_Q2_0)
+            decode_q2_0_row(canon + nn * (k / 128) * 34, k, wr);
+        else {
+            const uint8_t *codes = canon;
+            const uint8_t *scales = canon + n * (k / 2);
+            const uint8_t *biases = scales + n * (k / 64) * 2;
+            decode_mlx4_row(codes, scales, biases, nn, k, wr);
+        }
+    }
+    return 0;
+}
+
+/* fp16 image of the decoded weights: each exact fp64 weight rounded once to
+ * binary16 (nearest, ties to even).  This is the value a kernel must feed to
+ * an fp16 matrix unit for its dequantization to be called exact. */
+int orc_dequant_f16_rows(int codec, const uint8_t *canon, int64_t n, int64_t k,
+                         int64_t row0, int64_t nrows, double *scratch,
+                         uint16_t *out)
+{
+    int rc = orc_decode_rows(codec, canon, n, k, row0, nrows, scratch);
+    if (rc)
+        return rc;
+    orc_f64_to_f16_array(scratch, out, nrows * k);
+    return 0;
+}
+
+/* -------------------------------------------------------------- matmul --- */
+
+/* ref[i][j] = sum_{kk=0}^{k-1} x[i][kk] * w[j][kk], where x holds fp16 bit
+ * patterns with row stride ldx and w is the exact fp64 decode [n][k].  Naive
+ * triple loop: k ascending into a single fp64 accumulator per output.  The
+ * outer loop over rows is split across threads; no output's order changes. */
+void orc_matmul_xwt(const uint16_t *x, int64_t ldx, const double *w, int64_t m,
+                    int64_t n, int64_t k, double *ref, int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < m; ++i) {
+        double *xr = (double *)malloc((size_t)(k > 0 ? k : 1) * sizeof(double));
+        for (int64_t kk = 0; kk < k; ++kk)
+            xr[kk] = orc_f16_to_f64(x[i * ldx + kk]);
+        for (int64_t j = 0; j < n; ++j) {
+            const double *wr = w + j * k;
+            double acc = 0.0;
+            for (int64_t kk = 0; kk < k; ++kk)
+                acc += xr[kk] * wr[kk];
+            ref[i * n + j] = acc;
+        }
+        free(xr);
+    }
+}
+
+/* SiLU(g) * u = g / (1 + exp(-g)) * u, elementwise in fp64 (comparison page
+ * section 2.2: the activation applied to the gate projection, times up). */
+void orc_swiglu(const double *g, const double *u, double *out, int64_t count)
+{
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

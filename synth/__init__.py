@@ -1,0 +1,186 @@
+"""Seeded synthetic inputs for the quantized prefill GEMM path.
+
+This module only draws random numbers and lays them out in the canonical
+byte formats of the three weight codecs.  It performs no dequantization and
+no products: decoding and contraction belong to the oracle (``oracle/``) and
+to the HIP library, which share nothing but these inputs.
+
+Canonical byte formats (the input contract both sides read):
+
+* Q4_0 (GGUF block_q4_0, named on the project index page, Table B): blocks of
+  32 weights along K, 18 bytes each: little-endian fp16 scale ``d`` in bytes
+  0-1, then 16 bytes where byte ``j`` carries weight ``j`` in its low nibble
+  and weight ``j + 16`` in its high nibble.  Weight value ``(q - 8) * d``.
+* MLX4-G64 (MLX-style 4-bit affine, group 64 along K): three consecutive
+  arrays: codes as little-endian uint32 words ``[N, K/8]`` holding 8 codes,
+  element 0 in the low 4 bits; then fp16 scales ``[N, K/64]``; then fp16
+  biases ``[N, K/64]``.  Weight value ``q * s + b``.
+* Q2_0 (PrismML block_prism_q2_0, releases page, v0.3.0 "PrismML Q2_0
+  Ternary Codec"): blocks of 128 weights, 34 bytes: fp16 ``d`` in bytes 0-1,
+  then 32 bytes of 2-bit codes, weight ``i`` in byte ``2 + i // 4`` at bit
+  ``2 * (i % 4)``.  Weight value ``(q - 1) * d``.
+
+Distributions and shapes follow the five workloads of the method: fp16
+activations ~N(0,1); Q4_0 scales ~U(0.005, 0.02) with codes ~U{0..15}; MLX
+scales ~U(0.002, 0.01), biases ~N(0, 0.02), codes ~U{0..15}; Q2_0 scales
+~U(0.01, 0.05) with P(q=0,1,2,3) = 0.30, 0.35, 0.30, 0.05.
+
+Random streams: numpy PCG64 seeded from ``SeedSequence([seed, tensor_id])``
+so every tensor of every workload has its own reproducible stream.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+CODEC_Q4_0 = 1
+CODEC_MLX4_G64 = 2
+CODEC_Q2_0 = 3
+
+CODEC_NAMES = {CODEC_Q4_0: "q4_0", CODEC_MLX4_G64: "mlx4_g64", CODEC_Q2_0: "q2_0"}
+# weights per block (scale group) along K
+BLOCK = {CODEC_Q4_0: 32, CODEC_MLX4_G64: 64, CODEC_Q2_0: 128}
+
+BASE_SEED = 0x51C0DEC0
+
+# tensor ids inside one workload seed
+T_X, T_W, T_WG, T_WU = 1, 2, 3, 4
+
+
+def _rng(seed: int, tensor_id: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed & 0xFFFFFFFF, tensor_id])))
+
+
+def canonical_bytes(codec: int, n: int, k: int) -> int:
+    """Size in bytes of the canonical encoding of an [n, k] weight matrix."""
+    b = BLOCK[codec]
+    if k % b:
+        raise ValueError(f"K={k} is not a multiple of the {CODEC_NAMES[codec]} block {b}")
+    if codec == CODEC_Q4_0:
+        return n * (k // 32) * 18
+    if codec == CODEC_MLX4_G64:
+        return n * (k // 2) + 2 * (n * (k // 64) * 2)
+    if codec == CODEC_Q2_0:
+        return n * (k // 128) * 34
+    raise ValueError(codec)
+
+
+def fp16_uniform(rng: np.random.Generator, lo: float, hi: float, size) -> np.ndarray:
+    return (lo + (hi - lo) * rng.random(size)).astype(np.float16)
+
+
+def gen_x(m: int, k: int, seed: int, tensor_id: int = T_X) -> np.ndarray:
+    """fp16 activations [m, k] drawn from N(0, 1) and rounded to fp16."""
+    return _rng(seed, tensor_id).standard_normal((m, k)).astype(np.float16)
+
+
+def encode_q4_0(codes: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Lay out codes [n, k] (uint8 0..15) and fp16 scales [n, k/32] as Q4_0 blocks."""
+    n, k = codes.shape
+    nb = k // 32
+    q = codes.reshape(n, nb, 32).astype(np.uint8)
+    out = np.empty((n, nb, 18), dtype=np.uint8)
+    out[:, :, 0:2] = d.astype("<f2").reshape(n, nb, 1).view(np.uint8).reshape(n, nb, 2)
+    out[:, :, 2:18] = q[:, :, 0:16] | (q[:, :, 16:32] << 4)
+    return out.reshape(-1)
+
+
+def encode_mlx4(codes: np.ndarray, s: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Lay out codes [n, k] (0..15), fp16 scales and biases [n, k/64] in MLX order."""
+    n, k = codes.shape
+    q = codes.reshape(n, k // 8, 8).astype(np.uint32)
+    words = np.zeros((n, k // 8), dtype=np.uint32)
+    for e in range(8):
+        words |= q[:, :, e] << np.uint32(4 * e)
+    parts = [words.astype("<u4").view(np.uint8).reshape(-1),
+             s.astype("<f2").view(np.uint8).reshape(-1),
+             b.astype("<f2").view(np.uint8).reshape(-1)]
+    return np.concatenate(parts)
+
+
+def encode_q2_0(codes: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Lay out codes [n, k] (0..3) and fp16 scales [n, k/128] as Q2_0 blocks."""
+    n, k = codes.shape
+    nb = k // 128
+    q = codes.reshape(n, nb, 32, 4).astype(np.uint8)
+    out = np.empty((n, nb, 34), dtype=np.uint8)
+    out[:, :, 0:2] = d.astype("<f2").reshape(n, nb, 1).view(np.uint8).reshape(n, nb, 2)
+    out[:, :, 2:34] = q[..., 0] | (q[..., 1] << 2) | (q[..., 2] << 4) | (q[..., 3] << 6)
+    return out.reshape(-1)
+
+
+def gen_q4_0(n: int, k: int, seed: int, tensor_id: int = T_W,
+             d_range=(0.005, 0.02)) -> np.ndarray:
+    rng = _rng(seed, tensor_id)
+    codes = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
+    d = fp16_uniform(rng, d_range[0], d_range[1], (n, k // 32))
+    return encode_q4_0(codes, d)
+
+
+def gen_mlx4(n: int, k: int, seed: int, tensor_id: int = T_W,
+             s_range=(0.002, 0.01), b_sigma=0.02) -> np.ndarray:
+    rng = _rng(seed, tensor_id)
+    codes = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
+    s = fp16_uniform(rng, s_range[0], s_range[1], (n, k // 64))
+    b = (b_sigma * rng.standard_normal((n, k // 64))).astype(np.float16)
+    return encode_mlx4(codes, s, b)
+
+
+Q2_0_PROBS = (0.30, 0.35, 0.30, 0.05)
+
+
+def gen_q2_0(n: int, k: int, seed: int, tensor_id: int = T_W,
+             d_range=(0.01, 0.05), probs=Q2_0_PROBS) -> np.ndarray:
+    rng = _rng(seed, tensor_id)
+    u = rng.random((n, k))
+    edges = np.cumsum(np.asarray(probs, dtype=np.float64))[:-1]
+    codes = np.searchsorted(edges, u, side="right").astype(np.uint8)
+    d = fp16_uniform(rng, d_range[0], d_range[1], (n, k // 128))
+    return encode_q2_0(codes, d)
+
+
+GEN = {CODEC_Q4_0: gen_q4_0, CODEC_MLX4_G64: gen_mlx4, CODEC_Q2_0: gen_q2_0}
+
+
+def gen_weight(codec: int, n: int, k: int, seed: int, tensor_id: int = T_W) -> np.ndarray:
+    return GEN[codec](n, k, seed, tensor_id)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One of the five workloads: shapes, codec and which entry point runs it."""
+    name: str
+    op: str          # "prefill" | "swiglu" | "gemv"
+    codec: int
+    m: int
+    k: int
+    n: int
+    seed: int
+
+    def x(self) -> np.ndarray:
+        return gen_x(self.m, self.k, self.seed)
+
+    def weights(self):
+        if self.op == "swiglu":
+            return (gen_weight(self.codec, self.n, self.k, self.seed, T_WG),
+                    gen_weight(self.codec, self.n, self.k, self.seed, T_WU))
+        return (gen_weight(self.codec, self.n, self.k, self.seed, T_W),)
+
+    def flops(self) -> int:
+        mats = 2 if self.op == "swiglu" else 1
+        return 2 * self.m * self.n * self.k * mats
+
+    def algorithmic_bytes(self) -> int:
+        mats = 2 if self.op == "swiglu" else 1
+        return mats * canonical_bytes(self.codec, self.n, self.k) + 2 * self.m * self.k + 2 * self.m * self.n
+
+
+WORKLOADS = {
+    "q4_0_tiny_16x256x256": Workload("q4_0_tiny_16x256x256", "prefill", CODEC_Q4_0, 16, 256, 256, BASE_SEED + 1),
+    "q4_0_prefill_2048x2048x8192": Workload("q4_0_prefill_2048x2048x8192", "prefill", CODEC_Q4_0, 2048, 2048, 8192, BASE_SEED + 2),
+    "mlx4_swiglu_2048x4096x14336": Workload("mlx4_swiglu_2048x4096x14336", "swiglu", CODEC_MLX4_G64, 2048, 4096, 14336, BASE_SEED + 3),
+    "q2_0_prefill_2048x4096x4096": Workload("q2_0_prefill_2048x4096x4096", "prefill", CODEC_Q2_0, 2048, 4096, 4096, BASE_SEED + 4),
+    "q4_0_gemv_1x4096x14336": Workload("q4_0_gemv_1x4096x14336", "gemv", CODEC_Q4_0, 1, 4096, 14336, BASE_SEED + 5),
+    "q4_0_gemv_64x4096x14336": Workload("q4_0_gemv_64x4096x14336", "gemv", CODEC_Q4_0, 64, 4096, 14336, BASE_SEED + 5),
+}

@@ -1,0 +1,120 @@
+"""Pins for the oracle's exact codec decode.
+
+* Hand-worked fixtures (tests/golden/*.txt): byte strings whose weights follow
+  from the formulas on the pages by hand -- Q2_0 w = (q - 1) d with q = 3 -> +2d
+  in 34-byte, 128-weight blocks; Q4_0 w = (q - 8) d in 18-byte, 32-weight
+  blocks; MLX w = q s + b per 64-weight group.  They fix the offsets, signs,
+  nibble / bit order, block strides and row strides.
+* Geometry printed on the pages: Q2_0 is 2.125 bits per weight.
+* Closed forms: MLX q = 0 gives the bias bit for bit; the fp16 image of each
+  weight equals numpy's correctly rounded conversion of the exact value.
+* The seeded generator's encoders agree with the oracle's reading of the
+  canonical bytes (so GPU parity inputs mean what the fixtures say).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from golden_io import all_cases
+
+CASES = all_cases()
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_golden_decode(case):
+    canon = np.array(case["bytes"], dtype=np.uint8)
+    assert canon.size == synth.canonical_bytes(case["codec"], case["n"], case["k"])
+    w = oracle.decode(case["codec"], canon, case["n"], case["k"])
+    want = np.array(case["expect"], dtype=np.float64).reshape(case["n"], case["k"])
+    assert np.array_equal(w, want)
+
+
+def test_q2_0_bits_per_weight_printed_on_page():
+    weights, nbytes = oracle.block_geometry(oracle.Q2_0)
+    assert (weights, nbytes) == (128, 34)
+    assert nbytes * 8 / weights == 2.125
+
+
+def test_q4_0_geometry():
+    assert oracle.block_geometry(oracle.Q4_0) == (32, 18)
+
+
+def test_decode_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        oracle.decode(oracle.Q4_0, np.zeros(18, np.uint8), 1, 48)
+    with pytest.raises(ValueError):
+        oracle.decode(7, np.zeros(18, np.uint8), 1, 32)
+
+
+def test_mlx_zero_code_returns_bias_bits():
+    rng = np.random.default_rng(7)
+    n, k = 8, 256
+    codes = np.zeros((n, k), np.uint8)
+    s = rng.uniform(0.002, 0.01, (n, k // 64)).astype(np.float16)
+    b = (0.02 * rng.standard_normal((n, k // 64))).astype(np.float16)
+    b[0, 0] = np.float16(2.0 ** -20)     # subnormal bias survives
+    canon = synth.encode_mlx4(codes, s, b)
+    bits = oracle.dequant_f16_bits(oracle.MLX4_G64, canon, n, k)
+    want = np.repeat(b.view(np.uint16), 64, axis=1)
+    assert np.array_equal(bits, want)
+
+
+def _random_canon(codec, n, k, seed):
+    return synth.gen_weight(codec, n, k, seed)
+
+
+@pytest.mark.parametrize("codec", [1, 2, 3])
+def test_dequant_f16_matches_numpy_rounding(codec):
+    n, k = 16, 512
+    canon = _random_canon(codec, n, k, 99)
+    w = oracle.decode(codec, canon, n, k)
+    bits = oracle.dequant_f16_bits(codec, canon, n, k)
+    assert np.array_equal(bits, w.astype(np.float16).view(np.uint16))
+
+
+def test_generator_q4_0_encoding_matches_decode():
+    rng = np.random.default_rng(3)
+    n, k = 5, 96
+    codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    d = rng.uniform(0.005, 0.02, (n, k // 32)).astype(np.float16)
+    w = oracle.decode(1, synth.encode_q4_0(codes, d), n, k)
+    want = (codes.astype(np.float64) - 8) * np.repeat(d.astype(np.float64), 32, axis=1)
+    assert np.array_equal(w, want)
+
+
+def test_generator_mlx4_encoding_matches_decode():
+    rng = np.random.default_rng(4)
+    n, k = 3, 192
+    codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    s = rng.uniform(0.002, 0.01, (n, k // 64)).astype(np.float16)
+    b = (0.02 * rng.standard_normal((n, k // 64))).astype(np.float16)
+    w = oracle.decode(2, synth.encode_mlx4(codes, s, b), n, k)
+    want = codes * np.repeat(s.astype(np.float64), 64, axis=1) + np.repeat(b.astype(np.float64), 64, axis=1)
+    assert np.array_equal(w, want)
+
+
+def test_generator_q2_0_encoding_matches_decode():
+    rng = np.random.default_rng(5)
+    n, k = 4, 256
+    codes = rng.integers(0, 4, (n, k)).astype(np.uint8)
+    d = rng.uniform(0.01, 0.05, (n, k // 128)).astype(np.float16)
+    w = oracle.decode(3, synth.encode_q2_0(codes, d), n, k)
+    want = (codes.astype(np.float64) - 1) * np.repeat(d.astype(np.float64), 128, axis=1)
+    assert np.array_equal(w, want)
+
+
+def test_generator_q2_0_code_frequencies():
+    canon = synth.gen_q2_0(256, 1024, 11)
+    blk = canon.reshape(-1, 34)[:, 2:]
+    q = np.stack([(blk >> (2 * j)) & 3 for j in range(4)], axis=-1).reshape(-1)
+    freq = np.bincount(q, minlength=4) / q.size
+    assert np.allclose(freq, synth.Q2_0_PROBS, atol=0.005)
+
+
+def test_generator_is_deterministic():
+    a = synth.gen_q4_0(8, 64, 123)
+    b = synth.gen_q4_0(8, 64, 123)
+    c = synth.gen_q4_0(8, 64, 124)
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
+    assert np.array_equal(synth.gen_x(4, 64, 1), synth.gen_x(4, 64, 1))
