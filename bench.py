@@ -1,0 +1,236 @@
+"""Benchmark of the quantized prefill GEMM path on one MI355X.
+
+One step = one launch of the hot path over the measured workload, with inputs
+already resident in HBM.  The headline workload is the 1B-shape MLP
+up-projection prefill (Q4_0 weights [8192, 2048], X fp16 [2048, 2048]); the
+line reports TFLOP/s (2*M*N*K per second) with its fraction of the fp16 dense
+MFMA peak.  The other workloads (MLX4 fused SwiGLU, Q2_0 GEMM, M=1 / M=64
+GEMV) are timed the same way under "secondary", each with its own roofline.
+
+Cold caches: every timed launch uses one of R rotated copies of weights, X and
+Y (R copies together exceed the 256 MB Infinity Cache), in the spirit of the
+pages' cache flush before every measured run.  Timing: torch.cuda.Event on the
+stream the kernels are launched on, bracketing all K launches, after W warmup
+launches; ms_per_step is the mean launch duration.
+
+cpu_baseline: the fp64 oracle (tests' reference implementation) timed on a
+bounded sample of the same workload -- the first rows of X against all of W --
+on the host's cores; the GPU output is checked against it on the same sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       [--no-cpu] [--no-secondary] [--rotate R]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+MALL_BYTES = 256 << 20
+HEADLINE = "q4_0_prefill_2048x2048x8192"
+SECONDARY = ["mlx4_swiglu_2048x4096x14336", "q2_0_prefill_2048x4096x4096",
+             "q4_0_gemv_1x4096x14336", "q4_0_gemv_64x4096x14336"]
+KERNEL_SOURCES = ["gemm.hip", "gemv.hip", "unpack.h", "planar.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "quantized_prefill_gemm_codec_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def bound_of(wl) -> str:
+    return "hbm" if wl.op == "gemv" else "mfma"
+
+
+class Prepared:
+    """R rotated device copies of one workload's packed weights, X and Y."""
+
+    def __init__(self, torch, qg, wl, rotate=None):
+        self.wl = wl
+        x = wl.x()
+        self.x_host = x
+        self.canon = wl.weights()
+        planes = [qg.qg_pack_host(wl.codec, wl.n, wl.k, c) for c in self.canon]
+        per_set = sum(qs.size + sc.size for qs, sc in planes) + x.nbytes + 2 * wl.m * wl.n
+        if rotate is None:
+            rotate = max(2, min(16, -(-(MALL_BYTES + (32 << 20)) // per_set) + 1))
+        self.rotate = rotate
+        self.sets = []
+        for _ in range(rotate):
+            ws = [qg.QWeight(wl.codec, wl.n, wl.k, torch.from_numpy(qs).cuda(), torch.from_numpy(sc).cuda())
+                  for qs, sc in planes]
+            xd = torch.from_numpy(x).cuda()
+            ldy = 8 * ((wl.n + 7) // 8)
+            y = torch.empty((wl.m, ldy), dtype=torch.float16, device="cuda")
+            self.sets.append((ws, xd, y))
+        self.qg = qg
+
+    def launch(self, i):
+        ws, xd, y = self.sets[i % self.rotate]
+        qg, wl = self.qg, self.wl
+        out = y[:, :wl.n]
+        if wl.op == "swiglu":
+            qg.qgemm_swiglu(ws[0], ws[1], xd, out=out)
+        elif wl.op == "gemv":
+            qg.qgemv_decode(ws[0], xd, out=out)
+        else:
+            qg.qgemm_prefill(ws[0], xd, out=out)
+        return out
+
+
+def time_launches(torch, prep, steps, warmup):
+    for i in range(warmup):
+        prep.launch(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        prep.launch(warmup + i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def roofline(wl, ms, traffic=None):
+    if bound_of(wl) == "hbm":
+        achieved = wl.algorithmic_bytes() / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+    achieved = wl.flops() / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": traffic}
+
+
+def load_traffic(name):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(torch, prep, target_s=12.0):
+    """Oracle timed on the first rows of X against all of W; GPU checked on them."""
+    import oracle
+    wl = prep.wl
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count() or 1
+    per_row_flops = 2 * wl.n * wl.k * (2 if wl.op == "swiglu" else 1)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        if wl.op == "swiglu":
+            ref = oracle.swiglu_ref(wl.codec, prep.canon[0], prep.canon[1], wl.n, wl.k, prep.x_host[:rows],
+                                    threads=threads)
+        else:
+            ref = oracle.gemm_ref(wl.codec, prep.canon[0], wl.n, wl.k, prep.x_host[:rows], threads=threads)
+        return ref, time.perf_counter() - t0
+
+    probe = min(wl.m, max(threads, 16))
+    _, dt = run(probe)
+    rows = int(min(wl.m, max(probe, probe * target_s / max(dt, 1e-3))))
+    rows = max(1, rows)
+    ref, dt = run(rows)
+    y = prep.launch(0)
+    torch.cuda.synchronize()
+    yh = y[:rows].cpu().numpy().astype(np.float64)
+    finite = bool(np.all(np.isfinite(yh)))
+    err = float(np.max(np.abs(yh - ref)) / np.sqrt(np.mean(ref ** 2)))
+    base = {"value": round(per_row_flops * rows / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{rows} of {wl.m} rows of X against all {wl.n} rows of W (K={wl.k}), "
+                      f"exact fp64 decode + naive k-ascending fp64 loops, {dt:.1f} s"}
+    parity = {"sample_rows": rows, "max_abs_err_over_rms": err, "tol": 1e-2, "finite": finite,
+              "ok": bool(finite and err <= 1e-2)}
+    return base, parity
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE, choices=list(synth.WORKLOADS))
+    ap.add_argument("--rotate", type=int, default=None)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU layout of this path is a design note, not a run", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_prefill_gemm_codec_amd as qg
+    if not os.path.exists(qg.LIB_PATH):
+        from quantized_prefill_gemm_codec_amd import build as qbuild
+        qbuild.build()
+    if not torch.cuda.is_available():
+        print("no HIP device visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    wl = synth.WORKLOADS[args.workload]
+    prep = Prepared(torch, qg, wl, args.rotate)
+    print(f"# prepared {wl.name}: rotate={prep.rotate}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    ms = time_launches(torch, prep, args.steps, args.warmup)
+    print(f"# timed {wl.name}: {ms * 1e3:.1f} us/launch", file=sys.stderr, flush=True)
+
+    unit = "TFLOP/s" if bound_of(wl) == "mfma" else "GB/s"
+    value = wl.flops() / (ms * 1e-3) / 1e12 if unit == "TFLOP/s" else wl.algorithmic_bytes() / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": "quant GEMM TFLOPS at M=2048 (% fp16 MFMA peak); M=1 GEMV HBM GB/s",
+        "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": wl.name, "codec": synth.CODEC_NAMES[wl.codec], "m": wl.m, "n": wl.n, "k": wl.k,
+                   "op": wl.op, "rotate": prep.rotate},
+        "roofline": roofline(wl, ms, load_traffic(wl.name)),
+    }
+    if not args.no_secondary:
+        sec = {}
+        for name in SECONDARY:
+            if name == wl.name:
+                continue
+            w2 = synth.WORKLOADS[name]
+            p2 = Prepared(torch, qg, w2)
+            ms2 = time_launches(torch, p2, max(10, args.steps), args.warmup)
+            r2 = roofline(w2, ms2, load_traffic(name))
+            sec[name] = {"us_per_launch": round(ms2 * 1e3, 2), "tflops": round(w2.flops() / (ms2 * 1e-3) / 1e12, 2),
+                         "gbs": round(w2.algorithmic_bytes() / (ms2 * 1e-3) / 1e9, 1), "roofline": r2,
+                         "rotate": p2.rotate}
+            print(f"# timed {name}: {ms2 * 1e3:.1f} us/launch", file=sys.stderr, flush=True)
+            del p2
+            torch.cuda.empty_cache()
+        rec["secondary"] = sec
+    if not args.no_cpu:
+        base, parity = cpu_baseline(torch, prep)
+        rec["cpu_baseline"] = base
+        rec["parity"] = parity
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

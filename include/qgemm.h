@@ -1,0 +1,149 @@
+/*
+ * qgemm.h -- C-ABI of the MI355X (gfx950) quantized prefill GEMM library.
+ *
+ * Y = X * W^T where X holds fp16 activations [M, K] and W is a block-quantized
+ * weight matrix [N, K] whose codes are dequantized inside the kernels and
+ * contracted on the fp16 matrix cores with fp32 accumulation.
+ *
+ * Sources (m4-prefill-engine pages):
+ *  - comparison page, section 2.1: quantized GEMM on matrix units fed by
+ *    in-kernel dequantization; section 2.2: fused SiLU(Gate) x Up with X loaded
+ *    once and the gate / up products kept on chip; section 4: planar 16-byte
+ *    aligned code arrays read with 128-bit loads.
+ *  - releases page, v0.3.0: a C-ABI bridge over caller-owned device buffers;
+ *    a quantized linear layer that dispatches GEMV (M = 1) or GEMM (M > 1) for
+ *    every codec; PrismML Q2_0 codec (128 weights, 34 bytes, w = (q - 1) d,
+ *    q = 3 -> +2d).
+ *  - project index, Table B: block_q4_0 (GGUF Q4_0) and block_mlx_4bit weights.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers marked "device" are HIP device pointers; "host" ones are CPU
+ *    memory.  The caller owns every buffer.  The library allocates nothing,
+ *    keeps no pointer after a call returns and holds no mutable global state.
+ *  - Compute entry points enqueue work on `stream` (a hipStream_t; NULL is the
+ *    default stream) and return without synchronising.  A kernel fault shows
+ *    up at the caller's next synchronisation, as for any HIP launch.
+ *  - Errors are status codes; nothing is thrown across the ABI.  Argument
+ *    errors are detected before any launch, and then nothing is launched.
+ *  - Activations and outputs are row-major binary16.  Row strides are in
+ *    elements and must be multiples of 8 (16-byte rows); the base pointers of
+ *    x, y and of both weight planes must be 16-byte aligned.
+ *  - Each of x, y and the weight planes must span less than 2 GiB, and M, N
+ *    and K must be below 2^31 (QG_ERR_SHAPE otherwise).
+ *  - Weights are in the library's planar device format, produced from the
+ *    canonical codec bytes by qg_pack_host and sized by qg_packed_sizes.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight codecs.  Canonical byte formats (the input of qg_pack_host):
+ *  QG_CODEC_Q4_0     32-weight blocks of 18 bytes: fp16 d (little-endian),
+ *                    then 16 bytes, byte j = weight j (low nibble) and weight
+ *                    j + 16 (high nibble); w = (q - 8) * d.
+ *  QG_CODEC_MLX4_G64 codes as little-endian uint32 words [N, K/8] (element 0
+ *                    in the low nibble), then fp16 scales [N, K/64], then fp16
+ *                    biases [N, K/64]; w = q * s + b per 64-weight group.
+ *  QG_CODEC_Q2_0     128-weight blocks of 34 bytes: fp16 d, then 32 bytes of
+ *                    2-bit codes, weight i in byte i/4 at bit 2*(i%4);
+ *                    w = (q - 1) * d, so q = 3 gives +2d. */
+typedef enum {
+    QG_CODEC_Q4_0 = 1,
+    QG_CODEC_MLX4_G64 = 2,
+    QG_CODEC_Q2_0 = 3
+} qg_codec;
+
+typedef enum {
+    QG_OK = 0,
+    QG_ERR_NULL = -1,      /* a required pointer is NULL                       */
+    QG_ERR_CODEC = -2,     /* unknown codec id                                 */
+    QG_ERR_SHAPE = -3,     /* M/N/K out of range, K not a multiple of the block,
+                              stride smaller than the row, M > 64 for a GEMV,
+                              a buffer of 2 GiB or more, flags != 0           */
+    QG_ERR_ALIGN = -4,     /* pointer or stride not 16-byte aligned            */
+    QG_ERR_MISMATCH = -5,  /* gate/up descriptors differ in codec, N or K      */
+    QG_ERR_LAUNCH = -6,    /* the HIP launch itself failed                     */
+    QG_ERR_SIZE = -7       /* a host buffer is smaller than the format needs   */
+} qg_status;
+
+/* A packed weight matrix W [n, k] in the planar device format.
+ *  qs      device, code plane (qs_bytes from qg_packed_sizes)
+ *  scales  device, scale plane (scale_bytes): fp16 d for Q4_0 and Q2_0; for
+ *          MLX4-G64 each entry is the pair (fp16 scale, fp16 bias)
+ *  flags   must be 0 (reserved for layout variants)
+ * The descriptor itself is host memory and is only read during the call. */
+typedef struct {
+    int32_t codec;
+    int32_t flags;
+    int64_t n;
+    int64_t k;
+    const void *qs;
+    const void *scales;
+} qg_weight;
+
+/* Prefill projection Y[m, n] = sum_k X[m, k] * W[n, k]  (Y = X W^T).
+ *  w    host descriptor of W [N, K]
+ *  x    device fp16 [m, ldx], rows of K used       (m >= 1, ldx >= K)
+ *  y    device fp16 [m, ldy], first N columns written (ldy >= N)
+ * Dequantization happens inside the kernel; products accumulate in fp32 and
+ * are rounded once to fp16 (nearest even).  Any M >= 1 is accepted; small M
+ * is served by the weight-streaming kernel of qgemv_decode. */
+qg_status qgemm_prefill(const qg_weight *w, const void *x, int64_t m, int64_t ldx,
+                        void *y, int64_t ldy, void *stream);
+
+/* Fused gate/up projection with the SwiGLU epilogue (comparison page, section
+ * 2.2): out[m, n] = SiLU(g) * u with g = (X Wg^T)[m, n], u = (X Wu^T)[m, n],
+ * SiLU(g) = g / (1 + exp(-g)), evaluated in fp32 on the accumulators and
+ * rounded once to fp16.  Gate and up never reach device memory.
+ *  wg, wu  host descriptors with equal codec, N and K (else QG_ERR_MISMATCH)
+ *  x       device fp16 [m, ldx];  out  device fp16 [m, ldo] */
+qg_status qgemm_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x,
+                       int64_t m, int64_t ldx, void *out, int64_t ldo, void *stream);
+
+/* Weight-streaming small-M projection (decode, M = 1, and speculative
+ * verification of up to 64 candidate rows): Y = X W^T as for qgemm_prefill,
+ * for 1 <= m <= 64 (else QG_ERR_SHAPE).  Each weight byte is read from device
+ * memory once per call. */
+qg_status qgemv_decode(const qg_weight *w, const void *x, int64_t m, int64_t ldx,
+                       void *y, int64_t ldy, void *stream);
+
+/* Byte sizes of the two planar planes of an [n, k] matrix of `codec` (N is
+ * padded to 32 rows and K to 64 weights inside the planes; the padding decodes
+ * to zero).  Either out-pointer may be NULL. */
+qg_status qg_packed_sizes(int32_t codec, int64_t n, int64_t k, size_t *qs_bytes,
+                          size_t *scales_bytes);
+
+/* Size of the canonical encoding of an [n, k] matrix (see qg_codec). */
+qg_status qg_canonical_size(int32_t codec, int64_t n, int64_t k, size_t *bytes);
+
+/* Host-side repack of canonical codec bytes into the planar device format
+ * (comparison page, section 4: codes split from scales into 16-byte aligned
+ * planes).  Bit moves only; every code, scale and bias keeps its value.
+ *  canonical   host, canonical_bytes long (checked: QG_ERR_SIZE)
+ *  qs, scales  host outputs of the sizes from qg_packed_sizes; fully written
+ * Padding rows and columns get zero scales so that they decode to zero. */
+qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonical,
+                       size_t canonical_bytes, void *qs, void *scales);
+
+/* Dequantize W into fp16 w_fp16 [n, ldw] (device) with the same per-codec
+ * unpack routines the GEMM kernels feed to the matrix cores; each weight is the
+ * binary16 value nearest its exact codec value.  For verification. */
+qg_status qg_dequant(const qg_weight *w, void *w_fp16, int64_t ldw, void *stream);
+
+/* Static text for a status code. */
+const char *qg_status_str(qg_status s);
+
+/* ABI version of this header (major * 100 + minor). */
+int32_t qg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

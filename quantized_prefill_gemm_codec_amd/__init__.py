@@ -1,0 +1,216 @@
+"""Python binding of libqgemm.so: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C-ABI in
+``include/qgemm.h``; this module checks tensor dtypes, devices and strides,
+flattens leading batch dimensions (the pages' quantized linear layer accepts
+arbitrary leading dims: releases page, v0.3.0), allocates outputs with torch
+and passes raw pointers plus torch's current HIP stream.  There is no CPU
+fallback: if the library is not built, every entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemm.so")
+
+QG_CODEC_Q4_0 = 1
+QG_CODEC_MLX4_G64 = 2
+QG_CODEC_Q2_0 = 3
+CODECS = {"q4_0": QG_CODEC_Q4_0, "mlx4_g64": QG_CODEC_MLX4_G64, "q2_0": QG_CODEC_Q2_0}
+BLOCK = {QG_CODEC_Q4_0: 32, QG_CODEC_MLX4_G64: 64, QG_CODEC_Q2_0: 128}
+
+QG_OK = 0
+STATUS = {0: "QG_OK", -1: "QG_ERR_NULL", -2: "QG_ERR_CODEC", -3: "QG_ERR_SHAPE", -4: "QG_ERR_ALIGN",
+          -5: "QG_ERR_MISMATCH", -6: "QG_ERR_LAUNCH", -7: "QG_ERR_SIZE"}
+
+EXPORTS = ("qgemm_prefill", "qgemm_swiglu", "qgemv_decode", "qg_packed_sizes", "qg_canonical_size",
+           "qg_pack_host", "qg_dequant", "qg_status_str", "qg_version")
+
+
+class QGError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({_status_str(status)})")
+
+
+class qg_weight(ctypes.Structure):
+    _fields_ = [("codec", ctypes.c_int32), ("flags", ctypes.c_int32), ("n", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("qs", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libqgemm.so (raises when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m quantized_prefill_gemm_codec_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, p, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        W = ctypes.POINTER(qg_weight)
+        L.qgemm_prefill.argtypes = [W, p, i64, i64, p, i64, p]
+        L.qgemm_swiglu.argtypes = [W, W, p, i64, i64, p, i64, p]
+        L.qgemv_decode.argtypes = [W, p, i64, i64, p, i64, p]
+        L.qg_packed_sizes.argtypes = [i32, i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        L.qg_canonical_size.argtypes = [i32, i64, i64, ctypes.POINTER(sz)]
+        L.qg_pack_host.argtypes = [i32, i64, i64, p, sz, p, p]
+        L.qg_dequant.argtypes = [W, p, i64, p]
+        L.qg_status_str.argtypes = [ctypes.c_int]
+        L.qg_status_str.restype = ctypes.c_char_p
+        L.qg_version.restype = i32
+        for f in ("qgemm_prefill", "qgemm_swiglu", "qgemv_decode", "qg_packed_sizes", "qg_canonical_size",
+                  "qg_pack_host", "qg_dequant"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _status_str(st: int) -> str:
+    try:
+        return lib().qg_status_str(st).decode()
+    except Exception:  # library unavailable while formatting an error
+        return "?"
+
+
+def _check(st: int, where: str):
+    if st != QG_OK:
+        raise QGError(st, where)
+
+
+# ----------------------------------------------------------------- host side --
+
+def qg_packed_sizes(codec: int, n: int, k: int):
+    qs, sc = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().qg_packed_sizes(codec, n, k, ctypes.byref(qs), ctypes.byref(sc)), "qg_packed_sizes")
+    return qs.value, sc.value
+
+
+def qg_canonical_size(codec: int, n: int, k: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().qg_canonical_size(codec, n, k, ctypes.byref(b)), "qg_canonical_size")
+    return b.value
+
+
+def qg_pack_host(codec: int, n: int, k: int, canonical: np.ndarray):
+    """Canonical codec bytes -> (qs, scales) planar planes as numpy uint8 arrays."""
+    canonical = np.ascontiguousarray(canonical, dtype=np.uint8)
+    qs_b, sc_b = qg_packed_sizes(codec, n, k)
+    qs = np.empty(qs_b, dtype=np.uint8)
+    sc = np.empty(sc_b, dtype=np.uint8)
+    _check(lib().qg_pack_host(codec, n, k, canonical.ctypes.data, canonical.size, qs.ctypes.data, sc.ctypes.data),
+           "qg_pack_host")
+    return qs, sc
+
+
+# --------------------------------------------------------------- device side --
+
+def _torch():
+    import torch
+    return torch
+
+
+class QWeight:
+    """A packed weight matrix resident in device memory (torch-owned planes)."""
+
+    def __init__(self, codec: int, n: int, k: int, qs, scales):
+        self.codec, self.n, self.k = int(codec), int(n), int(k)
+        self.qs, self.scales = qs, scales
+        self._desc = qg_weight(self.codec, 0, self.n, self.k, qs.data_ptr(), scales.data_ptr())
+
+    @classmethod
+    def from_canonical(cls, codec: int, n: int, k: int, canonical: np.ndarray, device="cuda"):
+        torch = _torch()
+        qs, sc = qg_pack_host(codec, n, k, canonical)
+        return cls(codec, n, k, torch.from_numpy(qs).to(device), torch.from_numpy(sc).to(device))
+
+    @property
+    def desc(self):
+        return ctypes.byref(self._desc)
+
+    def nbytes(self) -> int:
+        return self.qs.numel() + self.scales.numel()
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _as_rows(x, k: int):
+    """Flatten leading dims to [M, K] rows with a 16-byte aligned row stride."""
+    torch = _torch()
+    if x.dtype != torch.float16 or not x.is_cuda:
+        raise TypeError("x must be a float16 tensor on a HIP device")
+    if x.dim() < 1 or x.shape[-1] != k:
+        raise ValueError(f"x has K={x.shape[-1] if x.dim() else None}, weights expect K={k}")
+    lead = tuple(x.shape[:-1])
+    x2 = x.reshape(-1, k)
+    m = x2.shape[0]
+    if x2.stride(-1) != 1 or (m > 1 and x2.stride(0) % 8) or x2.data_ptr() % 16:
+        x2 = x2.contiguous()
+    ldx = x2.stride(0) if m > 1 else k
+    return x2, lead, ldx
+
+
+def _out(m: int, n: int, device, out=None):
+    """Output rows [M, N] with a row stride that is a multiple of 8 elements."""
+    torch = _torch()
+    if out is not None:
+        o2 = out.reshape(-1, n)
+        if out.dtype != torch.float16 or o2.stride(-1) != 1 or o2.shape[0] != m:
+            raise ValueError("out must be float16 [..., N] with M rows and unit column stride")
+        return o2, (o2.stride(0) if m > 1 else 8 * ((n + 7) // 8)), out
+    ldy = 8 * ((n + 7) // 8)
+    buf = torch.empty((m, ldy), dtype=torch.float16, device=device)
+    return buf, ldy, buf[:, :n]
+
+
+def qgemm_prefill(w: QWeight, x, out=None, stream=None):
+    """Y = X W^T for fp16 X [..., K]; returns fp16 [..., N]."""
+    x2, lead, ldx = _as_rows(x, w.k)
+    m = x2.shape[0]
+    ybuf, ldy, y = _out(m, w.n, x.device, out)
+    _check(lib().qgemm_prefill(w.desc, x2.data_ptr(), m, ldx, ybuf.data_ptr(), ldy, _stream(stream)),
+           "qgemm_prefill")
+    return y.reshape(*lead, w.n) if out is None else out
+
+
+def qgemm_swiglu(wg: QWeight, wu: QWeight, x, out=None, stream=None):
+    """SiLU(X Wg^T) * (X Wu^T) for fp16 X [..., K]; returns fp16 [..., N]."""
+    x2, lead, ldx = _as_rows(x, wg.k)
+    m = x2.shape[0]
+    ybuf, ldy, y = _out(m, wg.n, x.device, out)
+    _check(lib().qgemm_swiglu(wg.desc, wu.desc, x2.data_ptr(), m, ldx, ybuf.data_ptr(), ldy, _stream(stream)),
+           "qgemm_swiglu")
+    return y.reshape(*lead, wg.n) if out is None else out
+
+
+def qgemv_decode(w: QWeight, x, out=None, stream=None):
+    """Weight-streaming Y = X W^T for 1 <= M <= 64 rows of X."""
+    x2, lead, ldx = _as_rows(x, w.k)
+    m = x2.shape[0]
+    ybuf, ldy, y = _out(m, w.n, x.device, out)
+    _check(lib().qgemv_decode(w.desc, x2.data_ptr(), m, ldx, ybuf.data_ptr(), ldy, _stream(stream)),
+           "qgemv_decode")
+    return y.reshape(*lead, w.n) if out is None else out
+
+
+def qg_dequant(w: QWeight, stream=None):
+    """fp16 image [N, K] of the weights, from the kernels' unpack routines."""
+    torch = _torch()
+    ldw = 8 * ((w.k + 7) // 8)
+    buf = torch.empty((w.n, ldw), dtype=torch.float16, device=w.qs.device)
+    _check(lib().qg_dequant(w.desc, buf.data_ptr(), ldw, _stream(stream)), "qg_dequant")
+    return buf[:, :w.k]
+
+
+def qg_version() -> int:
+    return int(lib().qg_version())

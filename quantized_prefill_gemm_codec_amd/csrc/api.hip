@@ -1,0 +1,141 @@
+// C-ABI entry points: argument validation, then one asynchronous launch on the
+// caller's stream.  Nothing is launched when an argument is rejected.
+#include "../../include/qgemm.h"
+#include "launch.h"
+
+using namespace qg;
+
+namespace {
+
+constexpr int64_t LIMIT = int64_t(1) << 31;   // bytes per buffer, and M/N/K
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_codec(int32_t c) { return c == Q4_0 || c == MLX4_G64 || c == Q2_0; }
+
+qg_status check_weight(const qg_weight *w)
+{
+    if (!w || !w->qs || !w->scales)
+        return QG_ERR_NULL;
+    if (!valid_codec(w->codec))
+        return QG_ERR_CODEC;
+    if (w->flags != 0 || w->n < 1 || w->k < 1 || w->n >= LIMIT || w->k >= LIMIT ||
+        w->k % block_size(w->codec) != 0)
+        return QG_ERR_SHAPE;
+    const Geometry g = geometry(w->codec, w->n, w->k);
+    if (g.qs_bytes >= LIMIT || g.scale_bytes >= LIMIT)
+        return QG_ERR_SHAPE;
+    if (!aligned16(w->qs) || !aligned16(w->scales))
+        return QG_ERR_ALIGN;
+    return QG_OK;
+}
+
+qg_status check_act(const void *p, int64_t rows, int64_t cols, int64_t ld)
+{
+    if (!p)
+        return QG_ERR_NULL;
+    // kernels form 32-bit byte offsets up to one 256-row tile past the last row
+    if (rows < 1 || rows >= LIMIT || ld < cols || ld >= LIMIT || ((rows - 1) * ld + cols) * 2 >= LIMIT ||
+        (rows + 256) * ld * 2 >= (int64_t(1) << 32))
+        return QG_ERR_SHAPE;
+    if (!aligned16(p) || ld % 8 != 0)
+        return QG_ERR_ALIGN;
+    return QG_OK;
+}
+
+Planes planes_of(const qg_weight *w)
+{
+    const Geometry g = geometry(w->codec, w->n, w->k);
+    Planes p;
+    p.qs = static_cast<const uint8_t *>(w->qs);
+    p.scales = w->scales;
+    p.qs_bytes = uint32_t(g.qs_bytes);
+    p.scale_bytes = uint32_t(g.scale_bytes);
+    return p;
+}
+
+GemmProblem problem(const qg_weight *w, const void *x, int64_t m, int64_t ldx, void *y, int64_t ldy)
+{
+    const Geometry g = geometry(w->codec, w->n, w->k);
+    GemmProblem p;
+    p.codec = w->codec;
+    p.w0 = planes_of(w);
+    p.w1 = p.w0;
+    p.x = static_cast<const _Float16 *>(x);
+    p.y = static_cast<_Float16 *>(y);
+    p.m = m;
+    p.n = w->n;
+    p.k = w->k;
+    p.ldx = ldx;
+    p.ldy = ldy;
+    p.groups = g.groups;
+    p.ksteps = g.ksteps;
+    p.kb128 = w->k / 128;
+    return p;
+}
+
+qg_status launched(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH; }
+
+qg_status check_gemm(const qg_weight *w, const void *x, int64_t m, int64_t ldx, void *y, int64_t ldy)
+{
+    qg_status st = check_weight(w);
+    if (st != QG_OK)
+        return st;
+    if ((st = check_act(x, m, w->k, ldx)) != QG_OK)
+        return st;
+    return check_act(y, m, w->n, ldy);
+}
+
+}  // namespace
+
+extern "C" {
+
+qg_status qgemm_prefill(const qg_weight *w, const void *x, int64_t m, int64_t ldx, void *y, int64_t ldy,
+                        void *stream)
+{
+    const qg_status st = check_gemm(w, x, m, ldx, y, ldy);
+    if (st != QG_OK)
+        return st;
+    const GemmProblem p = problem(w, x, m, ldx, y, ldy);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return launched(m <= 4 ? launch_gemv(p, s) : launch_gemm(p, false, s));
+}
+
+qg_status qgemm_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x, int64_t m, int64_t ldx, void *out,
+                       int64_t ldo, void *stream)
+{
+    qg_status st = check_gemm(wg, x, m, ldx, out, ldo);
+    if (st != QG_OK)
+        return st;
+    if ((st = check_weight(wu)) != QG_OK)
+        return st;
+    if (wu->codec != wg->codec || wu->n != wg->n || wu->k != wg->k)
+        return QG_ERR_MISMATCH;
+    GemmProblem p = problem(wg, x, m, ldx, out, ldo);
+    p.w1 = planes_of(wu);
+    return launched(launch_gemm(p, true, static_cast<hipStream_t>(stream)));
+}
+
+qg_status qgemv_decode(const qg_weight *w, const void *x, int64_t m, int64_t ldx, void *y, int64_t ldy,
+                       void *stream)
+{
+    const qg_status st = check_gemm(w, x, m, ldx, y, ldy);
+    if (st != QG_OK)
+        return st;
+    if (m > 64)
+        return QG_ERR_SHAPE;
+    const GemmProblem p = problem(w, x, m, ldx, y, ldy);
+    return launched(launch_gemv(p, static_cast<hipStream_t>(stream)));
+}
+
+qg_status qg_dequant(const qg_weight *w, void *w_fp16, int64_t ldw, void *stream)
+{
+    qg_status st = check_weight(w);
+    if (st != QG_OK)
+        return st;
+    if ((st = check_act(w_fp16, w->n, w->k, ldw)) != QG_OK)
+        return st;
+    const GemmProblem p = problem(w, nullptr, 1, w->k, nullptr, w->n);
+    return launched(launch_dequant(p, static_cast<_Float16 *>(w_fp16), ldw, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,26 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "unpack.h"
+
+namespace qg {
+
+struct GemmProblem {
+    int codec;
+    Planes w0, w1;             // w1: up projection for the fused SwiGLU
+    const _Float16 *x;
+    _Float16 *y;
+    int64_t m, n, k, ldx, ldy;
+    int64_t groups, ksteps, kb128;
+};
+
+// Tiled MFMA kernels.  Return a hipError_t of the launch.
+hipError_t launch_gemm(const GemmProblem &p, bool swiglu, hipStream_t stream);
+// Weight-streaming small-M kernels (1 <= m <= 64).
+hipError_t launch_gemv(const GemmProblem &p, hipStream_t stream);
+// fp16 image of the weights, [n, ldw].
+hipError_t launch_dequant(const GemmProblem &p, _Float16 *out, int64_t ldw, hipStream_t stream);
+
+}  // namespace qg

@@ -1,0 +1,184 @@
+// Host side of the C-ABI: plane sizes, canonical -> planar repack, status text.
+//
+// The repack only moves bits: every code keeps its value, every fp16 scale and
+// bias keeps its bit pattern.  The layout it produces is described in planar.h.
+#include <string.h>
+
+#include "../../include/qgemm.h"
+#include "planar.h"
+
+using namespace qg;
+
+namespace {
+
+bool valid_codec(int32_t c) { return c == Q4_0 || c == MLX4_G64 || c == Q2_0; }
+
+qg_status check_shape(int32_t codec, int64_t n, int64_t k)
+{
+    if (!valid_codec(codec))
+        return QG_ERR_CODEC;
+    if (n < 1 || k < 1 || k % block_size(codec) != 0)
+        return QG_ERR_SHAPE;
+    if (n > (int64_t(1) << 31) || k > (int64_t(1) << 31))
+        return QG_ERR_SHAPE;
+    return QG_OK;
+}
+
+size_t canonical_size(int32_t codec, int64_t n, int64_t k)
+{
+    if (codec == Q4_0)
+        return size_t(n) * size_t(k / 32) * 18;
+    if (codec == Q2_0)
+        return size_t(n) * size_t(k / 128) * 34;
+    return size_t(n) * size_t(k / 2) + 2 * size_t(n) * size_t(k / 64) * 2;
+}
+
+inline uint16_t rd16(const uint8_t *p) { return uint16_t(p[0] | (p[1] << 8)); }
+inline void wr16(uint8_t *p, uint16_t v)
+{
+    p[0] = uint8_t(v & 0xFF);
+    p[1] = uint8_t(v >> 8);
+}
+
+// code of weight (row, kk) in the canonical stream
+inline int canonical_code(int32_t codec, const uint8_t *c, int64_t row, int64_t kk, int64_t k)
+{
+    if (codec == Q4_0) {
+        const uint8_t *blk = c + (row * (k / 32) + kk / 32) * 18;
+        int j = int(kk % 32);
+        return j < 16 ? (blk[2 + j] & 0xF) : (blk[2 + j - 16] >> 4);
+    }
+    if (codec == Q2_0) {
+        const uint8_t *blk = c + (row * (k / 128) + kk / 128) * 34;
+        int i = int(kk % 128);
+        return (blk[2 + i / 4] >> (2 * (i % 4))) & 3;
+    }
+    const uint8_t *word = c + (row * (k / 8) + kk / 8) * 4;
+    int e = int(kk % 8);
+    return (word[e / 2] >> (4 * (e % 2))) & 0xF;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t qg_version(void) { return 100; }
+
+const char *qg_status_str(qg_status s)
+{
+    switch (s) {
+    case QG_OK: return "ok";
+    case QG_ERR_NULL: return "null pointer argument";
+    case QG_ERR_CODEC: return "unknown codec id";
+    case QG_ERR_SHAPE: return "unsupported shape (M/N/K range, K not a multiple of the block, stride too small)";
+    case QG_ERR_ALIGN: return "pointer or row stride not 16-byte aligned";
+    case QG_ERR_MISMATCH: return "gate and up weights differ in codec, N or K";
+    case QG_ERR_LAUNCH: return "kernel launch failed";
+    case QG_ERR_SIZE: return "host buffer smaller than the format requires";
+    }
+    return "unknown status";
+}
+
+qg_status qg_packed_sizes(int32_t codec, int64_t n, int64_t k, size_t *qs_bytes,
+                          size_t *scales_bytes)
+{
+    qg_status st = check_shape(codec, n, k);
+    if (st != QG_OK)
+        return st;
+    Geometry g = geometry(codec, n, k);
+    if (qs_bytes)
+        *qs_bytes = size_t(g.qs_bytes);
+    if (scales_bytes)
+        *scales_bytes = size_t(g.scale_bytes);
+    return QG_OK;
+}
+
+qg_status qg_canonical_size(int32_t codec, int64_t n, int64_t k, size_t *bytes)
+{
+    qg_status st = check_shape(codec, n, k);
+    if (st != QG_OK)
+        return st;
+    if (!bytes)
+        return QG_ERR_NULL;
+    *bytes = canonical_size(codec, n, k);
+    return QG_OK;
+}
+
+qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonical,
+                       size_t canonical_bytes, void *qs, void *scales)
+{
+    qg_status st = check_shape(codec, n, k);
+    if (st != QG_OK)
+        return st;
+    if (!canonical || !qs || !scales)
+        return QG_ERR_NULL;
+    if (canonical_bytes < canonical_size(codec, n, k))
+        return QG_ERR_SIZE;
+
+    const uint8_t *c = static_cast<const uint8_t *>(canonical);
+    uint8_t *q = static_cast<uint8_t *>(qs);
+    uint8_t *s = static_cast<uint8_t *>(scales);
+    Geometry g = geometry(codec, n, k);
+    const int cb = lane_code_bytes(codec);
+    const bool four_bit = codec != Q2_0;
+    // zero-weight code for padding: Q4_0 q = 8, Q2_0 q = 1, MLX q = 0 (s = b = 0)
+    const int pad_code = codec == Q4_0 ? 8 : codec == Q2_0 ? 1 : 0;
+
+    memset(q, 0, size_t(g.qs_bytes));
+    memset(s, 0, size_t(g.scale_bytes));
+
+    for (int64_t r = 0; r < g.groups; ++r) {
+        for (int64_t t = 0; t < g.ksteps; ++t) {
+            uint8_t *chunk = q + (r * g.ksteps + t) * 64 * cb;
+            for (int l = 0; l < 64; ++l) {
+                const int gh = l / 32, i = l % 32;
+                const int64_t row = r * 32 + i;
+                uint8_t *lane = chunk + l * cb;
+                for (int j = 0; j < 32; ++j) {
+                    const int64_t kk = t * 64 + gh * 32 + j;
+                    const int code = (row < n && kk < k) ? canonical_code(codec, c, row, kk, k) : pad_code;
+                    int byte, shift;
+                    if (four_bit) {
+                        const int dw = j / 8, e = j % 8;
+                        const int bit = 4 * (e / 2) + 16 * (e % 2);
+                        byte = 4 * dw + bit / 8;
+                        shift = bit % 8;
+                    } else {
+                        const int dw = j / 16, e = j % 16;
+                        const int bit = 2 * (e / 2) + 16 * (e % 2);
+                        byte = 4 * dw + bit / 8;
+                        shift = bit % 8;
+                    }
+                    lane[byte] = uint8_t(lane[byte] | (code << shift));
+                }
+            }
+        }
+    }
+
+    // scale / bias planes (padding entries stay zero -> padded weights decode to 0)
+    for (int64_t row = 0; row < n; ++row) {
+        const int64_t r = row / 32, i = row % 32;
+        if (codec == Q4_0) {
+            for (int64_t blk = 0; blk < k / 32; ++blk) {
+                const int64_t t = blk / 2, gh = blk % 2;
+                wr16(s + (((r * g.ksteps + t) * 2 + gh) * 32 + i) * 2, rd16(c + (row * (k / 32) + blk) * 18));
+            }
+        } else if (codec == Q2_0) {
+            const int64_t nb = k / 128;
+            for (int64_t blk = 0; blk < nb; ++blk)
+                wr16(s + ((r * nb + blk) * 32 + i) * 2, rd16(c + (row * nb + blk) * 34));
+        } else {
+            const int64_t ng = k / 64;
+            const uint8_t *sc = c + size_t(n) * size_t(k / 2);
+            const uint8_t *bi = sc + size_t(n) * size_t(ng) * 2;
+            for (int64_t grp = 0; grp < ng; ++grp) {
+                uint8_t *e = s + ((r * g.ksteps + grp) * 32 + i) * 4;
+                wr16(e, rd16(sc + (row * ng + grp) * 2));
+                wr16(e + 2, rd16(bi + (row * ng + grp) * 2));
+            }
+        }
+    }
+    return QG_OK;
+}
+
+}  // extern "C"

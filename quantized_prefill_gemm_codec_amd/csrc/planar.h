@@ -1,0 +1,82 @@
+// Planar device format of the packed weights (host and device).
+//
+// The pages trace a measured slowdown to interleaved block structs whose size
+// is not a multiple of 16 bytes (comparison page, section 4, the 20-byte MLX
+// struct: 20 mod 16 = 4); 18-byte Q4_0 and 34-byte Q2_0 blocks share the
+// problem (both are 2 mod 16).  The library therefore keeps codes and scales in
+// separate planes and orders the codes so that one 64-lane wavefront reads one
+// contiguous 1 KiB (4-bit) or 512 B (2-bit) chunk per 128-bit (64-bit) load --
+// the "2D block-swizzled" tile-major weight layout of the project index,
+// Pillar 1, Brick 2, laid out for gfx950 wavefronts.
+//
+// Geometry.  W [N, K] is cut into row groups of 32 rows and k-steps of 64
+// weights (N and K padded up; padding decodes to zero).  Within a (row group
+// r, k-step t) chunk, lane l = 32 * g + i owns row 32 r + i and the 32 weights
+// k = 64 t + 32 g + j, j = 0..31.  These are exactly the 8-element K slices a
+// lane feeds to v_mfma_f32_32x32x16_f16 over four 16-deep sub-steps:
+// sub-step s uses j = 8 s .. 8 s + 7.
+//
+// Code order inside a lane's bytes (chosen so that unpacking needs one shift,
+// one and-or per pair of weights and no byte shuffles):
+//  * 4-bit (Q4_0, MLX4-G64): 16 bytes = 4 dwords; dword s holds j = 8 s + e,
+//    with e = 2p at bits [4p, 4p+4) and e = 2p + 1 at bits [16+4p, 20+4p).
+//  * 2-bit (Q2_0): 8 bytes = 2 dwords; dword h holds j = 16 h + e, with
+//    e = 2p at bits [2p, 2p+2) and e = 2p + 1 at bits [16+2p, 18+2p).
+// So every extracted pair lands as (low half, high half) = (even e, odd e),
+// the element order of a packed fp16 register.
+//
+// Scale planes, one 64-lane (Q4_0) or 32-lane record per chunk:
+//  * Q4_0:     fp16 [N/32][K/64][2][32]  -- d of block 2t+g for lane (g, i)
+//  * MLX4-G64: u32  [N/32][K/64][32]     -- (s, b) of group t as two fp16
+//                                           (scale low half, bias high half),
+//                                           so one 32-bit load brings both
+//  * Q2_0:     fp16 [N/32][K/128][32]    -- d of block t/2
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#define QG_ROWS_PER_GROUP 32
+#define QG_KSTEP 64
+
+#ifdef __HIPCC__
+#define QG_HD __host__ __device__
+#else
+#define QG_HD
+#endif
+
+namespace qg {
+
+enum Codec : int32_t { Q4_0 = 1, MLX4_G64 = 2, Q2_0 = 3 };
+
+QG_HD inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+QG_HD inline int block_size(int codec)
+{
+    return codec == Q4_0 ? 32 : codec == MLX4_G64 ? 64 : codec == Q2_0 ? 128 : 0;
+}
+
+// bytes of codes a lane holds per chunk
+QG_HD inline int lane_code_bytes(int codec) { return codec == Q2_0 ? 8 : 16; }
+
+struct Geometry {
+    int64_t groups;   // row groups (N padded to 32) / 32
+    int64_t ksteps;   // K padded to 64, / 64
+    int64_t qs_bytes, scale_bytes;
+};
+
+QG_HD inline Geometry geometry(int codec, int64_t n, int64_t k)
+{
+    Geometry g;
+    g.groups = ceil_div(n, QG_ROWS_PER_GROUP);
+    g.ksteps = ceil_div(k, QG_KSTEP);
+    g.qs_bytes = g.groups * g.ksteps * 64 * lane_code_bytes(codec);
+    if (codec == Q4_0)
+        g.scale_bytes = g.groups * g.ksteps * 64 * 2;
+    else if (codec == MLX4_G64)
+        g.scale_bytes = g.groups * g.ksteps * 32 * 4;
+    else
+        g.scale_bytes = g.groups * ceil_div(k, 128) * 32 * 2;
+    return g;
+}
+
+}  // namespace qg

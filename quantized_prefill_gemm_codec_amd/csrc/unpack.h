@@ -1,0 +1,174 @@
+// Per-codec unpack stage (device): planar code words -> fp16 weights.
+//
+// The pages run every codec through one shared unpack contract that feeds the
+// matrix-unit GEMM, the SwiGLU core and the GEMV (releases page, v0.2.3,
+// TCodec::unpack_column); this header is that stage for gfx950.  All three
+// codecs use the same integer trick: OR-ing a 4-bit (or 2-bit) code into the
+// mantissa of the binary16 pattern 0x6400 (= 1024) gives exactly 1024 + q, two
+// codes per 32-bit register.  One packed fp16 subtraction of an integer
+// constant is then exact and yields the signed integer weight factor, and a
+// single packed multiply (or fused multiply-add) rounds once to the nearest
+// binary16 -- so the fp16 operand handed to the MFMA is the correctly rounded
+// value of the exact codec weight:
+//   Q4_0      w = (q - 8) * d              (v_pk_add_f16, v_pk_mul_f16)
+//   MLX4-G64  w = fma(q, s, b)             (v_pk_add_f16, v_pk_fma_f16)
+//   Q2_0      w = (q - 1) * d, q=3 -> +2d  (v_pk_add_f16, v_pk_mul_f16)
+// (Q2_0 values are exact; Q4_0 and MLX round once.  fp16 subnormals are kept:
+// an MLX weight with q = 0 is its bias, which may be subnormal.)
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "planar.h"
+
+namespace qg {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// The binary16 pattern 0x6400 (= 1024) twice, held in a VGPR the compiler
+// cannot see through: with the mask in an SGPR, mask-and-insert then fits one
+// v_and_or_b32 (gfx9 VOP3 encodings take no literal operands).
+__device__ __forceinline__ uint32_t magic1024()
+{
+    uint32_t r;
+    asm("v_mov_b32 %0, 0x64006400" : "=v"(r));
+    return r;
+}
+
+// (1024 + code_even, 1024 + code_odd) of pair p of a code dword
+__device__ __forceinline__ uint32_t pair4(uint32_t v, int p, uint32_t magic)
+{
+    return ((v >> (4 * p)) & 0x000F000Fu) | magic;
+}
+__device__ __forceinline__ uint32_t pair2(uint32_t v, int p, uint32_t magic)
+{
+    return ((v >> (2 * p)) & 0x00030003u) | magic;
+}
+
+// The codes a lane owns in one (row group, k-step) chunk, plus its scales.
+template <int CODEC> struct LaneCodes;
+
+template <> struct LaneCodes<Q4_0> {
+    u32x4 c;
+    _Float16 d;
+};
+template <> struct LaneCodes<MLX4_G64> {
+    u32x4 c;
+    uint32_t sb;   // fp16 scale (low half) and fp16 bias (high half)
+};
+template <> struct LaneCodes<Q2_0> {
+    u32x2 c;
+    _Float16 d;
+};
+
+// Integer offset that turns 1024 + q into the signed weight factor.
+template <int CODEC> struct CodeBias;
+template <> struct CodeBias<Q4_0> { static constexpr float v = 1032.0f; };
+template <> struct CodeBias<MLX4_G64> { static constexpr float v = 1024.0f; };
+template <> struct CodeBias<Q2_0> { static constexpr float v = 1025.0f; };
+
+// Pair p (0..3) of sub-step s (0..3) as exact fp16 integers (q - bias).
+template <int CODEC>
+__device__ __forceinline__ f16x2 factor_pair(const LaneCodes<CODEC> &lc, int s, int p, uint32_t magic)
+{
+    constexpr _Float16 off = _Float16(CodeBias<CODEC>::v);
+    const f16x2 o = {off, off};
+    uint32_t bits;
+    if constexpr (CODEC == Q2_0)
+        bits = pair2(lc.c[s >> 1], 4 * (s & 1) + p, magic);
+    else
+        bits = pair4(lc.c[s], p, magic);
+    return as_f16x2(bits) - o;
+}
+
+// The 8 fp16 weights of sub-step s in MFMA operand order (element e = k offset
+// 8 s + e inside the lane's 32-weight slice).
+template <int CODEC>
+__device__ __forceinline__ f16x8 unpack_substep(const LaneCodes<CODEC> &lc, int s, uint32_t magic)
+{
+    f16x8 out;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        f16x2 q = factor_pair<CODEC>(lc, s, p, magic);
+        f16x2 w;
+        if constexpr (CODEC == MLX4_G64) {
+            const f16x2 sb = as_f16x2(lc.sb);
+            const f16x2 sc = {sb[0], sb[0]};
+            const f16x2 bi = {sb[1], sb[1]};
+            w = __builtin_elementwise_fma(q, sc, bi);
+        } else {
+            const f16x2 dd = {lc.d, lc.d};
+            w = q * dd;
+        }
+        out[2 * p] = w[0];
+        out[2 * p + 1] = w[1];
+    }
+    return out;
+}
+
+// Planar plane pointers of one weight matrix (host side).
+struct Planes {
+    const uint8_t *qs;
+    const void *scales;
+    uint32_t qs_bytes, scale_bytes;
+};
+
+// Raw buffer descriptor over [base, base + bytes).  Loads whose byte offset
+// falls outside the range return zero, which is how every kernel masks the
+// M, N and K tails without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, int(bytes), 0x00020000);
+}
+
+constexpr uint32_t OOB = 0x80000000u;   // an offset no plane reaches
+
+struct PlaneRsrc {
+    __amdgpu_buffer_rsrc_t qs, sc;
+};
+
+__device__ __forceinline__ PlaneRsrc plane_rsrc(const Planes &w)
+{
+    PlaneRsrc r;
+    r.qs = make_rsrc(w.qs, w.qs_bytes);
+    r.sc = make_rsrc(w.scales, w.scale_bytes);
+    return r;
+}
+
+__device__ __forceinline__ _Float16 load_f16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(_Float16, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+
+// Load the chunk (row group rg, k-step t) codes and scales a lane owns.
+// `ksteps` = padded K / 64, `kb128` = K / 128 (Q2_0 scale plane pitch).
+// Row groups past the end read as zero codes with zero scales (weight 0).
+template <int CODEC>
+__device__ __forceinline__ LaneCodes<CODEC> load_lane(const PlaneRsrc &w, int rg, int t, int ksteps, int kb128,
+                                                      int lane)
+{
+    LaneCodes<CODEC> lc;
+    const uint32_t chunk = uint32_t(rg) * uint32_t(ksteps) + uint32_t(t);
+    const uint32_t i = uint32_t(lane & 31);
+    if constexpr (CODEC == Q2_0) {
+        lc.c = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(w.qs, (chunk * 64 + lane) * 8, 0, 0));
+        lc.d = load_f16(w.sc, ((uint32_t(rg) * kb128 + uint32_t(t >> 1)) * 32 + i) * 2);
+    } else {
+        lc.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, (chunk * 64 + lane) * 16, 0, 0));
+        if constexpr (CODEC == Q4_0)
+            lc.d = load_f16(w.sc, (chunk * 64 + lane) * 2);
+        else
+            lc.sb = __builtin_amdgcn_raw_buffer_load_b32(w.sc, (chunk * 32 + i) * 4, 0, 0);
+    }
+    return lc;
+}
+
+}  // namespace qg

@@ -1,0 +1,267 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C-ABI.
+
+Bars (the method's own): dequantized fp16 weights bit-exact against the
+oracle's correctly rounded decode; GEMM / SwiGLU / GEMV outputs finite and
+within max|err| / rms(ref) <= 1e-2 of the fp64 reference.  Full-size workloads
+are checked on sampled rows and columns the oracle computes directly.
+Integer-exact properties (identity probe, power-of-two scaling, row
+permutation, run-to-run determinism) are checked bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import quantized_prefill_gemm_codec_amd as qg
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no HIP device")
+    return t
+
+
+def _dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _weight(torch, codec, n, k, canon):
+    return qg.QWeight.from_canonical(codec, n, k, canon, device="cuda")
+
+
+def _err(y, ref):
+    y = np.asarray(y, np.float64)
+    assert np.all(np.isfinite(y)), "non-finite output"
+    rms = np.sqrt(np.mean(ref ** 2))
+    return float(np.max(np.abs(y - ref)) / rms)
+
+
+def _err_beyond_fp16_rounding(y, ref):
+    """max over elements of (|y - ref| - 2^-11 |ref|) / rms(ref).
+
+    The fused SwiGLU output is fp16 and heavy-tailed (a product of two
+    near-Gaussian sums): the half-ulp rounding of the output format alone,
+    up to 2^-11 |ref|, reaches ~1e-2 of rms at the largest elements.  The
+    tolerance applies to the error on top of that unavoidable rounding.
+    """
+    y = np.asarray(y, np.float64)
+    assert np.all(np.isfinite(y)), "non-finite output"
+    rms = np.sqrt(np.mean(ref ** 2))
+    return float(np.max(np.maximum(np.abs(y - ref) - 2.0 ** -11 * np.abs(ref), 0.0)) / rms)
+
+
+def _same_value_bits(a16, b16):
+    """fp16 arrays equal bit for bit, except that +0 and -0 compare equal."""
+    a = np.asarray(a16).view(np.uint16)
+    b = np.asarray(b16).view(np.uint16)
+    zero = ((a & 0x7FFF) == 0) & ((b & 0x7FFF) == 0)
+    return bool(np.all((a == b) | zero))
+
+
+# ------------------------------------------------------------- dequantization --
+
+DEQ_SHAPES = [(1, 256, 256), (1, 40, 96), (1, 1000, 544), (2, 33, 192), (2, 300, 1024),
+              (3, 37, 256), (3, 520, 1152)]
+
+
+@pytest.mark.parametrize("codec,n,k", DEQ_SHAPES)
+def test_dequant_bit_exact(torch, codec, n, k):
+    canon = synth.gen_weight(codec, n, k, 1000 + n)
+    w = _weight(torch, codec, n, k, canon)
+    got = qg.qg_dequant(w).cpu().numpy()
+    want = oracle.dequant_f16_bits(codec, canon, n, k).view(np.float16)
+    assert _same_value_bits(got, want)
+
+
+def test_dequant_keeps_subnormal_bias(torch):
+    n, k = 32, 128
+    codes = np.zeros((n, k), np.uint8)
+    s = np.full((n, k // 64), 0.5, np.float16)
+    b = (np.arange(n * (k // 64)).reshape(n, k // 64) % 7 + 1).astype(np.uint16).view(np.float16)   # subnormals
+    canon = synth.encode_mlx4(codes, s, b)
+    got = qg.qg_dequant(_weight(torch, 2, n, k, canon)).cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), np.repeat(b.view(np.uint16), 64, axis=1))
+
+
+@pytest.mark.parametrize("codec", [1, 2, 3])
+def test_identity_probe_through_gemm(torch, codec):
+    """X = I: every output is one product with 1.0, so Y = W^T exactly."""
+    n = k = 256
+    canon = synth.gen_weight(codec, n, k, 2000 + codec)
+    w = _weight(torch, codec, n, k, canon)
+    x = torch.eye(k, dtype=torch.float16, device="cuda")
+    y = qg.qgemm_prefill(w, x).cpu().numpy()
+    want = oracle.dequant_f16_bits(codec, canon, n, k).view(np.float16).T
+    assert _same_value_bits(y, want)
+
+
+# --------------------------------------------------------------- prefill GEMM --
+
+GEMM_SHAPES = [
+    (1, 16, 256, 256), (1, 5, 200, 96), (1, 33, 256, 288), (1, 127, 520, 64), (1, 128, 256, 32),
+    (1, 129, 136, 160), (1, 300, 264, 352), (1, 257, 1024, 256),
+    (2, 6, 256, 192), (2, 65, 200, 64), (2, 129, 272, 320), (2, 300, 512, 256),
+    (3, 7, 96, 128), (3, 100, 264, 384), (3, 129, 256, 256), (3, 320, 520, 512),
+]
+
+
+@pytest.mark.parametrize("codec,m,n,k", GEMM_SHAPES)
+def test_prefill_parity(torch, codec, m, n, k):
+    seed = 3000 + m + n + k
+    canon = synth.gen_weight(codec, n, k, seed)
+    x = synth.gen_x(m, k, seed)
+    w = _weight(torch, codec, n, k, canon)
+    y = qg.qgemm_prefill(w, _dev(torch, x)).cpu().numpy()
+    ref = oracle.gemm_ref(codec, canon, n, k, x)
+    assert _err(y, ref) <= TOL
+
+
+def test_prefill_leading_dims_and_strides(torch):
+    codec, n, k = 1, 136, 192
+    canon = synth.gen_weight(codec, n, k, 41)
+    w = _weight(torch, codec, n, k, canon)
+    x = synth.gen_x(6, k, 42)
+    ref = oracle.gemm_ref(codec, canon, n, k, x)
+    y3 = qg.qgemm_prefill(w, _dev(torch, x).reshape(2, 3, k)).cpu().numpy()
+    assert y3.shape == (2, 3, n) and _err(y3.reshape(6, n), ref) <= TOL
+    wide = torch.zeros((6, k + 40), dtype=torch.float16, device="cuda")
+    wide[:, :k] = _dev(torch, x)
+    wide[:, k:] = float("nan")                       # must never be read
+    out = torch.full((6, n + 24), float("nan"), dtype=torch.float16, device="cuda")
+    qg.qgemm_prefill(w, wide[:, :k], out=out[:, :n])
+    o = out.cpu().numpy()
+    assert _err(o[:, :n], ref) <= TOL
+    assert np.all(np.isnan(o[:, n:].astype(np.float32)))   # columns past N untouched
+
+
+def test_prefill_power_of_two_scale_is_exact(torch):
+    codec, m, n, k = 1, 300, 256, 256
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    d = rng.uniform(0.005, 0.02, (n, k // 32)).astype(np.float16)
+    x = _dev(torch, synth.gen_x(m, k, 6))
+    y1 = qg.qgemm_prefill(_weight(torch, codec, n, k, synth.encode_q4_0(codes, d)), x).cpu().numpy()
+    y2 = qg.qgemm_prefill(_weight(torch, codec, n, k, synth.encode_q4_0(codes, d * np.float16(2))), x).cpu().numpy()
+    a, b = y1.astype(np.float64), y2.astype(np.float64)
+    # x2 commutes with every fp32 rounding and with the fp16 output rounding,
+    # except in the fp16 subnormal range, whose quantum is fixed at 2^-24
+    normal = np.abs(a) >= 2.0 ** -14
+    assert normal.mean() > 0.99
+    bad = normal & (b != 2 * a)
+    assert not bad.any(), (int(bad.sum()), a[bad][:5], b[bad][:5])
+    assert np.all(np.abs(b - 2 * a)[~normal] <= 2.0 ** -23)
+
+
+def test_prefill_row_permutation_and_determinism(torch):
+    codec, m, n, k = 2, 512, 512, 512
+    canon = synth.gen_weight(codec, n, k, 7)
+    w = _weight(torch, codec, n, k, canon)
+    x = synth.gen_x(m, k, 8)
+    perm = np.random.default_rng(9).permutation(m)
+    y = qg.qgemm_prefill(w, _dev(torch, x)).cpu().numpy()
+    y_again = qg.qgemm_prefill(w, _dev(torch, x)).cpu().numpy()
+    yp = qg.qgemm_prefill(w, _dev(torch, x[perm])).cpu().numpy()
+    assert np.array_equal(y.view(np.uint16), y_again.view(np.uint16))
+    assert np.array_equal(yp.view(np.uint16), y[perm].view(np.uint16))
+
+
+# -------------------------------------------------------------------- SwiGLU --
+
+SWIGLU_SHAPES = [(2, 33, 200, 192), (2, 130, 256, 128), (2, 300, 264, 256), (1, 70, 136, 96), (3, 200, 128, 256)]
+
+
+@pytest.mark.parametrize("codec,m,n,k", SWIGLU_SHAPES)
+def test_swiglu_parity(torch, codec, m, n, k):
+    seed = 4000 + m + n
+    cg = synth.gen_weight(codec, n, k, seed, synth.T_WG)
+    cu = synth.gen_weight(codec, n, k, seed, synth.T_WU)
+    x = synth.gen_x(m, k, seed)
+    y = qg.qgemm_swiglu(_weight(torch, codec, n, k, cg), _weight(torch, codec, n, k, cu), _dev(torch, x)).cpu().numpy()
+    ref = oracle.swiglu_ref(codec, cg, cu, n, k, x)
+    assert _err_beyond_fp16_rounding(y, ref) <= TOL
+
+
+def test_swiglu_one_hot_probe(torch):
+    """One-hot X rows and an up matrix of exact ones: out = SiLU(wg[n, k_m])."""
+    m, n, k = 64, 256, 128
+    cg = synth.gen_weight(2, n, k, 11, synth.T_WG)
+    ones = synth.encode_mlx4(np.zeros((n, k), np.uint8), np.full((n, 2), 0.25, np.float16),
+                             np.ones((n, 2), np.float16))
+    km = np.arange(m) * 2 % k
+    x = np.zeros((m, k), np.float16)
+    x[np.arange(m), km] = 1
+    y = qg.qgemm_swiglu(_weight(torch, 2, n, k, cg), _weight(torch, 2, n, k, ones), _dev(torch, x)).cpu().numpy()
+    g = oracle.dequant_f16_bits(2, cg, n, k).view(np.float16).astype(np.float64)[:, km].T
+    ref = oracle.swiglu(g, np.ones_like(g))
+    assert np.all(np.abs(y.astype(np.float64) - ref) <= 2.0 ** -10 * np.abs(ref) + 2.0 ** -24)
+
+
+# ---------------------------------------------------------------------- GEMV --
+
+GEMV_SHAPES = [(1, 1, 1000, 512), (1, 2, 256, 96), (1, 3, 520, 256), (1, 4, 200, 1024), (1, 5, 256, 256),
+               (1, 17, 136, 192), (1, 64, 512, 512), (2, 1, 300, 256), (2, 4, 256, 512), (2, 33, 256, 128),
+               (3, 1, 264, 512), (3, 3, 256, 256), (3, 64, 200, 384)]
+
+
+@pytest.mark.parametrize("codec,m,n,k", GEMV_SHAPES)
+def test_gemv_parity(torch, codec, m, n, k):
+    seed = 5000 + m + n + k
+    canon = synth.gen_weight(codec, n, k, seed)
+    x = synth.gen_x(m, k, seed)
+    w = _weight(torch, codec, n, k, canon)
+    y = qg.qgemv_decode(w, _dev(torch, x)).cpu().numpy()
+    ref = oracle.gemm_ref(codec, canon, n, k, x)
+    assert _err(y, ref) <= TOL
+    y2 = qg.qgemv_decode(w, _dev(torch, x)).cpu().numpy()
+    assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
+
+
+def test_gemv_single_vector_shape(torch):
+    codec, n, k = 1, 256, 256
+    canon = synth.gen_weight(codec, n, k, 51)
+    x = synth.gen_x(1, k, 52)
+    y = qg.qgemv_decode(_weight(torch, codec, n, k, canon), _dev(torch, x[0])).cpu().numpy()
+    assert y.shape == (n,)
+    assert _err(y[None, :], oracle.gemm_ref(codec, canon, n, k, x)) <= TOL
+
+
+# ----------------------------------------------------- full-size workloads --
+
+def _sample(rng, size, count):
+    if size <= count:
+        return np.arange(size)
+    s = rng.choice(np.arange(1, size - 1), count - 2, replace=False)
+    return np.sort(np.concatenate([[0, size - 1], s]))
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_full_workload_sampled(torch, name):
+    wl = synth.WORKLOADS[name]
+    x = wl.x()
+    mats = wl.weights()
+    ws = [_weight(torch, wl.codec, wl.n, wl.k, c) for c in mats]
+    xd = _dev(torch, x)
+    if wl.op == "swiglu":
+        y = qg.qgemm_swiglu(ws[0], ws[1], xd)
+    elif wl.op == "gemv":
+        y = qg.qgemv_decode(ws[0], xd)
+    else:
+        y = qg.qgemm_prefill(ws[0], xd)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    rng = np.random.default_rng(wl.seed)
+    rows_m = _sample(rng, wl.m, 12)
+    rows_n = _sample(rng, wl.n, 384)
+    ys = y.cpu().numpy()[np.ix_(rows_m, rows_n)]
+    if wl.op == "swiglu":
+        ref = oracle.swiglu_ref(wl.codec, mats[0], mats[1], wl.n, wl.k, x[rows_m], rows_n=rows_n)
+        assert _err_beyond_fp16_rounding(ys, ref) <= TOL
+    else:
+        ref = oracle.gemm_ref(wl.codec, mats[0], wl.n, wl.k, x[rows_m], rows_n=rows_n)
+        assert _err(ys, ref) <= TOL

@@ -1,0 +1,196 @@
+"""Host-side checks of libqgemm.so that need no GPU.
+
+* The library loads and exports every function include/qgemm.h declares.
+* qg_packed_sizes / qg_canonical_size follow the documented geometry.
+* qg_pack_host moves bits only: reading the planar planes back with an
+  independent reader written from the layout description gives, for every
+  weight, the code and scale of the canonical bytes, hence the oracle's value.
+* Argument errors come back as status codes before any launch (only rejected
+  argument sets are used, so nothing reaches a device).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import quantized_prefill_gemm_codec_amd as qg
+from golden_io import all_cases
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "qgemm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(q\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = qg.lib()
+    names = _header_functions()
+    assert set(names) >= {"qgemm_prefill", "qgemm_swiglu", "qgemv_decode", "qg_pack_host", "qg_dequant"}
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(qg.EXPORTS)
+    assert qg.qg_version() == 100
+
+
+@pytest.mark.parametrize("codec,n,k", [(1, 8192, 2048), (1, 40, 96), (2, 14336, 4096), (3, 4096, 4096), (3, 33, 128)])
+def test_sizes(codec, n, k):
+    qs, sc = qg.qg_packed_sizes(codec, n, k)
+    groups, ksteps = -(-n // 32), -(-k // 64)
+    code_bytes = 8 if codec == 3 else 16
+    assert qs == groups * ksteps * 64 * code_bytes
+    if codec == 1:
+        assert sc == groups * ksteps * 64 * 2
+    elif codec == 2:
+        assert sc == groups * ksteps * 32 * 4
+    else:
+        assert sc == groups * (k // 128) * 32 * 2
+    assert qg.qg_canonical_size(codec, n, k) == synth.canonical_bytes(codec, n, k)
+
+
+def _read_planar(codec, n, k, qs, sc):
+    """Independent reader of the planar layout -> (codes [n,k], scale, bias)."""
+    groups, ksteps = -(-n // 32), -(-k // 64)
+    cb = 8 if codec == 3 else 16
+    lanes = qs.reshape(groups, ksteps, 64, cb)
+    codes = np.zeros((groups * 32, ksteps * 64), np.int64)
+    for j in range(32):
+        if codec == 3:
+            dw, e = divmod(j, 16)
+            bit = 2 * (e // 2) + 16 * (e % 2)
+            byte = lanes[..., 4 * dw + bit // 8].astype(np.int64)
+            q = (byte >> (bit % 8)) & 3
+        else:
+            dw, e = divmod(j, 8)
+            bit = 4 * (e // 2) + 16 * (e % 2)
+            byte = lanes[..., 4 * dw + bit // 8].astype(np.int64)
+            q = (byte >> (bit % 8)) & 15
+        # q: [groups, ksteps, 64 lanes]; lane l = 32 g + i owns row 32 r + i, k = 64 t + 32 g + j
+        for g in range(2):
+            blk = q[:, :, 32 * g:32 * g + 32]                 # [groups, ksteps, 32 rows]
+            rows = blk.transpose(0, 2, 1).reshape(groups * 32, ksteps)
+            codes[:, np.arange(ksteps) * 64 + 32 * g + j] = rows
+    codes = codes[:n, :k]
+    kk = np.arange(k)
+    rr = np.arange(n)
+    if codec == 1:
+        d = sc.view(np.float16).reshape(groups, ksteps, 2, 32)
+        blk = kk // 32
+        scale = d[rr[:, None] // 32, blk[None, :] // 2, blk[None, :] % 2, rr[:, None] % 32]
+        return codes, scale.astype(np.float64), None
+    if codec == 2:
+        sb = sc.view(np.float16).reshape(groups, ksteps, 32, 2)
+        s = sb[rr[:, None] // 32, kk[None, :] // 64, rr[:, None] % 32, 0]
+        b = sb[rr[:, None] // 32, kk[None, :] // 64, rr[:, None] % 32, 1]
+        return codes, s.astype(np.float64), b.astype(np.float64)
+    d = sc.view(np.float16).reshape(groups, k // 128, 32)
+    scale = d[rr[:, None] // 32, kk[None, :] // 128, rr[:, None] % 32]
+    return codes, scale.astype(np.float64), None
+
+
+def _value(codec, codes, scale, bias):
+    if codec == 1:
+        return (codes - 8) * scale
+    if codec == 2:
+        return codes * scale + bias
+    return (codes - 1) * scale
+
+
+@pytest.mark.parametrize("codec,n,k", [(1, 40, 96), (1, 64, 64), (2, 33, 192), (3, 37, 256), (3, 32, 128)])
+def test_pack_roundtrip_random(codec, n, k):
+    canon = synth.gen_weight(codec, n, k, 77)
+    qs, sc = qg.qg_pack_host(codec, n, k, canon)
+    codes, scale, bias = _read_planar(codec, n, k, qs, sc)
+    assert np.array_equal(_value(codec, codes, scale, bias), oracle.decode(codec, canon, n, k))
+
+
+CASES = all_cases()
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_pack_roundtrip_golden(case):
+    codec, n, k = case["codec"], case["n"], case["k"]
+    canon = np.array(case["bytes"], np.uint8)
+    qs, sc = qg.qg_pack_host(codec, n, k, canon)
+    codes, scale, bias = _read_planar(codec, n, k, qs, sc)
+    want = np.array(case["expect"], np.float64).reshape(n, k)
+    assert np.array_equal(_value(codec, codes, scale, bias), want)
+
+
+def test_pack_padding_decodes_to_zero():
+    codec, n, k = 1, 40, 96       # N padded to 64 rows, K to 128
+    qs, sc = qg.qg_pack_host(codec, n, k, synth.gen_weight(codec, n, k, 5))
+    d = sc.view(np.float16).reshape(2, 2, 2, 32)
+    assert np.all(d[1, :, :, 8:] == 0)          # rows 40..63
+    assert np.all(d[:, 1, 1, :] == 0)           # k 96..127 (block 3)
+
+
+def test_pack_errors():
+    buf = np.zeros(64, np.uint8)
+    L = qg.lib()
+    p = buf.ctypes.data
+    assert L.qg_pack_host(9, 1, 32, p, 64, p, p) == -2
+    assert L.qg_pack_host(1, 1, 48, p, 64, p, p) == -3
+    assert L.qg_pack_host(3, 1, 64, p, 64, p, p) == -3
+    assert L.qg_pack_host(1, 0, 32, p, 64, p, p) == -3
+    assert L.qg_pack_host(1, 2, 32, p, 35, p, p) == -7
+    assert L.qg_pack_host(1, 1, 32, None, 64, p, p) == -1
+    with pytest.raises(qg.QGError):
+        qg.qg_packed_sizes(2, 4, 96)
+
+
+def _w(codec=1, n=64, k=64, qs=0x10000, sc=0x20000, flags=0):
+    return qg.qg_weight(codec, flags, n, k, qs, sc)
+
+
+FAKE = 0x100000    # aligned, non-null; never dereferenced: every call below is rejected
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(w=_w(codec=7)), -2),
+    (dict(w=_w(k=48)), -3),
+    (dict(w=_w(flags=1)), -3),
+    (dict(w=_w(qs=0)), -1),
+    (dict(w=_w(qs=0x10008)), -4),
+    (dict(m=0), -3),
+    (dict(ldx=60), -3),
+    (dict(ldx=68), -4),
+    (dict(ldy=12), -3),
+    (dict(x=FAKE + 8), -4),
+    (dict(x=0), -1),
+    (dict(y=0), -1),
+])
+def test_gemm_argument_errors(args, status):
+    L = qg.lib()
+    w = args.get("w", _w())
+    m = args.get("m", 4)
+    x = args.get("x", FAKE)
+    y = args.get("y", FAKE)
+    ldx = args.get("ldx", 64)
+    ldy = args.get("ldy", 64)
+    assert L.qgemm_prefill(ctypes.byref(w), x, m, ldx, y, ldy, None) == status
+    assert L.qgemv_decode(ctypes.byref(w), x, m, ldx, y, ldy, None) == status
+    assert L.qgemm_swiglu(ctypes.byref(w), ctypes.byref(w), x, m, ldx, y, ldy, None) == status
+
+
+def test_gemv_rejects_large_m_and_swiglu_mismatch():
+    L = qg.lib()
+    w = _w()
+    assert L.qgemv_decode(ctypes.byref(w), FAKE, 65, 64, FAKE, 64, None) == -3
+    pairs = [(_w(), _w(n=96)), (_w(), _w(k=128)), (_w(k=128), _w(codec=3, k=128))]
+    for wg, wu in pairs:
+        assert (wg.codec, wg.n, wg.k) != (wu.codec, wu.n, wu.k)
+        assert L.qgemm_swiglu(ctypes.byref(wg), ctypes.byref(wu), FAKE, 4, wg.k, FAKE, 128, None) == -5
+    assert L.qg_dequant(ctypes.byref(_w()), FAKE, 60, None) == -3
+    assert L.qg_dequant(ctypes.byref(_w(codec=0)), FAKE, 64, None) == -2
+
+
+def test_status_strings():
+    for st in qg.STATUS:
+        assert qg.lib().qg_status_str(st)
