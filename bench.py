@@ -77,20 +77,28 @@ class Prepared:
             xd = torch.from_numpy(x).cuda()
             ldy = 8 * ((wl.n + 7) // 8)
             y = torch.empty((wl.m, ldy), dtype=torch.float16, device="cuda")
-            self.sets.append((ws, xd, y))
+            self.sets.append((ws, xd, y, ldy))
         self.qg = qg
+        # The timed loop calls the C-ABI entry points with argument tuples built
+        # once (same functions the binding wraps), so launches outpace the GPU.
+        L = qg.lib()
+        stream = qg._stream(None)
+        self.calls = []
+        for ws, xd, y, ldy in self.sets:
+            if wl.op == "swiglu":
+                self.calls.append((L.qgemm_swiglu, (ws[0].desc, ws[1].desc, xd.data_ptr(), wl.m, wl.k,
+                                                    y.data_ptr(), ldy, stream)))
+            elif wl.op == "gemv":
+                self.calls.append((L.qgemv_decode, (ws[0].desc, xd.data_ptr(), wl.m, wl.k, y.data_ptr(), ldy, stream)))
+            else:
+                self.calls.append((L.qgemm_prefill, (ws[0].desc, xd.data_ptr(), wl.m, wl.k, y.data_ptr(), ldy, stream)))
 
     def launch(self, i):
-        ws, xd, y = self.sets[i % self.rotate]
-        qg, wl = self.qg, self.wl
-        out = y[:, :wl.n]
-        if wl.op == "swiglu":
-            qg.qgemm_swiglu(ws[0], ws[1], xd, out=out)
-        elif wl.op == "gemv":
-            qg.qgemv_decode(ws[0], xd, out=out)
-        else:
-            qg.qgemm_prefill(ws[0], xd, out=out)
-        return out
+        fn, args = self.calls[i % self.rotate]
+        st = fn(*args)
+        if st != 0:
+            raise RuntimeError(f"{fn.__name__} returned status {st}")
+        return self.sets[i % self.rotate][2][:, :self.wl.n]
 
 
 def time_launches(torch, prep, steps, warmup):
@@ -119,15 +127,20 @@ def roofline(wl, ms, traffic=None):
 
 
 def load_traffic(name):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if current."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from the
+    committed rocprofv3 summary; None if absent or taken with other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     if not os.path.exists(path):
         return None
+    sha = kernel_source_hash()
     with open(path) as f:
-        t = json.load(f)
-    if t.get("kernel_source_sha") != kernel_source_hash():
-        return None
-    return t.get("bytes_per_launch")
+        for line in f:
+            if line.startswith("#") or "workload=" not in line:
+                continue
+            kv = dict(tok.split("=", 1) for tok in line.split() if "=" in tok and not tok.startswith('kernel="'))
+            if kv.get("workload") == name and kv.get("kernel_sha") == sha:
+                return int(kv["bytes_per_launch"])
+    return None
 
 
 def cpu_baseline(torch, prep, target_s=12.0):
@@ -174,6 +187,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -190,6 +205,17 @@ def main():
         print("no HIP device visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+
+    if args.copy_calib:
+        nbytes = args.copy_calib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy_calibration", "bytes_read": nbytes, "bytes_written": nbytes,
+                          "launches": args.steps}), flush=True)
+        return
 
     wl = synth.WORKLOADS[args.workload]
     prep = Prepared(torch, qg, wl, args.rotate)

@@ -59,6 +59,9 @@ __device__ __forceinline__ float silu_mul(float g, float u)
     return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100, SG_DS_WR = 0x200;
+
 template <int CODEC, int BM, int BN, int WM, int WN, bool SWIGLU>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
 {
@@ -66,14 +69,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
     constexpr int NMAT = SWIGLU ? 2 : 1;
-    constexpr int XCH = BM * 8 / NT;
-    static_assert(FM >= 1 && FN >= 1 && XCH >= 1 && (BM * 8) % NT == 0, "tile");
+    constexpr int XCH = BM * 8 / NT;        // 16-byte X chunks per thread per k-step
+    constexpr int STAGE = BM * 128;         // bytes of one X stage in LDS
+    static_assert(FM >= 1 && FN >= 1 && XCH >= 1 && (BM * 8) % NT == 0 && TM % 64 == 0 || FM == 1, "tile");
 
-    __shared__ u32x4 lds_x[2][BM * 8];
+    __shared__ u32x4 lds_x[2 * BM * 8];
+    char *lds = reinterpret_cast<char *>(lds_x);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM, wn = wave / WM;
     const int i = lane & 31, g = lane >> 5;
     const uint32_t magic = magic1024();
@@ -81,44 +86,73 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
     const int tile = remap_tile(blockIdx.x, a.tiles_m * a.tiles_n);
     const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
     const int m0 = tm * BM, n0 = tn * BN;
+    const int last = a.ksteps - 1;
+    const int ktail = a.k & 63;             // 32 when the last k-step is half empty (Q4_0)
 
-    const __amdgpu_buffer_rsrc_t xr_rsrc = make_rsrc(a.x, a.x_bytes);
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, a.x_bytes);
     const PlaneRsrc w0 = plane_rsrc(a.w0);
     const PlaneRsrc w1 = plane_rsrc(SWIGLU ? a.w1 : a.w0);
 
-    // per-thread X chunk coordinates (fixed across k-steps)
-    uint32_t xoff[XCH];
-    int xlds[XCH];
+    // X staging: thread chunk c covers tile row r = (tid + NT c) / 8 and the
+    // 16-byte column ch = tid % 8; rows past M and the K tail get out-of-range
+    // vector offsets (zero fill), the k-step goes in the scalar offset.
+    const int ch = tid & 7;
+    uint32_t xv[XCH], xvt[XCH], xl[XCH];
 #pragma unroll
     for (int c = 0; c < XCH; ++c) {
-        const int q = tid + NT * c, r = q >> 3, ch = q & 7;
-        xoff[c] = (uint32_t(m0 + r) * uint32_t(a.ldx) + uint32_t(ch * 8)) * 2u;
-        xlds[c] = r * 8 + (ch ^ swz(r));
+        const int r = (tid + NT * c) >> 3;
+        xv[c] = (m0 + r < a.m) ? (uint32_t(m0 + r) * uint32_t(a.ldx) + uint32_t(ch * 8)) * 2u : OOB;
+        xvt[c] = (ch * 8 < ktail) ? xv[c] : OOB;
+        xl[c] = uint32_t(r * 8 + (ch ^ swz(r))) * 16u;
     }
-    u32x4 xr[XCH];
-    auto load_x = [&](int t) {
-#pragma unroll
-        for (int c = 0; c < XCH; ++c) {
-            const int col = t * 64 + ((tid + NT * c) & 7) * 8;
-            const uint32_t off = col < a.k ? xoff[c] + uint32_t(t) * 128u : OOB;
-            xr[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr_rsrc, off, 0, 0));
-        }
-    };
-    auto store_x = [&](int buf) {
+    auto load_x = [&](int t, u32x4(&dst)[XCH]) {
+        const bool tail = (t == last) && ktail != 0;
 #pragma unroll
         for (int c = 0; c < XCH; ++c)
-            lds_x[buf][xlds[c]] = xr[c];
+            dst[c] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, tail ? xvt[c] : xv[c], uint32_t(t) * 128u, 0));
+    };
+    auto store_x = [&](int buf, const u32x4(&src)[XCH]) {
+#pragma unroll
+        for (int c = 0; c < XCH; ++c)
+            *reinterpret_cast<u32x4 *>(lds + buf * STAGE + xl[c]) = src[c];
+    };
+
+    // MFMA B-operand reads: row r = wm*TM + fm*32 + i, 16-byte column 4g + s;
+    // swz(r) depends only on i and the parity of fm.
+    uint32_t rb[2][4];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int r = wm * TM + p * 32 + i;
+            rb[p][s] = uint32_t(r * 8 + ((4 * g + s) ^ swz(r))) * 16u;
+        }
+    auto read_x = [&](int buf, int s, f16x8(&xf)[FM]) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+            xf[fm] = *reinterpret_cast<const f16x8 *>(lds + buf * STAGE + rb[fm & 1][s] + (fm & ~1) * 4096);
     };
 
     const int rg0 = (n0 + wn * TN) >> 5;
-    LaneCodes<CODEC> cw[NMAT][FN];
+    LaneOffsets lo[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+        lo[fn] = lane_offsets<CODEC>(rg0 + fn, a.groups, lane);
     auto load_w = [&](int t, LaneCodes<CODEC>(&dst)[NMAT][FN]) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-            dst[0][fn] = load_lane<CODEC>(w0, rg0 + fn, t, a.ksteps, a.kb128, lane);
+            dst[0][fn] = load_lane<CODEC>(w0, lo[fn], rg0 + fn, t, a.ksteps, a.kb128);
             if constexpr (SWIGLU)
-                dst[NMAT - 1][fn] = load_lane<CODEC>(w1, rg0 + fn, t, a.ksteps, a.kb128, lane);
+                dst[NMAT - 1][fn] = load_lane<CODEC>(w1, lo[fn], rg0 + fn, t, a.ksteps, a.kb128);
         }
+    };
+    auto unpack = [&](const LaneCodes<CODEC>(&cw)[NMAT][FN], int s, f16x8(&wf)[NMAT][FN]) {
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                wf[mt][fn] = unpack_substep<CODEC>(cw[mt][fn], s, magic);
     };
 
     f32x16 acc[NMAT][FM][FN];
@@ -132,45 +166,70 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
                 for (int e = 0; e < 16; ++e)
                     acc[mt][fm][fn][e] = 0.0f;
 
-    load_x(0);
-    load_w(0, cw);
-    store_x(0);
-    __syncthreads();
-
-    for (int t = 0; t < a.ksteps; ++t) {
-        const int buf = t & 1;
-        // prefetch step t+1 (past the end these read harmless in-range or zero data)
-        LaneCodes<CODEC> cn[NMAT][FN];
-        load_x(t + 1);
-        load_w(t + 1, cn);
+    // One k-step: codes for t are in cw, X(t) is in LDS stage buf.  Fetch
+    // step t+1 (clamped: every scalar offset stays inside its buffer), then
+    // run the four 16-deep sub-steps, preparing sub-step s+1 (LDS reads and
+    // unpack) while the MFMAs of sub-step s issue.
+    auto step = [&](int t, int buf, const LaneCodes<CODEC>(&cw)[NMAT][FN], LaneCodes<CODEC>(&cn)[NMAT][FN]) {
+        const int tnx = min(t + 1, last);
+        u32x4 xr[XCH];
+        load_x(tnx, xr);
+        load_w(tnx, cn);
+        f16x8 xf[2][FM];
+        f16x8 wf[2][NMAT][FN];
+        read_x(buf, 0, xf[0]);
+        unpack(cw, 0, wf[0]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            f16x8 wf[NMAT][FN];
+            const int cur = s & 1;
+            if (s < 3) {
+                read_x(buf, s + 1, xf[cur ^ 1]);
+                unpack(cw, s + 1, wf[cur ^ 1]);
+            }
 #pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt)
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
-                    wf[mt][fn] = unpack_substep<CODEC>(cw[mt][fn], s, magic);
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int r = wm * TM + fm * 32 + i;
-                const f16x8 xf = __builtin_bit_cast(f16x8, lds_x[buf][r * 8 + ((4 * g + s) ^ swz(r))]);
+            for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
                 for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
                     for (int fn = 0; fn < FN; ++fn)
-                        acc[mt][fm][fn] =
-                            __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[mt][fn], xf, acc[mt][fm][fn], 0, 0, 0);
+                        acc[mt][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[cur][mt][fn], xf[cur][fm],
+                                                                                 acc[mt][fm][fn], 0, 0, 0);
+            {
+                constexpr int NMF = FM * FN * NMAT;
+                constexpr int NV = (NMAT * FN * 16 + NMF - 1) / NMF;
+#pragma unroll
+                for (int j = 0; j < NMF; ++j) {
+                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                    if (s < 3)
+                        __builtin_amdgcn_sched_group_barrier(SG_VALU, NV, 0);
+                    if (s < 3 && j < FM)
+                        __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+                    if (s == 0 && j < XCH + 2 * NMAT * FN)
+                        __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+                    if (s == 3 && j < XCH)
+                        __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
+                }
             }
         }
-        store_x(buf ^ 1);
-#pragma unroll
-        for (int mt = 0; mt < NMAT; ++mt)
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-                cw[mt][fn] = cn[mt][fn];
+        store_x(buf ^ 1, xr);
         __syncthreads();
+    };
+
+    {
+        u32x4 xr0[XCH];
+        load_x(0, xr0);
+        store_x(0, xr0);
     }
+    LaneCodes<CODEC> ca[NMAT][FN], cb[NMAT][FN];
+    load_w(0, ca);
+    __syncthreads();
+    int t = 0;
+    for (; t + 1 < a.ksteps; t += 2) {
+        step(t, 0, ca, cb);
+        step(t + 1, 1, cb, ca);
+    }
+    if (t < a.ksteps)
+        step(t, 0, ca, cb);
 
     // Epilogue: lane (i, g), register 4q+e of block (fm, fn) holds
     // C[n = fn*32 + 8q + 4g + e][m = fm*32 + i].
@@ -194,9 +253,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
                         v[e] = acc[0][fm][fn][4 * q + e];
                 }
                 if (n + 3 < a.n) {
-                    f16x2 lo = {_Float16(v[0]), _Float16(v[1])};
-                    f16x2 hi = {_Float16(v[2]), _Float16(v[3])};
-                    *reinterpret_cast<u32x2 *>(yrow + n) = u32x2{as_u32(lo), as_u32(hi)};
+                    f16x2 lo2 = {_Float16(v[0]), _Float16(v[1])};
+                    f16x2 hi2 = {_Float16(v[2]), _Float16(v[3])};
+                    *reinterpret_cast<u32x2 *>(yrow + n) = u32x2{as_u32(lo2), as_u32(hi2)};
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
@@ -207,6 +266,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
         }
     }
 }
+
 
 template <int CODEC, int BM, int BN, int WM, int WN, bool SWIGLU>
 hipError_t launch_tile(const GemmProblem &p, hipStream_t stream)

@@ -54,7 +54,8 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
     float *xsum = reinterpret_cast<float *>(smem + MM * kchunks);   // [MM][2*ksteps]
     float *red = xsum + (CODEC == MLX4_G64 ? MM * 2 * a.ksteps : 0);  // [4][MM][32]
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i = lane & 31, g = lane >> 5;
     const int rg = blockIdx.x;
     const uint32_t magic = magic1024();
@@ -65,10 +66,11 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
     const int t1 = min(a.ksteps, t0 + per);
 
     // first batch of codes before the X staging, to overlap the latencies
+    const LaneOffsets lo = lane_offsets<CODEC>(rg, a.groups, lane);
     LaneCodes<CODEC> lc[GEMV_PF];
 #pragma unroll
     for (int u = 0; u < GEMV_PF; ++u)
-        lc[u] = load_lane<CODEC>(w, rg, min(t0 + u, a.ksteps - 1), a.ksteps, a.kb128, lane);
+        lc[u] = load_lane<CODEC>(w, lo, rg, min(t0 + u, a.ksteps - 1), a.ksteps, a.kb128);
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
     for (int q = tid; q < MM * kchunks; q += GEMV_NT) {
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
             // refill this slot with the k-step one batch ahead
             const int tn = tb + GEMV_PF + u;
             if (tn < t1)
-                lc[u] = load_lane<CODEC>(w, rg, tn, a.ksteps, a.kb128, lane);
+                lc[u] = load_lane<CODEC>(w, lo, rg, tn, a.ksteps, a.kb128);
         }
     }
 
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(Planes wp, int n, int k, i
     const int i = lane & 31, g = lane >> 5;
     const uint32_t magic = magic1024();
     const PlaneRsrc w = plane_rsrc(wp);
-    const LaneCodes<CODEC> lc = load_lane<CODEC>(w, rg, t, ksteps, kb128, lane);
+    const LaneCodes<CODEC> lc = load_lane<CODEC>(w, lane_offsets<CODEC>(rg, groups, lane), rg, t, ksteps, kb128);
     const int row = rg * 32 + i;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {

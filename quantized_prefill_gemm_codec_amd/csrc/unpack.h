@@ -143,30 +143,60 @@ __device__ __forceinline__ PlaneRsrc plane_rsrc(const Planes &w)
     return r;
 }
 
-__device__ __forceinline__ _Float16 load_f16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+__device__ __forceinline__ _Float16 load_f16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
-    return __builtin_bit_cast(_Float16, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+    return __builtin_bit_cast(_Float16, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
+}
+
+// Per-lane vector offsets of one row group's chunks.  A row group past the
+// end of the matrix gets out-of-range offsets, so its loads return zero
+// codes with zero scales (weight 0).  Vector offsets are what the hardware
+// range-checks, so the chunk-dependent part that goes in the scalar offset
+// must itself stay inside the plane (callers keep 0 <= t < ksteps).
+struct LaneOffsets {
+    uint32_t q, s;
+};
+
+template <int CODEC>
+__device__ __forceinline__ LaneOffsets lane_offsets(int rg, int groups, int lane)
+{
+    LaneOffsets o;
+    const uint32_t i = uint32_t(lane & 31);
+    if (rg >= groups) {
+        o.q = OOB;
+        o.s = OOB;
+    } else if constexpr (CODEC == Q2_0) {
+        o.q = uint32_t(lane) * 8;
+        o.s = i * 2;
+    } else if constexpr (CODEC == Q4_0) {
+        o.q = uint32_t(lane) * 16;
+        o.s = uint32_t(lane) * 2;
+    } else {
+        o.q = uint32_t(lane) * 16;
+        o.s = i * 4;
+    }
+    return o;
 }
 
 // Load the chunk (row group rg, k-step t) codes and scales a lane owns.
 // `ksteps` = padded K / 64, `kb128` = K / 128 (Q2_0 scale plane pitch).
-// Row groups past the end read as zero codes with zero scales (weight 0).
+// rg and t are wave-uniform: the chunk part of each address is a scalar
+// offset, the lane part a fixed vector offset.
 template <int CODEC>
-__device__ __forceinline__ LaneCodes<CODEC> load_lane(const PlaneRsrc &w, int rg, int t, int ksteps, int kb128,
-                                                      int lane)
+__device__ __forceinline__ LaneCodes<CODEC> load_lane(const PlaneRsrc &w, LaneOffsets o, int rg, int t, int ksteps,
+                                                      int kb128)
 {
     LaneCodes<CODEC> lc;
     const uint32_t chunk = uint32_t(rg) * uint32_t(ksteps) + uint32_t(t);
-    const uint32_t i = uint32_t(lane & 31);
     if constexpr (CODEC == Q2_0) {
-        lc.c = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(w.qs, (chunk * 64 + lane) * 8, 0, 0));
-        lc.d = load_f16(w.sc, ((uint32_t(rg) * kb128 + uint32_t(t >> 1)) * 32 + i) * 2);
+        lc.c = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(w.qs, o.q, chunk * 512, 0));
+        lc.d = load_f16(w.sc, o.s, (uint32_t(rg) * kb128 + uint32_t(t >> 1)) * 64);
     } else {
-        lc.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, (chunk * 64 + lane) * 16, 0, 0));
+        lc.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 1024, 0));
         if constexpr (CODEC == Q4_0)
-            lc.d = load_f16(w.sc, (chunk * 64 + lane) * 2);
+            lc.d = load_f16(w.sc, o.s, chunk * 128);
         else
-            lc.sb = __builtin_amdgcn_raw_buffer_load_b32(w.sc, (chunk * 32 + i) * 4, 0, 0);
+            lc.sb = __builtin_amdgcn_raw_buffer_load_b32(w.sc, o.s, chunk * 128, 0);
     }
     return lc;
 }
