@@ -268,6 +268,355 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
 }
 
 
+// ---------------------------------------------------------------------------
+// Large-tile kernel: every operand reaches LDS by hardware DMA.
+//
+// X tiles, code chunks and scale records of k-step t+2 are copied from HBM
+// straight into LDS stage (t+2) % 3 with buffer_load ... lds (no registers,
+// no ds_write), two k-steps ahead of use.  These loads are issued from inline
+// assembly so that the only wait on them is the explicit vmcnt before the
+// end-of-step barrier (the compiler would otherwise drain all of them before
+// every LDS read).  Waves then read their MFMA operands from LDS: X fragments
+// (B operand) and their own row groups' code slices (A operand, unpacked in
+// registers).  The epilogue converts the accumulators to fp16 into LDS and
+// writes whole rows of Y with 16-byte stores.
+// ---------------------------------------------------------------------------
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// M0 carries the LDS destination of a DMA load; no other code in these kernels
+// uses M0, so clobbering it is safe.
+__device__ __forceinline__ void dma_b128(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+                 "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+                 "s"(lds)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Raw buffer descriptor words (base, num_records, gfx9 raw-buffer flags) for
+// the inline-assembly loads; out-of-range vector offsets read zero.
+__device__ __forceinline__ u32x4 rsrc_words(const void *p, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    return u32x4{uint32_t(a), uint32_t(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+
+// s_waitcnt vmcnt(N) leaving the LDS and export counters alone (gfx9 encoding).
+template <int N> __device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void *p)
+{
+    return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)(p)));
+}
+
+// Tile order: each XCD gets a contiguous run of tiles, and runs are laid out
+// in groups of GM m-tiles so that the tiles resident on one XCD at a time
+// share both X rows and weight row groups in its L2.
+__device__ __forceinline__ void grouped_tile(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    const int nt = tiles_m * tiles_n;
+    int l = bid;
+    if ((nt & 7) == 0)
+        l = (bid & 7) * (nt >> 3) + (bid >> 3);
+    constexpr int GM = 4;
+    const int per_group = GM * tiles_n;
+    const int group = l / per_group;
+    const int first = group * GM;
+    const int gsm = min(tiles_m - first, GM);
+    const int idx = l - group * per_group;
+    tm = first + idx % gsm;
+    tn = idx / gsm;
+}
+
+template <int CODEC, int BM, int BN, int WM, int WN, bool SWIGLU>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_kernel(GemmArgs a)
+{
+    constexpr int NW = WM * WN, NT = 64 * NW;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int NMAT = SWIGLU ? 2 : 1;
+    constexpr int RG = BN / 32;                            // row groups per matrix per tile
+    constexpr int CB = CODEC == Q2_0 ? 8 : 16;             // code bytes per lane per chunk
+    constexpr int WCH = 64 * CB;                           // bytes per (row group, k-step) chunk
+    constexpr int SB = CODEC == Q2_0 ? 64 : 128;           // scale bytes per (row group, k-step)
+    constexpr int X_OFF = 0, X_BYTES = BM * 128;
+    constexpr int W_OFF = X_BYTES, W_BYTES = NMAT * RG * WCH;
+    constexpr int S_OFF = W_OFF + W_BYTES, S_BYTES = NMAT * RG * SB;
+    constexpr int STAGE = S_OFF + S_BYTES;
+    constexpr int NSTAGE = 3;
+    constexpr int EPI_BYTES = BM * BN * 2;
+    constexpr int LDS_BYTES = NSTAGE * STAGE > EPI_BYTES ? NSTAGE * STAGE : EPI_BYTES;
+    constexpr int NX = X_BYTES / 1024, NWI = W_BYTES / 1024, NSI = S_BYTES / 256;   // DMA instructions per stage
+    constexpr int XPW = NX / NW, WPW = (NWI + NW - 1) / NW, SPW = (NSI + NW - 1) / NW;
+    constexpr int VMIN = XPW + NWI / NW + NSI / NW;         // fewest DMA ops any wave issues per stage
+    static_assert(NX % NW == 0 && W_BYTES % 1024 == 0 && S_BYTES % 256 == 0 && STAGE % 16 == 0, "dma tiling");
+    static_assert(FM % 2 == 0 && VMIN >= 1, "tile");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+    const uint32_t lds0 = lds_u32(lds);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WM, wn = wave / WM;
+    const int i = lane & 31, g = lane >> 5;
+    const uint32_t magic = magic1024();
+
+    int tm, tn;
+    grouped_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int last = a.ksteps - 1;
+    const int ktail = a.k & 63;
+    const int rg0 = n0 >> 5;
+
+    const u32x4 xr = rsrc_words(a.x, a.x_bytes);
+    const u32x4 q0 = rsrc_words(a.w0.qs, a.w0.qs_bytes), s0 = rsrc_words(a.w0.scales, a.w0.scale_bytes);
+    const u32x4 q1 = SWIGLU ? rsrc_words(a.w1.qs, a.w1.qs_bytes) : q0;
+    const u32x4 s1 = SWIGLU ? rsrc_words(a.w1.scales, a.w1.scale_bytes) : s0;
+
+    // ---- per-lane DMA source offsets (fixed across k-steps) ----
+    // X: instruction j fills LDS slots 64j..64j+63; slot p holds tile row
+    // p/8, 16-byte column (p%8) ^ swz(row).
+    uint32_t xv[XPW], xvt[XPW];
+#pragma unroll
+    for (int u = 0; u < XPW; ++u) {
+        const int p = (wave + NW * u) * 64 + lane;
+        const int r = p >> 3, ch = (p & 7) ^ swz(r);
+        xv[u] = (m0 + r < a.m) ? (uint32_t(m0 + r) * uint32_t(a.ldx) + uint32_t(ch * 8)) * 2u : OOB;
+        xvt[u] = (ch * 8 < ktail) ? xv[u] : OOB;
+    }
+    // codes: instruction j covers chunk bytes [1024 j, 1024 j + 1024) of the
+    // stage's code area (one 4-bit chunk, or two 2-bit chunks)
+    uint32_t wv[WPW];
+    int wmat[WPW];
+#pragma unroll
+    for (int u = 0; u < WPW; ++u) {
+        const int j = wave + NW * u;
+        const int c = (CB == 16) ? j : 2 * j + (lane >> 5);
+        const int mt = c / RG, rg = c % RG;
+        const uint32_t lo = (CB == 16) ? uint32_t(lane) * 16 : uint32_t(lane & 31) * 16;
+        wmat[u] = ((CB == 16) ? j : 2 * j) / RG;     // wave-uniform: RG is even
+        (void)mt;
+        wv[u] = (j < NWI && rg0 + rg < a.groups) ? uint32_t(rg0 + rg) * uint32_t(a.ksteps) * WCH + lo : OOB;
+    }
+    // scales: dword instruction j covers bytes [256 j, 256 j + 256) of the
+    // stage's scale area, SB bytes per (matrix, row group)
+    uint32_t sv[SPW];
+    int smat[SPW];
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+        const int j = wave + NW * u;
+        const int b = 256 * j + 4 * lane;
+        const int c = b / SB, o = b % SB;
+        const int rg = c % RG;
+        smat[u] = (256 * j / SB) / RG;              // wave-uniform: chunks never straddle matrices
+        const uint32_t pitch = CODEC == Q2_0 ? uint32_t(a.kb128) * 64u : uint32_t(a.ksteps) * 128u;
+        sv[u] = (j < NSI && rg0 + rg < a.groups) ? uint32_t(rg0 + rg) * pitch + uint32_t(o) : OOB;
+    }
+
+    auto issue_stage = [&](int t, int stage) {
+        const uint32_t base = lds0 + uint32_t(stage * STAGE);
+        const bool tail = (t == last) && ktail != 0;
+#pragma unroll
+        for (int u = 0; u < XPW; ++u)
+            dma_b128(xr, tail ? xvt[u] : xv[u], uint32_t(t) * 128u,
+                     base + X_OFF + uint32_t((wave + NW * u) * 1024));
+#pragma unroll
+        for (int u = 0; u < WPW; ++u) {
+            const int j = wave + NW * u;
+            if (j < NWI)
+                dma_b128(wmat[u] ? q1 : q0, wv[u], uint32_t(t) * WCH, base + W_OFF + uint32_t(j * 1024));
+        }
+#pragma unroll
+        for (int u = 0; u < SPW; ++u) {
+            const int j = wave + NW * u;
+            const uint32_t so = CODEC == Q2_0 ? uint32_t(t >> 1) * 64u : uint32_t(t) * 128u;
+            if (j < NSI)
+                dma_b32(smat[u] ? s1 : s0, sv[u], so, base + S_OFF + uint32_t(j * 256));
+        }
+    };
+
+    // ---- MFMA operand reads from a stage ----
+    uint32_t rb[2][4];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int r = wm * TM + p * 32 + i;
+            rb[p][s] = uint32_t(r * 8 + ((4 * g + s) ^ swz(r))) * 16u;
+        }
+    auto read_x = [&](const char *st, int s, f16x8(&xf)[FM]) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+            xf[fm] = *reinterpret_cast<const f16x8 *>(st + X_OFF + rb[fm & 1][s] + (fm & ~1) * 4096);
+    };
+    auto read_w = [&](const char *st, LaneCodes<CODEC>(&cw)[NMAT][FN]) {
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int c = mt * RG + wn * FN + fn;
+                const char *wp = st + W_OFF + c * WCH + lane * CB;
+                const char *sp = st + S_OFF + c * SB;
+                if constexpr (CODEC == Q2_0) {
+                    cw[mt][fn].c = *reinterpret_cast<const u32x2 *>(wp);
+                    cw[mt][fn].d = *reinterpret_cast<const _Float16 *>(sp + i * 2);
+                } else {
+                    cw[mt][fn].c = *reinterpret_cast<const u32x4 *>(wp);
+                    if constexpr (CODEC == Q4_0)
+                        cw[mt][fn].d = *reinterpret_cast<const _Float16 *>(sp + lane * 2);
+                    else
+                        cw[mt][fn].sb = *reinterpret_cast<const uint32_t *>(sp + i * 4);
+                }
+            }
+    };
+    auto unpack = [&](const LaneCodes<CODEC>(&cw)[NMAT][FN], int s, f16x8(&wf)[NMAT][FN]) {
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                wf[mt][fn] = unpack_substep<CODEC>(cw[mt][fn], s, magic);
+    };
+
+    f32x16 acc[NMAT][FM][FN];
+#pragma unroll
+    for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[mt][fm][fn][e] = 0.0f;
+
+    issue_stage(0, 0);
+    issue_stage(min(1, last), 1);
+    wait_vmcnt<VMIN>();
+    __syncthreads();
+    LaneCodes<CODEC> cw[NMAT][FN];
+    read_w(lds, cw);
+
+    for (int t = 0; t < a.ksteps; ++t) {
+        const int st = t % NSTAGE;
+        issue_stage(min(t + 2, last), (t + 2) % NSTAGE);
+        const char *sp = lds + st * STAGE;
+        f16x8 xf[2][FM];
+        f16x8 wf[2][NMAT][FN];
+        read_x(sp, 0, xf[0]);
+        unpack(cw, 0, wf[0]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int cur = s & 1;
+            if (s < 3) {
+                read_x(sp, s + 1, xf[cur ^ 1]);
+                unpack(cw, s + 1, wf[cur ^ 1]);
+            }
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+                        acc[mt][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[cur][mt][fn], xf[cur][fm],
+                                                                                 acc[mt][fm][fn], 0, 0, 0);
+            constexpr int NMF = FM * FN * NMAT;
+            constexpr int NV = (NMAT * FN * 16 + NMF - 1) / NMF;
+#pragma unroll
+            for (int j = 0; j < NMF; ++j) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                if (s < 3)
+                    __builtin_amdgcn_sched_group_barrier(SG_VALU, NV, 0);
+                if (s < 3 && j < FM)
+                    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+            }
+        }
+        // stage t+1 has landed once at most the newest stage's DMAs remain
+        wait_vmcnt<VMIN>();
+        __syncthreads();
+        read_w(lds + ((t + 1) % NSTAGE) * STAGE, cw);
+    }
+
+    // ---- epilogue: fp16 tile staged in LDS, then whole-row 16-byte stores ----
+    wait_vmcnt<0>();
+    __syncthreads();
+    constexpr int CPR = BN / 8;                           // 16-byte chunks per tile row
+    static_assert(CPR >= 16, "epilogue swizzle");
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        const int ml = wm * TM + fm * 32 + i;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int nl = wn * TN + fn * 32 + 8 * q + 4 * g;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (SWIGLU)
+                        v[e] = silu_mul(acc[0][fm][fn][4 * q + e], acc[1][fm][fn][4 * q + e]);
+                    else
+                        v[e] = acc[0][fm][fn][4 * q + e];
+                }
+                const f16x2 lo2 = {_Float16(v[0]), _Float16(v[1])};
+                const f16x2 hi2 = {_Float16(v[2]), _Float16(v[3])};
+                const int pc = (nl >> 3) ^ (ml & 15);
+                *reinterpret_cast<u32x2 *>(lds + ml * (BN * 2) + pc * 16 + (nl & 4) * 2) = u32x2{as_u32(lo2), as_u32(hi2)};
+            }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < BM * CPR; idx += NT) {
+        const int ml = idx / CPR, c = idx % CPR;
+        const int m = m0 + ml, n = n0 + c * 8;
+        if (m >= a.m || n >= a.n)
+            continue;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + ml * (BN * 2) + ((c ^ (ml & 15)) * 16));
+        _Float16 *dst = a.y + int64_t(m) * a.ldy + n;
+        if (n + 7 < a.n) {
+            *reinterpret_cast<u32x4 *>(dst) = v;
+        } else {
+            const f16x8 h = __builtin_bit_cast(f16x8, v);
+            for (int e = 0; e < 8 && n + e < a.n; ++e)
+                dst[e] = h[e];
+        }
+    }
+}
+
+template <int CODEC, int BM, int BN, int WM, int WN, bool SWIGLU>
+hipError_t launch_dma(const GemmProblem &p, hipStream_t stream)
+{
+    GemmArgs a;
+    a.w0 = p.w0;
+    a.w1 = p.w1;
+    a.x = p.x;
+    a.y = p.y;
+    a.x_bytes = uint32_t(((p.m - 1) * p.ldx + p.k) * 2);
+    a.m = int(p.m);
+    a.n = int(p.n);
+    a.k = int(p.k);
+    a.ldx = int(p.ldx);
+    a.ldy = int(p.ldy);
+    a.groups = int(p.groups);
+    a.ksteps = int(p.ksteps);
+    a.kb128 = int(p.kb128);
+    a.tiles_m = int(ceil_div(p.m, BM));
+    a.tiles_n = int(ceil_div(p.n, BN));
+    void *args[] = {&a};
+    const dim3 grid(unsigned(a.tiles_m * a.tiles_n)), block(64 * WM * WN);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_dma_kernel<CODEC, BM, BN, WM, WN, SWIGLU>), grid,
+                           block, args, 0, stream);
+}
+
 template <int CODEC, int BM, int BN, int WM, int WN, bool SWIGLU>
 hipError_t launch_tile(const GemmProblem &p, hipStream_t stream)
 {
@@ -299,6 +648,14 @@ template <int CODEC>
 hipError_t launch_codec(const GemmProblem &p, bool swiglu, hipStream_t stream)
 {
     constexpr int64_t FILL = 256;   // compute units on MI355X
+#ifndef QG_NO_DMA
+    if (swiglu && p.m > 128)
+        return launch_dma<CODEC, 256, 128, 2, 4, true>(p, stream);
+    if (!swiglu && p.m > 128 && tiles(p, 256, 256) >= FILL)
+        return launch_dma<CODEC, 256, 256, 2, 4, false>(p, stream);
+    if (!swiglu && p.m > 128)
+        return launch_dma<CODEC, 256, 128, 2, 4, false>(p, stream);
+#endif
     if (swiglu) {
         if (p.m > 128)
             return launch_tile<CODEC, 256, 128, 2, 4, true>(p, stream);
