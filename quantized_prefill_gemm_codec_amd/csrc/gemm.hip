@@ -25,6 +25,7 @@
 //  * All global loads are raw buffer loads: out-of-range rows, row groups and
 //    the K tail read as zero, so tails need no branches.
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace qg {
 namespace {
@@ -281,44 +282,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
 // registers).  The epilogue converts the accumulators to fp16 into LDS and
 // writes whole rows of Y with 16-byte stores.
 // ---------------------------------------------------------------------------
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// M0 carries the LDS destination of a DMA load; no other code in these kernels
-// uses M0, so clobbering it is safe.
-__device__ __forceinline__ void dma_b128(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
-                 "s"(lds)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void dma_b32(u32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
-                 "s"(lds)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// Raw buffer descriptor words (base, num_records, gfx9 raw-buffer flags) for
-// the inline-assembly loads; out-of-range vector offsets read zero.
-__device__ __forceinline__ u32x4 rsrc_words(const void *p, uint32_t bytes)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(p);
-    return u32x4{uint32_t(a), uint32_t(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
-}
-
-// s_waitcnt vmcnt(N) leaving the LDS and export counters alone (gfx9 encoding).
-template <int N> __device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ uint32_t lds_u32(const void *p)
-{
-    return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)(p)));
-}
-
 // Tile order: each XCD gets a contiguous run of tiles, and runs are laid out
 // in groups of GM m-tiles so that the tiles resident on one XCD at a time
 // share both X rows and weight row groups in its L2.

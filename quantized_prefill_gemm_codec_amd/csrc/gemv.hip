@@ -3,21 +3,21 @@
 // Pages: releases page v0.3.0 (the quantized linear layer switches to a GEMV
 // for M = 1 on every codec); project index Pillar 4 (decode is bound by bytes
 // streamed divided by bandwidth).  The GEMV reads every weight byte once, so it
-// is HBM-bound: the design goal is many 128-bit loads in flight and just
-// enough VALU per byte.
+// is HBM-bound: the design goal is the whole code stream in flight from the
+// first cycles and as little VALU per byte as the codec allows.
 //
-// GEMV kernel (1 <= M <= 4): one 256-thread workgroup per 32-row group of W.
-//  * X [M, K] is staged in LDS once per workgroup; every lane of a half-wave
-//    reads the same 16 bytes, so the fragment reads are LDS broadcasts.
-//  * The four waves split the k-steps; each lane streams its own 16-byte code
-//    slice per k-step (one 128-bit load, contiguous 1 KiB per wave) and its
-//    scale, several k-steps ahead of use.
-//  * The codes are turned into exact fp16 integers (q - offset) with the same
-//    unpack routines as the GEMM, dotted with X by v_dot2_f32_f16 into a per
-//    block fp32 sum, and the block scale is applied once per block in fp32:
-//      Q4_0 / Q2_0:  acc += d * sum_k x_k (q_k - c)
-//      MLX4-G64:     acc += s * sum_k x_k q_k + b * sum_k x_k
-//    (the per-group sums of X are computed once per workgroup in LDS).
+// GEMV kernel (1 <= M <= 4): one workgroup of GEMV_NW waves per 32-row group.
+//  * Wave w owns k-steps [w * per, (w + 1) * per) of the row group and keeps
+//    GEMV_PF of them in flight: per k-step one 128-bit (64-bit for Q2_0) code
+//    load and one scale load per lane, contiguous across the wave.  The first
+//    batch is issued before X [M, K] is staged in LDS, so the X latency hides
+//    behind it; every consumed slot is refilled with the k-step one batch on.
+//    (Eight waves with four slots each measured fastest on the 14336 x 4096
+//    Q4_0 decode shape: more loads in flight per wave did not help.)
+//  * The 1024 offset of the mantissa trick is not subtracted per weight:
+//    slice_dots dots the raw (1024 + 2^f q) halves with X and block_sum removes
+//    the offsets and the codec zero point once per 32-weight slice with a term
+//    that depends on X only (slice_correction, computed once per workgroup).
 //  * Lane halves, then waves, are reduced in a fixed order: results are
 //    bit-identical from run to run.
 #include "launch.h"
@@ -25,8 +25,10 @@
 namespace qg {
 namespace {
 
-constexpr int GEMV_NT = 256;
-constexpr int GEMV_PF = 8;   // k-steps of codes in flight per lane
+constexpr int GEMV_NW = 8;               // waves per workgroup (split of the k-steps)
+constexpr int GEMV_NT = 64 * GEMV_NW;
+constexpr int GEMV_PF = 4;               // k-steps of codes in flight per lane
+constexpr int GEMV_X_LDS_MAX = 64 * 1024; // largest staged X (M x K fp16) the GEMV takes
 
 struct GemvArgs {
     Planes w;
@@ -35,65 +37,147 @@ struct GemvArgs {
     uint32_t x_bytes;
     int m, n, k, ldx, ldy;
     int groups, ksteps, kb128;
+    int per;                 // k-steps per wave
+    int x_lds;               // bytes of the X region
 };
 
-template <int CODEC> __device__ __forceinline__ float scale_of(const LaneCodes<CODEC> &lc)
+template <int CODEC> constexpr int corr_floats() { return CODEC == MLX4_G64 ? 2 : 1; }
+
+// x_s[p] = x_{2p} + x_{2p+1} summed over the 4 sub-step chunks of the slice.
+template <int CODEC>
+__device__ __forceinline__ void slice_correction(const u32x4 *chunks, float *out)
 {
-    if constexpr (CODEC == MLX4_G64)
-        return float(as_f16x2(lc.sb)[0]);
-    else
-        return float(lc.d);
+    float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const f16x8 v = __builtin_bit_cast(f16x8, chunks[c]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            sp[p] += float(v[2 * p]) + float(v[2 * p + 1]);
+    }
+    if constexpr (CODEC == Q4_0) {
+        out[0] = -1032.0f * (sp[0] + sp[2]) - 72.0f * (sp[1] + sp[3]);
+    } else if constexpr (CODEC == MLX4_G64) {
+        out[0] = -1024.0f * (sp[0] + sp[2]) - 64.0f * (sp[1] + sp[3]);
+        out[1] = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+    } else {
+        out[0] = -1024.0f * (sp[0] + 0.25f * sp[1] + 0.0625f * sp[2] + 0.015625f * sp[3]) -
+                 ((sp[0] + sp[1]) + (sp[2] + sp[3]));
+    }
+}
+
+template <int CODEC> struct CodeWords { using type = u32x4; };
+template <> struct CodeWords<Q2_0> { using type = u32x2; };
+
+// Dot products of a lane's 32 codes with the matching X values, taken on the
+// codes as they sit in the packed word: OR-ing a code field into the mantissa
+// of binary16 1024 gives 1024 + 2^f q for a field at bit f of the half-word
+// (f < 10), so no shift per field is needed -- only one 8-bit shift per word
+// for the fields above bit 7.  v_dot2_f32_f16 multiplies exactly and sums in
+// fp32; per class of fields with the same factor 2^f one fp32 partial sum:
+//   Q4_0 / MLX4:  d[0] (fields at bits 0, 8 -> factor 1), d[1] (bits 4, 12 -> 16)
+//   Q2_0:         d[p] (fields at bits 2p, 8 + 2p -> factor 4^p), p = 0..3
+// block_sum then removes the 1024 offsets (and the codec zero point) with the
+// precomputed X term: sum_k (q_k - z) x_k = sum_c d[c] / 2^f_c + corr.
+template <int CODEC, int MM>
+__device__ __forceinline__ void slice_dots(const typename CodeWords<CODEC>::type &c, const u32x4 *const (&xrow)[MM],
+                                           uint32_t magic, float (&d)[4][MM])
+{
+    if constexpr (CODEC == Q2_0) {
+#pragma unroll
+        for (int wi = 0; wi < 2; ++wi) {
+            const uint32_t wv = c[wi];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const uint32_t src = half ? (wv >> 8) : wv;
+                const int s = 2 * wi + half;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const uint32_t h = (src & (0x00030003u << (2 * p))) | magic;
+#pragma unroll
+                    for (int mr = 0; mr < MM; ++mr)
+                        d[p][mr] = __builtin_amdgcn_fdot2(as_f16x2(h), as_f16x2(xrow[mr][s][p]), d[p][mr], false);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t wv = c[s], w8 = wv >> 8;
+            const uint32_t h0 = (wv & 0x000F000Fu) | magic, h1 = (wv & 0x00F000F0u) | magic;
+            const uint32_t h2 = (w8 & 0x000F000Fu) | magic, h3 = (w8 & 0x00F000F0u) | magic;
+#pragma unroll
+            for (int mr = 0; mr < MM; ++mr) {
+                const u32x4 xv = xrow[mr][s];
+                d[0][mr] = __builtin_amdgcn_fdot2(as_f16x2(h0), as_f16x2(xv[0]), d[0][mr], false);
+                d[0][mr] = __builtin_amdgcn_fdot2(as_f16x2(h2), as_f16x2(xv[2]), d[0][mr], false);
+                d[1][mr] = __builtin_amdgcn_fdot2(as_f16x2(h1), as_f16x2(xv[1]), d[1][mr], false);
+                d[1][mr] = __builtin_amdgcn_fdot2(as_f16x2(h3), as_f16x2(xv[3]), d[1][mr], false);
+            }
+        }
+    }
+}
+
+// acc + scale * sum_k (q_k - z) x_k (+ bias * sum_k x_k for MLX4); `sc` is the
+// lane's scale record (fp16 d, or fp16 s | fp16 b << 16 for MLX4).
+template <int CODEC>
+__device__ __forceinline__ float block_sum(uint32_t sc, const float (&d)[4], const float *corr, float acc)
+{
+    const f16x2 sb = as_f16x2(sc);
+    if constexpr (CODEC == Q2_0) {
+        const float v = __builtin_fmaf(d[3], 0.015625f, __builtin_fmaf(d[2], 0.0625f, __builtin_fmaf(d[1], 0.25f, d[0])));
+        return __builtin_fmaf(float(sb[0]), v + corr[0], acc);
+    } else if constexpr (CODEC == Q4_0) {
+        return __builtin_fmaf(float(sb[0]), __builtin_fmaf(d[1], 0.0625f, d[0]) + corr[0], acc);
+    } else {
+        const float v = __builtin_fmaf(d[1], 0.0625f, d[0]) + corr[0];
+        return __builtin_fmaf(float(sb[0]), v, __builtin_fmaf(float(sb[1]), corr[1], acc));
+    }
 }
 
 template <int CODEC, int MM>
 __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
 {
+    constexpr int NC = corr_floats<CODEC>();
+
     extern __shared__ u32x4 smem[];
+    char *lds = reinterpret_cast<char *>(smem);
     const int kchunks = a.ksteps * 8;                 // 16-byte chunks per X row
-    u32x4 *xs = smem;                                 // [MM][kchunks]
-    float *xsum = reinterpret_cast<float *>(smem + MM * kchunks);   // [MM][2*ksteps]
-    float *red = xsum + (CODEC == MLX4_G64 ? MM * 2 * a.ksteps : 0);  // [4][MM][32]
+    const u32x4 *xs = smem;                           // [MM][kchunks]
+    float *corr = reinterpret_cast<float *>(lds + a.x_lds);   // [MM][ksteps][2][NC]
+    float *red = corr + MM * a.ksteps * 2 * NC;       // [GEMV_NW][MM][32]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i = lane & 31, g = lane >> 5;
     const int rg = blockIdx.x;
     const uint32_t magic = magic1024();
+
+    const int t0 = min(wave * a.per, a.ksteps);
+    const int t1 = min(a.ksteps, t0 + a.per);
+
+    // the first GEMV_PF k-steps of codes and scales
     const PlaneRsrc w = plane_rsrc(a.w);
-
-    const int per = (a.ksteps + 3) >> 2;
-    const int t0 = wave * per;
-    const int t1 = min(a.ksteps, t0 + per);
-
-    // first batch of codes before the X staging, to overlap the latencies
     const LaneOffsets lo = lane_offsets<CODEC>(rg, a.groups, lane);
     LaneCodes<CODEC> lc[GEMV_PF];
 #pragma unroll
     for (int u = 0; u < GEMV_PF; ++u)
-        lc[u] = load_lane<CODEC>(w, lo, rg, min(t0 + u, a.ksteps - 1), a.ksteps, a.kb128);
+        if (t0 + u < t1)
+            lc[u] = load_lane<CODEC>(w, lo, rg, t0 + u, a.ksteps, a.kb128);
 
+    // X rows into LDS
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
     for (int q = tid; q < MM * kchunks; q += GEMV_NT) {
         const int mr = q / kchunks, ch = q - mr * kchunks;
         const uint32_t off = (mr < a.m && ch * 8 < a.k) ? (uint32_t(mr) * uint32_t(a.ldx) + uint32_t(ch) * 8u) * 2u : OOB;
-        xs[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+        smem[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
     }
     __syncthreads();
-    if constexpr (CODEC == MLX4_G64) {
-        for (int q = tid; q < MM * 2 * a.ksteps; q += GEMV_NT) {
-            const int mr = q / (2 * a.ksteps), h = q - mr * 2 * a.ksteps;
-            float sum = 0.0f;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const f16x8 v = __builtin_bit_cast(f16x8, xs[mr * kchunks + h * 4 + c]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    sum += float(v[e]);
-            }
-            xsum[q] = sum;
-        }
-        __syncthreads();
+    for (int q = tid; q < MM * a.ksteps * 2; q += GEMV_NT) {
+        const int mr = q / (2 * a.ksteps), h = q - mr * 2 * a.ksteps;   // h = 2 t + g
+        slice_correction<CODEC>(xs + mr * kchunks + h * 4, corr + q * NC);
     }
+    __syncthreads();
 
     float acc[MM];
 #pragma unroll
@@ -105,31 +189,26 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
         for (int u = 0; u < GEMV_PF; ++u) {
             const int t = tb + u;
             if (t < t1) {
-                float blk[MM];
+                const u32x4 *xrow[MM];
 #pragma unroll
                 for (int mr = 0; mr < MM; ++mr)
-                    blk[mr] = 0.0f;
+                    xrow[mr] = xs + mr * kchunks + t * 8 + 4 * g;
+                float dots[4][MM];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    u32x4 xv[MM];
+                for (int c = 0; c < 4; ++c)
 #pragma unroll
                     for (int mr = 0; mr < MM; ++mr)
-                        xv[mr] = xs[mr * kchunks + t * 8 + 4 * g + s];
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const f16x2 f = factor_pair<CODEC>(lc[u], s, p, magic);
-#pragma unroll
-                        for (int mr = 0; mr < MM; ++mr)
-                            blk[mr] = __builtin_amdgcn_fdot2(f, as_f16x2(xv[mr][p]), blk[mr], false);
-                    }
-                }
-                const float sc = scale_of<CODEC>(lc[u]);
+                        dots[c][mr] = 0.0f;
+                slice_dots<CODEC, MM>(lc[u].c, xrow, magic, dots);
+                uint32_t sc;
+                if constexpr (CODEC == MLX4_G64)
+                    sc = lc[u].sb;
+                else
+                    sc = __builtin_bit_cast(unsigned short, lc[u].d);
 #pragma unroll
                 for (int mr = 0; mr < MM; ++mr) {
-                    if constexpr (CODEC == MLX4_G64)
-                        acc[mr] += sc * blk[mr] + float(as_f16x2(lc[u].sb)[1]) * xsum[mr * 2 * a.ksteps + 2 * t + g];
-                    else
-                        acc[mr] += sc * blk[mr];
+                    const float d4[4] = {dots[0][mr], dots[1][mr], dots[2][mr], dots[3][mr]};
+                    acc[mr] = block_sum<CODEC>(sc, d4, corr + ((mr * a.ksteps + t) * 2 + g) * NC, acc[mr]);
                 }
             }
             // refill this slot with the k-step one batch ahead
@@ -152,8 +231,10 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
 #pragma unroll
             for (int mr = 0; mr < MM; ++mr) {
                 if (mr < a.m) {
-                    const float v = ((red[(0 * MM + mr) * 32 + i] + red[(1 * MM + mr) * 32 + i]) +
-                                     red[(2 * MM + mr) * 32 + i]) + red[(3 * MM + mr) * 32 + i];
+                    float v = red[mr * 32 + i];
+#pragma unroll
+                    for (int w = 1; w < GEMV_NW; ++w)
+                        v += red[(w * MM + mr) * 32 + i];
                     a.y[int64_t(mr) * a.ldy + n] = _Float16(v);
                 }
             }
@@ -184,6 +265,23 @@ __global__ __launch_bounds__(256) void dequant_kernel(Planes wp, int n, int k, i
     }
 }
 
+// LDS layout of one GEMV workgroup: X, the X corrections, the wave partial sums.
+struct GemvLds {
+    int per, x_lds;
+    size_t bytes;
+};
+
+inline GemvLds gemv_lds(int codec, int64_t mm, int64_t ksteps)
+{
+    GemvLds l;
+    l.per = int((ksteps + GEMV_NW - 1) / GEMV_NW);
+    const int64_t x = mm * ksteps * 128;
+    l.x_lds = int(x);
+    const int64_t nc = codec == MLX4_G64 ? 2 : 1;
+    l.bytes = size_t(l.x_lds + mm * ksteps * 2 * nc * 4 + GEMV_NW * mm * 32 * 4);
+    return l;
+}
+
 template <int CODEC, int MM>
 hipError_t launch_gemv_mm(const GemmProblem &p, hipStream_t stream)
 {
@@ -200,11 +298,12 @@ hipError_t launch_gemv_mm(const GemmProblem &p, hipStream_t stream)
     a.groups = int(p.groups);
     a.ksteps = int(p.ksteps);
     a.kb128 = int(p.kb128);
-    const size_t lds = size_t(MM) * size_t(a.ksteps) * 128 +
-                       (CODEC == MLX4_G64 ? size_t(MM) * 2 * size_t(a.ksteps) * 4 : 0) + 4 * MM * 32 * 4;
+    const GemvLds l = gemv_lds(CODEC, MM, p.ksteps);
+    a.per = l.per;
+    a.x_lds = l.x_lds;
     void *args[] = {&a};
     return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_kernel<CODEC, MM>), dim3(unsigned(a.groups)),
-                           dim3(GEMV_NT), args, lds, stream);
+                           dim3(GEMV_NT), args, l.bytes, stream);
 }
 
 template <int CODEC>
@@ -219,16 +318,11 @@ hipError_t launch_gemv_codec(const GemmProblem &p, hipStream_t stream)
 
 }  // namespace
 
-// LDS the VALU GEMV needs; beyond this the tiled MFMA kernel serves small M.
-static size_t gemv_lds_bytes(const GemmProblem &p)
-{
-    const int64_t mm = p.m == 1 ? 1 : p.m == 2 ? 2 : 4;
-    return size_t(mm * p.ksteps * 128 + (p.codec == MLX4_G64 ? mm * 2 * p.ksteps * 4 : 0) + 4 * mm * 32 * 4);
-}
-
 hipError_t launch_gemv(const GemmProblem &p, hipStream_t stream)
 {
-    if (p.m > 4 || gemv_lds_bytes(p) > 64 * 1024)
+    // beyond 4 rows, or an X too large to stage, the tiled MFMA kernel serves small M
+    const int64_t mm = p.m == 1 ? 1 : p.m == 2 ? 2 : 4;
+    if (p.m > 4 || mm * p.ksteps * 128 > GEMV_X_LDS_MAX || gemv_lds(p.codec, mm, p.ksteps).bytes > 64 * 1024)
         return launch_gemm(p, false, stream);
     switch (p.codec) {
     case Q4_0: return launch_gemv_codec<Q4_0>(p, stream);
