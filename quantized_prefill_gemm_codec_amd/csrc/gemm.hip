@@ -7,23 +7,26 @@
 // chip, only the activation written); project index Pillar 1 (128-bit loads,
 // block-swizzled weight layout, conflict-free shared tiles).
 //
-// Work decomposition (one workgroup of WM x WN wave64 per BM x BN output tile):
+// Common to both kernels (one workgroup of WM x WN wave64 per BM x BN tile):
 //  * Wave (wm, wn) owns a TM x TN sub-tile = FM x FN blocks of 32 x 32.
-//  * Per 64-deep k-step the workgroup stages the X tile [BM x 64] fp16 in LDS
-//    (double-buffered; 16-byte chunks XOR-swizzled by row so that the 128-bit
-//    fragment reads of 16 consecutive rows hit distinct banks).
-//  * Each wave streams the planar codes of its own FN row groups straight
-//    from memory into registers (one 128-bit load per lane per row group),
-//    unpacks them to fp16 in registers in MFMA operand order and issues the
-//    MFMAs: A = weights (rows n), B = activations (rows m), so each lane ends
-//    with 4 consecutive n of one m -> 8-byte fp16 stores of Y.
-//  * The next k-step's X tile and codes are fetched into registers before the
-//    current step's MFMAs (the pages' q_next ping-pong) and written to the
-//    other LDS buffer afterwards: one barrier per k-step.
-//  * With 8 waves (2 per SIMD) one wave's unpack and LDS traffic overlaps the
-//    other wave's matrix-core work.
+//  * Per 64-deep k-step the X tile [BM x 64] fp16 sits in LDS, its 16-byte
+//    chunks XOR-swizzled by row so that the 128-bit fragment reads of 16
+//    consecutive rows hit distinct banks.
+//  * Each wave unpacks the planar codes of its own FN row groups to fp16 in
+//    registers, in MFMA operand order, and issues the MFMAs: A = weights (rows
+//    n), B = activations (rows m), so each lane ends with 4 consecutive n of
+//    one m.
 //  * All global loads are raw buffer loads: out-of-range rows, row groups and
 //    the K tail read as zero, so tails need no branches.
+//
+// gemm_kernel (64 < M <= 128, and SwiGLU up to M = 128): codes stream from
+// memory straight into registers and the next k-step's X tile is fetched into
+// registers before the current step's MFMAs (the pages' q_next ping-pong),
+// then written to the other LDS buffer: one barrier per k-step.
+//
+// gemm_dma_kernel (M > 128, and M <= 64 with a split k-loop): X tiles, code
+// chunks and scale records all reach LDS by hardware DMA a few k-steps ahead
+// of use; see the comment above the kernel.
 #include "launch.h"
 #include "lds_dma.h"
 
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
     constexpr int NMAT = SWIGLU ? 2 : 1;
     constexpr int XCH = BM * 8 / NT;        // 16-byte X chunks per thread per k-step
     constexpr int STAGE = BM * 128;         // bytes of one X stage in LDS
-    static_assert(FM >= 1 && FN >= 1 && XCH >= 1 && (BM * 8) % NT == 0 && TM % 64 == 0 || FM == 1, "tile");
+    static_assert(FM >= 1 && FN >= 1 && XCH >= 1 && (BM * 8) % NT == 0 && (TM % 64 == 0 || FM == 1), "tile");
 
     __shared__ u32x4 lds_x[2 * BM * 8];
     char *lds = reinterpret_cast<char *>(lds_x);
@@ -301,10 +304,16 @@ __device__ __forceinline__ void grouped_tile(int bid, int tiles_m, int tiles_n, 
     tn = idx / gsm;
 }
 
-template <int CODEC, int BM, int BN, int WM, int WN, bool SWIGLU>
-__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_kernel(GemmArgs a)
+// WK > 1 splits the k-steps of a tile into WK contiguous slices, one per
+// group of WM x WN waves; each group has its own X / code / scale slice in
+// every stage, and the WK fp32 partial tiles are summed in LDS (fixed order)
+// in the epilogue.  Used for small M, where the tiles alone would leave most
+// SIMDs idle.  NSTAGE stages are in flight (loads run NSTAGE-1 steps ahead).
+template <int CODEC, int BM, int BN, int WM, int WN, int WK, bool SWIGLU, int NSTAGE>
+__global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs a)
 {
-    constexpr int NW = WM * WN, NT = 64 * NW;
+    constexpr int NWT = WM * WN;                           // waves per k-slice
+    constexpr int NW = NWT * WK, NT = 64 * NW;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
     constexpr int NMAT = SWIGLU ? 2 : 1;
@@ -315,15 +324,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_kernel(GemmArgs a)
     constexpr int X_OFF = 0, X_BYTES = BM * 128;
     constexpr int W_OFF = X_BYTES, W_BYTES = NMAT * RG * WCH;
     constexpr int S_OFF = W_OFF + W_BYTES, S_BYTES = NMAT * RG * SB;
-    constexpr int STAGE = S_OFF + S_BYTES;
-    constexpr int NSTAGE = 3;
-    constexpr int EPI_BYTES = BM * BN * 2;
+    constexpr int SLICE = (S_OFF + S_BYTES + 255) / 256 * 256;   // one k-slice of one stage
+    constexpr int STAGE = WK * SLICE;
+    constexpr int AHEAD = NSTAGE - 1;
+    constexpr int PPITCH = BN * 4 + 16;                    // fp32 partial tile row pitch (WK > 1)
+    constexpr int EPI_BYTES = WK == 1 ? BM * BN * 2 : WK * BM * PPITCH;
     constexpr int LDS_BYTES = NSTAGE * STAGE > EPI_BYTES ? NSTAGE * STAGE : EPI_BYTES;
-    constexpr int NX = X_BYTES / 1024, NWI = W_BYTES / 1024, NSI = S_BYTES / 256;   // DMA instructions per stage
-    constexpr int XPW = NX / NW, WPW = (NWI + NW - 1) / NW, SPW = (NSI + NW - 1) / NW;
-    constexpr int VMIN = XPW + NWI / NW + NSI / NW;         // fewest DMA ops any wave issues per stage
-    static_assert(NX % NW == 0 && W_BYTES % 1024 == 0 && S_BYTES % 256 == 0 && STAGE % 16 == 0, "dma tiling");
-    static_assert(FM % 2 == 0 && VMIN >= 1, "tile");
+    constexpr int NX = X_BYTES / 1024, NWI = W_BYTES / 1024, NSI = (S_BYTES + 255) / 256;   // DMA ops per slice
+    constexpr int XPW = NX / NWT, WPW = (NWI + NWT - 1) / NWT, SPW = (NSI + NWT - 1) / NWT;
+    constexpr int VMIN = XPW + NWI / NWT + NSI / NWT;       // fewest DMA ops any wave issues per stage
+    constexpr int VWAIT = (AHEAD - 1) * VMIN;               // DMA ops that may stay in flight
+    static_assert(NX % NWT == 0 && W_BYTES % 1024 == 0 && SLICE % 256 == 0, "dma tiling");
+    static_assert((FM == 1 || FM % 2 == 0) && VMIN >= 1 && NSTAGE >= 3 && VWAIT < 64, "tile");
+    static_assert(!(SWIGLU && WK > 1), "the split-K epilogue sums plain GEMM partials");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
     __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
@@ -332,7 +345,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_kernel(GemmArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave % WM, wn = wave / WM;
+    const int wk = wave / NWT, wr = wave % NWT;            // k-slice, wave inside the slice group
+    const int wm = wr % WM, wn = wr / WM;
     const int i = lane & 31, g = lane >> 5;
     const uint32_t magic = magic1024();
 
@@ -342,6 +356,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_kernel(GemmArgs a)
     const int last = a.ksteps - 1;
     const int ktail = a.k & 63;
     const int rg0 = n0 >> 5;
+    const int kq = (a.ksteps + WK - 1) / WK;                // iterations (k-steps per slice)
+    const int kbase = wk * kq;                             // first k-step of this wave's slice
 
     const u32x4 xr = rsrc_words(a.x, a.x_bytes);
     const u32x4 q0 = rsrc_words(a.w0.qs, a.w0.qs_bytes), s0 = rsrc_words(a.w0.scales, a.w0.scale_bytes);
@@ -354,7 +370,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_kernel(GemmArgs a)
     uint32_t xv[XPW], xvt[XPW];
 #pragma unroll
     for (int u = 0; u < XPW; ++u) {
-        const int p = (wave + NW * u) * 64 + lane;
+        const int p = (wr + NWT * u) * 64 + lane;
         const int r = p >> 3, ch = (p & 7) ^ swz(r);
         xv[u] = (m0 + r < a.m) ? (uint32_t(m0 + r) * uint32_t(a.ldx) + uint32_t(ch * 8)) * 2u : OOB;
         xvt[u] = (ch * 8 < ktail) ? xv[u] : OOB;
@@ -365,7 +381,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_kernel(GemmArgs a)
     int wmat[WPW];
 #pragma unroll
     for (int u = 0; u < WPW; ++u) {
-        const int j = wave + NW * u;
+        const int j = wr + NWT * u;
         const int c = (CB == 16) ? j : 2 * j + (lane >> 5);
         const int mt = c / RG, rg = c % RG;
         const uint32_t lo = (CB == 16) ? uint32_t(lane) * 16 : uint32_t(lane & 31) * 16;
@@ -379,34 +395,39 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_kernel(GemmArgs a)
     int smat[SPW];
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
-        const int j = wave + NW * u;
+        const int j = wr + NWT * u;
         const int b = 256 * j + 4 * lane;
         const int c = b / SB, o = b % SB;
         const int rg = c % RG;
         smat[u] = (256 * j / SB) / RG;              // wave-uniform: chunks never straddle matrices
         const uint32_t pitch = CODEC == Q2_0 ? uint32_t(a.kb128) * 64u : uint32_t(a.ksteps) * 128u;
-        sv[u] = (j < NSI && rg0 + rg < a.groups) ? uint32_t(rg0 + rg) * pitch + uint32_t(o) : OOB;
+        sv[u] = (j < NSI && b < S_BYTES && rg0 + rg < a.groups) ? uint32_t(rg0 + rg) * pitch + uint32_t(o) : OOB;
     }
 
-    auto issue_stage = [&](int t, int stage) {
-        const uint32_t base = lds0 + uint32_t(stage * STAGE);
+    // iteration i of this wave's slice = k-step kbase + i; past the end of K
+    // (last slice of a ragged split) every vector offset is out of range, so
+    // the stage fills with zeros and the MFMAs add nothing.
+    auto issue_stage = [&](int i, int stage) {
+        const uint32_t base = lds0 + uint32_t(stage * STAGE + wk * SLICE);
+        const int t = min(kbase + i, last);
+        const bool in = kbase + i <= last;
         const bool tail = (t == last) && ktail != 0;
 #pragma unroll
         for (int u = 0; u < XPW; ++u)
-            dma_b128(xr, tail ? xvt[u] : xv[u], uint32_t(t) * 128u,
-                     base + X_OFF + uint32_t((wave + NW * u) * 1024));
+            dma_b128(xr, in ? (tail ? xvt[u] : xv[u]) : OOB, uint32_t(t) * 128u,
+                     base + X_OFF + uint32_t((wr + NWT * u) * 1024));
 #pragma unroll
         for (int u = 0; u < WPW; ++u) {
-            const int j = wave + NW * u;
+            const int j = wr + NWT * u;
             if (j < NWI)
-                dma_b128(wmat[u] ? q1 : q0, wv[u], uint32_t(t) * WCH, base + W_OFF + uint32_t(j * 1024));
+                dma_b128(wmat[u] ? q1 : q0, in ? wv[u] : OOB, uint32_t(t) * WCH, base + W_OFF + uint32_t(j * 1024));
         }
 #pragma unroll
         for (int u = 0; u < SPW; ++u) {
-            const int j = wave + NW * u;
+            const int j = wr + NWT * u;
             const uint32_t so = CODEC == Q2_0 ? uint32_t(t >> 1) * 64u : uint32_t(t) * 128u;
             if (j < NSI)
-                dma_b32(smat[u] ? s1 : s0, sv[u], so, base + S_OFF + uint32_t(j * 256));
+                dma_b32(smat[u] ? s1 : s0, in ? sv[u] : OOB, so, base + S_OFF + uint32_t(j * 256));
         }
     };
 
@@ -463,17 +484,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_kernel(GemmArgs a)
                 for (int e = 0; e < 16; ++e)
                     acc[mt][fm][fn][e] = 0.0f;
 
-    issue_stage(0, 0);
-    issue_stage(min(1, last), 1);
-    wait_vmcnt<VMIN>();
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i)
+        issue_stage(min(i, kq - 1), i);
+    wait_vmcnt<VWAIT>();
     __syncthreads();
     LaneCodes<CODEC> cw[NMAT][FN];
-    read_w(lds, cw);
+    const int slice = wk * SLICE;
+    read_w(lds + slice, cw);
 
-    for (int t = 0; t < a.ksteps; ++t) {
+    for (int t = 0; t < kq; ++t) {
         const int st = t % NSTAGE;
-        issue_stage(min(t + 2, last), (t + 2) % NSTAGE);
-        const char *sp = lds + st * STAGE;
+        issue_stage(min(t + AHEAD, kq - 1), (t + AHEAD) % NSTAGE);
+        const char *sp = lds + st * STAGE + slice;
         f16x8 xf[2][FM];
         f16x8 wf[2][NMAT][FN];
         read_x(sp, 0, xf[0]);
@@ -504,17 +527,57 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_kernel(GemmArgs a)
                     __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
             }
         }
-        // stage t+1 has landed once at most the newest stage's DMAs remain
-        wait_vmcnt<VMIN>();
+        // stage t+1 has landed once at most the newest AHEAD-1 stages' DMAs remain
+        wait_vmcnt<VWAIT>();
         __syncthreads();
-        read_w(lds + ((t + 1) % NSTAGE) * STAGE, cw);
+        read_w(lds + ((t + 1) % NSTAGE) * STAGE + slice, cw);
     }
 
     // ---- epilogue: fp16 tile staged in LDS, then whole-row 16-byte stores ----
     wait_vmcnt<0>();
     __syncthreads();
     constexpr int CPR = BN / 8;                           // 16-byte chunks per tile row
-    static_assert(CPR >= 16, "epilogue swizzle");
+    if constexpr (WK > 1) {
+        // fp32 partial tile of each k-slice, then the fixed-order sum
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int ml = wm * TM + fm * 32 + i;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int nl = wn * TN + fn * 32 + 8 * q + 4 * g;
+                    f32x4 v = {acc[0][fm][fn][4 * q], acc[0][fm][fn][4 * q + 1], acc[0][fm][fn][4 * q + 2],
+                               acc[0][fm][fn][4 * q + 3]};
+                    *reinterpret_cast<f32x4 *>(lds + (wk * BM + ml) * PPITCH + nl * 4) = v;
+                }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < BM * CPR; idx += NT) {
+            const int ml = idx / CPR, c = idx % CPR;
+            const int m = m0 + ml, n = n0 + c * 8;
+            if (m >= a.m || n >= a.n)
+                continue;
+            f32x4 lo = *reinterpret_cast<const f32x4 *>(lds + ml * PPITCH + c * 32);
+            f32x4 hi = *reinterpret_cast<const f32x4 *>(lds + ml * PPITCH + c * 32 + 16);
+#pragma unroll
+            for (int k = 1; k < WK; ++k) {
+                lo += *reinterpret_cast<const f32x4 *>(lds + (k * BM + ml) * PPITCH + c * 32);
+                hi += *reinterpret_cast<const f32x4 *>(lds + (k * BM + ml) * PPITCH + c * 32 + 16);
+            }
+            const f16x8 h = {_Float16(lo[0]), _Float16(lo[1]), _Float16(lo[2]), _Float16(lo[3]),
+                             _Float16(hi[0]), _Float16(hi[1]), _Float16(hi[2]), _Float16(hi[3])};
+            _Float16 *dst = a.y + int64_t(m) * a.ldy + n;
+            if (n + 7 < a.n) {
+                *reinterpret_cast<f16x8 *>(dst) = h;
+            } else {
+                for (int e = 0; e < 8 && n + e < a.n; ++e)
+                    dst[e] = h[e];
+            }
+        }
+        return;
+    }
+    static_assert(WK > 1 || CPR >= 16, "epilogue swizzle");
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
         const int ml = wm * TM + fm * 32 + i;
@@ -555,7 +618,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_dma_kernel(GemmArgs a)
     }
 }
 
-template <int CODEC, int BM, int BN, int WM, int WN, bool SWIGLU>
+template <int CODEC, int BM, int BN, int WM, int WN, int WK, bool SWIGLU, int NSTAGE>
 hipError_t launch_dma(const GemmProblem &p, hipStream_t stream)
 {
     GemmArgs a;
@@ -575,9 +638,10 @@ hipError_t launch_dma(const GemmProblem &p, hipStream_t stream)
     a.tiles_m = int(ceil_div(p.m, BM));
     a.tiles_n = int(ceil_div(p.n, BN));
     void *args[] = {&a};
-    const dim3 grid(unsigned(a.tiles_m * a.tiles_n)), block(64 * WM * WN);
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_dma_kernel<CODEC, BM, BN, WM, WN, SWIGLU>), grid,
-                           block, args, 0, stream);
+    const dim3 grid(unsigned(a.tiles_m * a.tiles_n)), block(64 * WM * WN * WK);
+    return hipLaunchKernel(
+        reinterpret_cast<const void *>(&gemm_dma_kernel<CODEC, BM, BN, WM, WN, WK, SWIGLU, NSTAGE>), grid, block,
+        args, 0, stream);
 }
 
 template <int CODEC, int BM, int BN, int WM, int WN, bool SWIGLU>
@@ -611,28 +675,21 @@ template <int CODEC>
 hipError_t launch_codec(const GemmProblem &p, bool swiglu, hipStream_t stream)
 {
     constexpr int64_t FILL = 256;   // compute units on MI355X
-#ifndef QG_NO_DMA
-    if (swiglu && p.m > 128)
-        return launch_dma<CODEC, 256, 128, 2, 4, true>(p, stream);
-    if (!swiglu && p.m > 128 && tiles(p, 256, 256) >= FILL)
-        return launch_dma<CODEC, 256, 256, 2, 4, false>(p, stream);
-    if (!swiglu && p.m > 128)
-        return launch_dma<CODEC, 256, 128, 2, 4, false>(p, stream);
-#endif
-    if (swiglu) {
-        if (p.m > 128)
-            return launch_tile<CODEC, 256, 128, 2, 4, true>(p, stream);
-        if (p.m > 64)
-            return launch_tile<CODEC, 128, 128, 2, 2, true>(p, stream);
-        return launch_tile<CODEC, 64, 64, 2, 2, true>(p, stream);
+    if (p.m > 128) {
+        if (swiglu)
+            return launch_dma<CODEC, 256, 128, 2, 4, 1, true, 3>(p, stream);
+        if (tiles(p, 256, 256) >= FILL)
+            return launch_dma<CODEC, 256, 256, 2, 4, 1, false, 3>(p, stream);
+        return launch_dma<CODEC, 256, 128, 2, 4, 1, false, 3>(p, stream);
     }
-    if (p.m > 128 && tiles(p, 256, 256) >= FILL)
-        return launch_tile<CODEC, 256, 256, 2, 4, false>(p, stream);
-    if (p.m > 128)
-        return launch_tile<CODEC, 256, 128, 2, 4, false>(p, stream);
-    if (p.m > 64)
-        return launch_tile<CODEC, 128, 128, 2, 2, false>(p, stream);
-    return launch_tile<CODEC, 64, 64, 2, 2, false>(p, stream);
+    // small M: 64 x 64 tiles with the k-steps split four ways inside the
+    // workgroup (eight waves), so that N / 64 tiles keep the SIMDs busy
+    if (!swiglu && p.m <= 64)
+        return launch_dma<CODEC, 64, 64, 1, 2, 4, false, 3>(p, stream);
+    if (swiglu)
+        return p.m > 64 ? launch_tile<CODEC, 128, 128, 2, 2, true>(p, stream)
+                        : launch_tile<CODEC, 64, 64, 2, 2, true>(p, stream);
+    return launch_tile<CODEC, 128, 128, 2, 2, false>(p, stream);
 }
 
 }  // namespace

@@ -108,6 +108,8 @@ GEMM_SHAPES = [
     (1, 129, 136, 160), (1, 300, 264, 352), (1, 257, 1024, 256),
     (2, 6, 256, 192), (2, 65, 200, 64), (2, 129, 272, 320), (2, 300, 512, 256),
     (3, 7, 96, 128), (3, 100, 264, 384), (3, 129, 256, 256), (3, 320, 520, 512),
+    # small M with several k-steps per slice of the split k-loop, ragged last slice
+    (1, 48, 320, 2080), (2, 40, 72, 1152), (3, 64, 96, 1408),
 ]
 
 
