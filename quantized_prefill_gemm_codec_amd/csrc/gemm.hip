@@ -492,21 +492,34 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     LaneCodes<CODEC> cw[NMAT][FN];
     const int slice = wk * SLICE;
     read_w(lds + slice, cw);
-
+    // Operands of sub-step 0 are prepared during sub-step 3 of the previous
+    // k-step, so the k-step boundary (wait + barrier + first LDS reads and
+    // unpack) overlaps matrix-core work instead of draining it.
+    f16x8 xf[2][FM];
+    f16x8 wf[2][NMAT][FN];
+    read_x(lds + slice, 0, xf[0]);
+    unpack(cw, 0, wf[0]);
     for (int t = 0; t < kq; ++t) {
         const int st = t % NSTAGE;
         issue_stage(min(t + AHEAD, kq - 1), (t + AHEAD) % NSTAGE);
         const char *sp = lds + st * STAGE + slice;
-        f16x8 xf[2][FM];
-        f16x8 wf[2][NMAT][FN];
-        read_x(sp, 0, xf[0]);
-        unpack(cw, 0, wf[0]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int cur = s & 1;
             if (s < 3) {
                 read_x(sp, s + 1, xf[cur ^ 1]);
                 unpack(cw, s + 1, wf[cur ^ 1]);
+            } else {
+                // stage t+1 has landed once at most the newest AHEAD-1 stages'
+                // DMAs remain; after the barrier nobody reads stage t again.
+                // sched_barrier: sub-step 3's operands stay ahead of the wait.
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vmcnt<VWAIT>();
+                __syncthreads();
+                const char *np = lds + ((t + 1) % NSTAGE) * STAGE + slice;
+                read_w(np, cw);
+                read_x(np, 0, xf[cur ^ 1]);
+                unpack(cw, 0, wf[cur ^ 1]);
             }
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
@@ -521,16 +534,11 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
 #pragma unroll
             for (int j = 0; j < NMF; ++j) {
                 __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                if (s < 3)
-                    __builtin_amdgcn_sched_group_barrier(SG_VALU, NV, 0);
-                if (s < 3 && j < FM)
+                __builtin_amdgcn_sched_group_barrier(SG_VALU, NV, 0);
+                if (j < FM)
                     __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
             }
         }
-        // stage t+1 has landed once at most the newest AHEAD-1 stages' DMAs remain
-        wait_vmcnt<VWAIT>();
-        __syncthreads();
-        read_w(lds + ((t + 1) % NSTAGE) * STAGE + slice, cw);
     }
 
     // ---- epilogue: fp16 tile staged in LDS, then whole-row 16-byte stores ----
