@@ -85,7 +85,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM, wn = wave / WM;
     const int i = lane & 31, g = lane >> 5;
-    const uint32_t magic = magic1024();
+    const Magics mg = make_magics();
 
     const int tile = remap_tile(blockIdx.x, a.tiles_m * a.tiles_n);
     const int tm = tile % a.tiles_m, tn = tile / a.tiles_m;
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
         for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-                wf[mt][fn] = unpack_substep<CODEC>(cw[mt][fn], s, magic);
+                wf[mt][fn] = unpack_substep<CODEC>(cw[mt][fn], s, mg);
     };
 
     f32x16 acc[NMAT][FM][FN];
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     const int wk = wave / NWT, wr = wave % NWT;            // k-slice, wave inside the slice group
     const int wm = wr % WM, wn = wr / WM;
     const int i = lane & 31, g = lane >> 5;
-    const uint32_t magic = magic1024();
+    const Magics mg = make_magics();
 
     int tm, tn;
     grouped_tile(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
         for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-                wf[mt][fn] = unpack_substep<CODEC>(cw[mt][fn], s, magic);
+                wf[mt][fn] = unpack_substep<CODEC>(cw[mt][fn], s, mg);
     };
 
     f32x16 acc[NMAT][FM][FN];

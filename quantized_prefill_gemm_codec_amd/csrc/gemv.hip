@@ -252,13 +252,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(Planes wp, int n, int k, i
         return;
     const int rg = chunk / ksteps, t = chunk - rg * ksteps;
     const int i = lane & 31, g = lane >> 5;
-    const uint32_t magic = magic1024();
+    const Magics mg = make_magics();
     const PlaneRsrc w = plane_rsrc(wp);
     const LaneCodes<CODEC> lc = load_lane<CODEC>(w, lane_offsets<CODEC>(rg, groups, lane), rg, t, ksteps, kb128);
     const int row = rg * 32 + i;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        const f16x8 v = unpack_substep<CODEC>(lc, s, magic);
+        const f16x8 v = unpack_substep<CODEC>(lc, s, mg);
         const int kk = t * 64 + 32 * g + 8 * s;
         if (row < n && kk < k)
             *reinterpret_cast<f16x8 *>(out + int64_t(row) * ldw + kk) = v;

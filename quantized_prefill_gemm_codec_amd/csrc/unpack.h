@@ -3,13 +3,16 @@
 // The pages run every codec through one shared unpack contract that feeds the
 // matrix-unit GEMM, the SwiGLU core and the GEMV (releases page, v0.2.3,
 // TCodec::unpack_column); this header is that stage for gfx950.  All three
-// codecs use the same integer trick: OR-ing a 4-bit (or 2-bit) code into the
-// mantissa of the binary16 pattern 0x6400 (= 1024) gives exactly 1024 + q, two
-// codes per 32-bit register.  One packed fp16 subtraction of an integer
-// constant is then exact and yields the signed integer weight factor, and a
-// single packed multiply (or fused multiply-add) rounds once to the nearest
-// binary16 -- so the fp16 operand handed to the MFMA is the correctly rounded
-// value of the exact codec weight:
+// codecs use the same integer trick: OR-ing a code field into the mantissa of
+// a binary16 power of two 2^E whose mantissa step 2^(E-10) equals the field's
+// own bit weight gives exactly 2^E + q, two codes per 32-bit register (one per
+// half).  Choosing E per field position (E = 10 for bits 0.., 6 for bits 4..
+// of a 4-bit field; E = 10, 8, 6, 4 for 2-bit fields at bits 0, 2, 4, 6)
+// reads each field in place -- one 8-bit shift per code word reaches the rest.
+// One packed fp16 subtraction of 2^E + zero point is then exact and yields the
+// signed integer weight factor, and a single packed multiply (or fused
+// multiply-add) rounds once to the nearest binary16 -- so the fp16 operand
+// handed to the MFMA is the correctly rounded value of the exact codec weight:
 //   Q4_0      w = (q - 8) * d              (v_pk_add_f16, v_pk_mul_f16)
 //   MLX4-G64  w = fma(q, s, b)             (v_pk_add_f16, v_pk_fma_f16)
 //   Q2_0      w = (q - 1) * d, q=3 -> +2d  (v_pk_add_f16, v_pk_mul_f16)
@@ -33,24 +36,25 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
 __device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
-// The binary16 pattern 0x6400 (= 1024) twice, held in a VGPR the compiler
-// cannot see through: with the mask in an SGPR, mask-and-insert then fits one
+// A binary16 power of two, twice, held in a VGPR the compiler cannot see
+// through: with the mask in an SGPR, mask-and-insert then fits one
 // v_and_or_b32 (gfx9 VOP3 encodings take no literal operands).
-__device__ __forceinline__ uint32_t magic1024()
+template <uint32_t V> __device__ __forceinline__ uint32_t opaque_u32()
 {
     uint32_t r;
-    asm("v_mov_b32 %0, 0x64006400" : "=v"(r));
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(V));
     return r;
 }
+__device__ __forceinline__ uint32_t magic1024() { return opaque_u32<0x64006400u>(); }
 
-// (1024 + code_even, 1024 + code_odd) of pair p of a code dword
-__device__ __forceinline__ uint32_t pair4(uint32_t v, int p, uint32_t magic)
+// The insertion constants (2^E, 2^E) of the unpack, one register each.
+struct Magics {
+    uint32_t m1024, m256, m64, m16;
+};
+__device__ __forceinline__ Magics make_magics()
 {
-    return ((v >> (4 * p)) & 0x000F000Fu) | magic;
-}
-__device__ __forceinline__ uint32_t pair2(uint32_t v, int p, uint32_t magic)
-{
-    return ((v >> (2 * p)) & 0x00030003u) | magic;
+    return Magics{opaque_u32<0x64006400u>(), opaque_u32<0x5C005C00u>(), opaque_u32<0x54005400u>(),
+                  opaque_u32<0x4C004C00u>()};
 }
 
 // The codes a lane owns in one (row group, k-step) chunk, plus its scales.
@@ -69,44 +73,55 @@ template <> struct LaneCodes<Q2_0> {
     _Float16 d;
 };
 
-// Integer offset that turns 1024 + q into the signed weight factor.
-template <int CODEC> struct CodeBias;
-template <> struct CodeBias<Q4_0> { static constexpr float v = 1032.0f; };
-template <> struct CodeBias<MLX4_G64> { static constexpr float v = 1024.0f; };
-template <> struct CodeBias<Q2_0> { static constexpr float v = 1025.0f; };
+// Codec zero point: the weight factor is q - z.
+template <int CODEC> struct CodeZero;
+template <> struct CodeZero<Q4_0> { static constexpr int v = 8; };
+template <> struct CodeZero<MLX4_G64> { static constexpr int v = 0; };
+template <> struct CodeZero<Q2_0> { static constexpr int v = 1; };
 
-// Pair p (0..3) of sub-step s (0..3) as exact fp16 integers (q - bias).
-template <int CODEC>
-__device__ __forceinline__ f16x2 factor_pair(const LaneCodes<CODEC> &lc, int s, int p, uint32_t magic)
+// (2^E + q_even, 2^E + q_odd) -> exact fp16 (q_even - z, q_odd - z)
+template <int CODEC, int E>
+__device__ __forceinline__ f16x2 factor(uint32_t bits)
 {
-    constexpr _Float16 off = _Float16(CodeBias<CODEC>::v);
+    constexpr _Float16 off = _Float16(float((1 << E) + CodeZero<CODEC>::v));
     const f16x2 o = {off, off};
-    uint32_t bits;
-    if constexpr (CODEC == Q2_0)
-        bits = pair2(lc.c[s >> 1], 4 * (s & 1) + p, magic);
-    else
-        bits = pair4(lc.c[s], p, magic);
     return as_f16x2(bits) - o;
 }
 
 // The 8 fp16 weights of sub-step s in MFMA operand order (element e = k offset
-// 8 s + e inside the lane's 32-weight slice).
+// 8 s + e inside the lane's 32-weight slice).  Pair p = elements (2p, 2p+1).
 template <int CODEC>
-__device__ __forceinline__ f16x8 unpack_substep(const LaneCodes<CODEC> &lc, int s, uint32_t magic)
+__device__ __forceinline__ f16x8 unpack_substep(const LaneCodes<CODEC> &lc, int s, const Magics &mg)
 {
+    f16x2 q[4];
+    if constexpr (CODEC == Q2_0) {
+        // word s/2 holds sub-steps 2 (s/2) (fields at bits 0..7 of each half)
+        // and 2 (s/2) + 1 (bits 8..15, brought down by one shift)
+        const uint32_t src = (s & 1) ? (lc.c[s >> 1] >> 8) : lc.c[s >> 1];
+        q[0] = factor<CODEC, 10>((src & 0x00030003u) | mg.m1024);
+        q[1] = factor<CODEC, 8>((src & 0x000C000Cu) | mg.m256);
+        q[2] = factor<CODEC, 6>((src & 0x00300030u) | mg.m64);
+        q[3] = factor<CODEC, 4>((src & 0x00C000C0u) | mg.m16);
+    } else {
+        // pairs 0, 1 at bits 0..7 of each half, pairs 2, 3 at bits 8..15
+        const uint32_t w = lc.c[s], w8 = w >> 8;
+        q[0] = factor<CODEC, 10>((w & 0x000F000Fu) | mg.m1024);
+        q[1] = factor<CODEC, 6>((w & 0x00F000F0u) | mg.m64);
+        q[2] = factor<CODEC, 10>((w8 & 0x000F000Fu) | mg.m1024);
+        q[3] = factor<CODEC, 6>((w8 & 0x00F000F0u) | mg.m64);
+    }
     f16x8 out;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        f16x2 q = factor_pair<CODEC>(lc, s, p, magic);
         f16x2 w;
         if constexpr (CODEC == MLX4_G64) {
             const f16x2 sb = as_f16x2(lc.sb);
             const f16x2 sc = {sb[0], sb[0]};
             const f16x2 bi = {sb[1], sb[1]};
-            w = __builtin_elementwise_fma(q, sc, bi);
+            w = __builtin_elementwise_fma(q[p], sc, bi);
         } else {
             const f16x2 dd = {lc.d, lc.d};
-            w = q * dd;
+            w = q[p] * dd;
         }
         out[2 * p] = w[0];
         out[2 * p + 1] = w[1];
