@@ -16,6 +16,8 @@
  *     34 bytes (fp16 scale then 32 bytes of 2-bit codes), w = (q - 1) * d with
  *     the reserved code q = 3 giving +2d.
  *   - project index, Table B: block_q4_0 (GGUF Q4_0) and block_mlx_4bit weights.
+ *   - releases page, v0.3.0, "Quantization Registry Extension": Q8_0 is one of
+ *     the registry's built-in formats (no layout given there).
  *   - comparison page, section 2.2: SwiGLU is SiLU(Gate) x Up on one input X.
  *   - releases page, v0.2 "Honest Verification Labeling": the check is a CPU
  *     double-precision gold computation.
@@ -29,6 +31,8 @@
  *     nibble; scales and biases are fp16; one group per 64 weights along K.
  *   - Q2_0 code order: weight i sits in byte i / 4 of the code field at bit
  *     2 * (i % 4); q = 3 is applied without clamping.
+ *   - Q8_0: GGUF block_q8_0, 34 bytes per 32 weights: fp16 d, then weight j
+ *     as the two's-complement byte 2 + j; w = q * d.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fopenmp -fPIC -shared -lm
  * (no fast-math: every operation is a correctly rounded IEEE fp64 operation).
@@ -45,6 +49,7 @@
 #define ORC_Q4_0 1
 #define ORC_MLX4_G64 2
 #define ORC_Q2_0 3
+#define ORC_Q8_0 4
 
 /* ---------------------------------------------------------------- fp16 --- */
 
@@ -137,6 +142,7 @@ int orc_block_geometry(int codec, int64_t *weights, int64_t *bytes)
     case ORC_Q4_0:     *weights = 32;  *bytes = 18; return 1;
     case ORC_MLX4_G64: *weights = 64;  *bytes = 36; return 1;
     case ORC_Q2_0:     *weights = 128; *bytes = 34; return 1;
+    case ORC_Q8_0:     *weights = 32;  *bytes = 34; return 1;
     default: return 0;
     }
 }
@@ -171,6 +177,21 @@ static void decode_q2_0_row(const uint8_t *row, int64_t k, double *w)
         for (int i = 0; i < 128; ++i) {
             int q = (blk[2 + i / 4] >> (2 * (i % 4))) & 3;
             w[b * 128 + i] = (double)(q - 1) * d;
+        }
+    }
+}
+
+/* Q8_0: per 32-weight block (34 bytes), d = fp16 at bytes 0-1; weight j is
+ * the signed byte 2 + j (two's complement, -128..127) and w = q * d.  Exact in
+ * fp64 (an 8-bit integer times an 11-bit significand). */
+static void decode_q8_0_row(const uint8_t *row, int64_t k, double *w)
+{
+    for (int64_t b = 0; b < k / 32; ++b) {
+        const uint8_t *blk = row + b * 34;
+        double d = orc_f16_to_f64(rd_u16le(blk));
+        for (int j = 0; j < 32; ++j) {
+            int q = blk[2 + j] < 128 ? (int)blk[2 + j] : (int)blk[2 + j] - 256;
+            w[b * 32 + j] = (double)q * d;
         }
     }
 }
@@ -212,6 +233,8 @@ int orc_decode_rows(int codec, const uint8_t *canon, int64_t n, int64_t k,
             decode_q4_0_row(canon + nn * (k / 32) * 18, k, wr);
         else if (codec == ORC_Q2_0)
             decode_q2_0_row(canon + nn * (k / 128) * 34, k, wr);
+        else if (codec == ORC_Q8_0)
+            decode_q8_0_row(canon + nn * (k / 32) * 34, k, wr);
         else {
             const uint8_t *codes = canon;
             const uint8_t *scales = canon + n * (k / 2);

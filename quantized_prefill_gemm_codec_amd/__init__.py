@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libqgemm.so")
 QG_CODEC_Q4_0 = 1
 QG_CODEC_MLX4_G64 = 2
 QG_CODEC_Q2_0 = 3
+QG_CODEC_Q8_0 = 4
 CODECS = {"q4_0": QG_CODEC_Q4_0, "mlx4_g64": QG_CODEC_MLX4_G64, "q2_0": QG_CODEC_Q2_0}
 BLOCK = {QG_CODEC_Q4_0: 32, QG_CODEC_MLX4_G64: 64, QG_CODEC_Q2_0: 128}
 

@@ -11,7 +11,7 @@ using namespace qg;
 
 namespace {
 
-bool valid_codec(int32_t c) { return c == Q4_0 || c == MLX4_G64 || c == Q2_0; }
+bool valid_codec(int32_t c) { return c == Q4_0 || c == MLX4_G64 || c == Q2_0 || c == Q8_0; }
 
 qg_status check_shape(int32_t codec, int64_t n, int64_t k)
 {
@@ -30,6 +30,8 @@ size_t canonical_size(int32_t codec, int64_t n, int64_t k)
         return size_t(n) * size_t(k / 32) * 18;
     if (codec == Q2_0)
         return size_t(n) * size_t(k / 128) * 34;
+    if (codec == Q8_0)
+        return size_t(n) * size_t(k / 32) * 34;
     return size_t(n) * size_t(k / 2) + 2 * size_t(n) * size_t(k / 64) * 2;
 }
 
@@ -40,9 +42,13 @@ inline void wr16(uint8_t *p, uint16_t v)
     p[1] = uint8_t(v >> 8);
 }
 
-// code of weight (row, kk) in the canonical stream
+// code of weight (row, kk) in the canonical stream (Q8_0: q + 128, 0..255)
 inline int canonical_code(int32_t codec, const uint8_t *c, int64_t row, int64_t kk, int64_t k)
 {
+    if (codec == Q8_0) {
+        const uint8_t *blk = c + (row * (k / 32) + kk / 32) * 34;
+        return int(blk[2 + kk % 32] ^ 0x80u);
+    }
     if (codec == Q4_0) {
         const uint8_t *blk = c + (row * (k / 32) + kk / 32) * 18;
         int j = int(kk % 32);
@@ -120,9 +126,10 @@ qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonica
     uint8_t *s = static_cast<uint8_t *>(scales);
     Geometry g = geometry(codec, n, k);
     const int cb = lane_code_bytes(codec);
-    const bool four_bit = codec != Q2_0;
-    // zero-weight code for padding: Q4_0 q = 8, Q2_0 q = 1, MLX q = 0 (s = b = 0)
-    const int pad_code = codec == Q4_0 ? 8 : codec == Q2_0 ? 1 : 0;
+    const bool four_bit = codec == Q4_0 || codec == MLX4_G64;
+    // zero-weight code for padding: Q4_0 q = 8, Q2_0 q = 1, Q8_0 q = 0 (stored
+    // 128), MLX q = 0 (s = b = 0)
+    const int pad_code = codec == Q4_0 ? 8 : codec == Q2_0 ? 1 : codec == Q8_0 ? 128 : 0;
 
     memset(q, 0, size_t(g.qs_bytes));
     memset(s, 0, size_t(g.scale_bytes));
@@ -133,12 +140,19 @@ qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonica
             for (int l = 0; l < 64; ++l) {
                 const int gh = l / 32, i = l % 32;
                 const int64_t row = r * 32 + i;
-                uint8_t *lane = chunk + l * cb;
+                uint8_t *lane = chunk + l * (cb == 32 ? 16 : cb);
                 for (int j = 0; j < 32; ++j) {
                     const int64_t kk = t * 64 + gh * 32 + j;
                     const int code = (row < n && kk < k) ? canonical_code(codec, c, row, kk, k) : pad_code;
                     int byte, shift;
-                    if (four_bit) {
+                    if (codec == Q8_0) {
+                        // word 2 s + e / 4 of the lane's 8; words 4 h .. 4 h + 3
+                        // sit in the chunk's half h (1 KiB apart)
+                        const int s8 = j / 8, e = j % 8, word = 2 * s8 + e / 4, e4 = e % 4;
+                        const int bit = 8 * (e4 / 2) + 16 * (e4 % 2);
+                        byte = (word / 4) * 1024 + (word % 4) * 4 + bit / 8;
+                        shift = 0;
+                    } else if (four_bit) {
                         const int dw = j / 8, e = j % 8;
                         const int bit = 4 * (e / 2) + 16 * (e % 2);
                         byte = 4 * dw + bit / 8;
@@ -158,10 +172,11 @@ qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonica
     // scale / bias planes (padding entries stay zero -> padded weights decode to 0)
     for (int64_t row = 0; row < n; ++row) {
         const int64_t r = row / 32, i = row % 32;
-        if (codec == Q4_0) {
+        if (codec == Q4_0 || codec == Q8_0) {
+            const int64_t bb = codec == Q4_0 ? 18 : 34;
             for (int64_t blk = 0; blk < k / 32; ++blk) {
                 const int64_t t = blk / 2, gh = blk % 2;
-                wr16(s + (((r * g.ksteps + t) * 2 + gh) * 32 + i) * 2, rd16(c + (row * (k / 32) + blk) * 18));
+                wr16(s + (((r * g.ksteps + t) * 2 + gh) * 32 + i) * 2, rd16(c + (row * (k / 32) + blk) * bb));
             }
         } else if (codec == Q2_0) {
             const int64_t nb = k / 128;

@@ -22,11 +22,17 @@
 //    with e = 2p at bits [4p, 4p+4) and e = 2p + 1 at bits [16+4p, 20+4p).
 //  * 2-bit (Q2_0): 8 bytes = 2 dwords; dword h holds j = 16 h + e, with
 //    e = 2p at bits [2p, 2p+2) and e = 2p + 1 at bits [16+2p, 18+2p).
+//  * 8-bit (Q8_0): 32 bytes = 8 dwords, stored as two 16-byte halves 1 KiB
+//    apart (the chunk is [half 0 of all 64 lanes][half 1 of all 64 lanes], so
+//    each half is one contiguous 128-bit wave load); dword 2 s + h' holds
+//    j = 8 s + 4 h' + e, with e = 0, 1, 2, 3 at bits 0, 16, 8, 24, as the
+//    unsigned byte q + 128.
 // So every extracted pair lands as (low half, high half) = (even e, odd e),
 // the element order of a packed fp16 register.
 //
 // Scale planes, one 64-lane (Q4_0) or 32-lane record per chunk:
 //  * Q4_0:     fp16 [N/32][K/64][2][32]  -- d of block 2t+g for lane (g, i)
+//  * Q8_0:     same as Q4_0
 //  * MLX4-G64: u32  [N/32][K/64][32]     -- (s, b) of group t as two fp16
 //                                           (scale low half, bias high half),
 //                                           so one 32-bit load brings both
@@ -46,17 +52,17 @@
 
 namespace qg {
 
-enum Codec : int32_t { Q4_0 = 1, MLX4_G64 = 2, Q2_0 = 3 };
+enum Codec : int32_t { Q4_0 = 1, MLX4_G64 = 2, Q2_0 = 3, Q8_0 = 4 };
 
 QG_HD inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 QG_HD inline int block_size(int codec)
 {
-    return codec == Q4_0 ? 32 : codec == MLX4_G64 ? 64 : codec == Q2_0 ? 128 : 0;
+    return codec == Q4_0 ? 32 : codec == MLX4_G64 ? 64 : codec == Q2_0 ? 128 : codec == Q8_0 ? 32 : 0;
 }
 
 // bytes of codes a lane holds per chunk
-QG_HD inline int lane_code_bytes(int codec) { return codec == Q2_0 ? 8 : 16; }
+QG_HD inline int lane_code_bytes(int codec) { return codec == Q2_0 ? 8 : codec == Q8_0 ? 32 : 16; }
 
 struct Geometry {
     int64_t groups;   // row groups (N padded to 32) / 32
@@ -70,7 +76,7 @@ QG_HD inline Geometry geometry(int codec, int64_t n, int64_t k)
     g.groups = ceil_div(n, QG_ROWS_PER_GROUP);
     g.ksteps = ceil_div(k, QG_KSTEP);
     g.qs_bytes = g.groups * g.ksteps * 64 * lane_code_bytes(codec);
-    if (codec == Q4_0)
+    if (codec == Q4_0 || codec == Q8_0)
         g.scale_bytes = g.groups * g.ksteps * 64 * 2;
     else if (codec == MLX4_G64)
         g.scale_bytes = g.groups * g.ksteps * 32 * 4;

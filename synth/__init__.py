@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for the quantized prefill GEMM path.
 
 This module only draws random numbers and lays them out in the canonical
-byte formats of the three weight codecs.  It performs no dequantization and
+byte formats of the weight codecs.  It performs no dequantization and
 no products: decoding and contraction belong to the oracle (``oracle/``) and
 to the HIP library, which share nothing but these inputs.
 
@@ -19,11 +19,17 @@ Canonical byte formats (the input contract both sides read):
   Ternary Codec"): blocks of 128 weights, 34 bytes: fp16 ``d`` in bytes 0-1,
   then 32 bytes of 2-bit codes, weight ``i`` in byte ``2 + i // 4`` at bit
   ``2 * (i % 4)``.  Weight value ``(q - 1) * d``.
+* Q8_0 (GGUF block_q8_0; the registry of the releases page, v0.3.0, lists Q8_0
+  without a layout): blocks of 32 weights, 34 bytes: fp16 ``d`` in bytes 0-1,
+  then weight ``j`` as the two's-complement byte ``2 + j``.  Weight value
+  ``q * d``.
 
 Distributions and shapes follow the five workloads of the method: fp16
 activations ~N(0,1); Q4_0 scales ~U(0.005, 0.02) with codes ~U{0..15}; MLX
 scales ~U(0.002, 0.01), biases ~N(0, 0.02), codes ~U{0..15}; Q2_0 scales
-~U(0.01, 0.05) with P(q=0,1,2,3) = 0.30, 0.35, 0.30, 0.05.
+~U(0.01, 0.05) with P(q=0,1,2,3) = 0.30, 0.35, 0.30, 0.05.  The Q8_0 workload
+(a next-step codec, not one of the five) uses codes ~U{-127..127} and scales
+~U(0.0005, 0.0015), which keeps its weights in the Q4_0 workload's range.
 
 Random streams: numpy PCG64 seeded from ``SeedSequence([seed, tensor_id])``
 so every tensor of every workload has its own reproducible stream.
@@ -37,10 +43,11 @@ import numpy as np
 CODEC_Q4_0 = 1
 CODEC_MLX4_G64 = 2
 CODEC_Q2_0 = 3
+CODEC_Q8_0 = 4
 
-CODEC_NAMES = {CODEC_Q4_0: "q4_0", CODEC_MLX4_G64: "mlx4_g64", CODEC_Q2_0: "q2_0"}
+CODEC_NAMES = {CODEC_Q4_0: "q4_0", CODEC_MLX4_G64: "mlx4_g64", CODEC_Q2_0: "q2_0", CODEC_Q8_0: "q8_0"}
 # weights per block (scale group) along K
-BLOCK = {CODEC_Q4_0: 32, CODEC_MLX4_G64: 64, CODEC_Q2_0: 128}
+BLOCK = {CODEC_Q4_0: 32, CODEC_MLX4_G64: 64, CODEC_Q2_0: 128, CODEC_Q8_0: 32}
 
 BASE_SEED = 0x51C0DEC0
 
@@ -63,6 +70,8 @@ def canonical_bytes(codec: int, n: int, k: int) -> int:
         return n * (k // 2) + 2 * (n * (k // 64) * 2)
     if codec == CODEC_Q2_0:
         return n * (k // 128) * 34
+    if codec == CODEC_Q8_0:
+        return n * (k // 32) * 34
     raise ValueError(codec)
 
 
@@ -110,6 +119,16 @@ def encode_q2_0(codes: np.ndarray, d: np.ndarray) -> np.ndarray:
     return out.reshape(-1)
 
 
+def encode_q8_0(codes: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Lay out codes [n, k] (int8) and fp16 scales [n, k/32] as Q8_0 blocks."""
+    n, k = codes.shape
+    nb = k // 32
+    out = np.empty((n, nb, 34), dtype=np.uint8)
+    out[:, :, 0:2] = d.astype("<f2").reshape(n, nb, 1).view(np.uint8).reshape(n, nb, 2)
+    out[:, :, 2:34] = codes.astype(np.int8).reshape(n, nb, 32).view(np.uint8)
+    return out.reshape(-1)
+
+
 def gen_q4_0(n: int, k: int, seed: int, tensor_id: int = T_W,
              d_range=(0.005, 0.02)) -> np.ndarray:
     rng = _rng(seed, tensor_id)
@@ -140,7 +159,15 @@ def gen_q2_0(n: int, k: int, seed: int, tensor_id: int = T_W,
     return encode_q2_0(codes, d)
 
 
-GEN = {CODEC_Q4_0: gen_q4_0, CODEC_MLX4_G64: gen_mlx4, CODEC_Q2_0: gen_q2_0}
+def gen_q8_0(n: int, k: int, seed: int, tensor_id: int = T_W,
+             d_range=(0.0005, 0.0015)) -> np.ndarray:
+    rng = _rng(seed, tensor_id)
+    codes = rng.integers(-127, 128, size=(n, k), dtype=np.int16).astype(np.int8)
+    d = fp16_uniform(rng, d_range[0], d_range[1], (n, k // 32))
+    return encode_q8_0(codes, d)
+
+
+GEN = {CODEC_Q4_0: gen_q4_0, CODEC_MLX4_G64: gen_mlx4, CODEC_Q2_0: gen_q2_0, CODEC_Q8_0: gen_q8_0}
 
 
 def gen_weight(codec: int, n: int, k: int, seed: int, tensor_id: int = T_W) -> np.ndarray:
@@ -183,4 +210,6 @@ WORKLOADS = {
     "q2_0_prefill_2048x4096x4096": Workload("q2_0_prefill_2048x4096x4096", "prefill", CODEC_Q2_0, 2048, 4096, 4096, BASE_SEED + 4),
     "q4_0_gemv_1x4096x14336": Workload("q4_0_gemv_1x4096x14336", "gemv", CODEC_Q4_0, 1, 4096, 14336, BASE_SEED + 5),
     "q4_0_gemv_64x4096x14336": Workload("q4_0_gemv_64x4096x14336", "gemv", CODEC_Q4_0, 64, 4096, 14336, BASE_SEED + 5),
+    # next-step codec on the 1B-shape up-projection
+    "q8_0_prefill_2048x2048x8192": Workload("q8_0_prefill_2048x2048x8192", "prefill", CODEC_Q8_0, 2048, 2048, 8192, BASE_SEED + 6),
 }

@@ -39,13 +39,14 @@ def test_library_exports_every_declared_symbol():
     assert qg.qg_version() == 100
 
 
-@pytest.mark.parametrize("codec,n,k", [(1, 8192, 2048), (1, 40, 96), (2, 14336, 4096), (3, 4096, 4096), (3, 33, 128)])
+@pytest.mark.parametrize("codec,n,k", [(1, 8192, 2048), (1, 40, 96), (2, 14336, 4096), (3, 4096, 4096), (3, 33, 128),
+                                     (4, 8192, 2048), (4, 40, 96)])
 def test_sizes(codec, n, k):
     qs, sc = qg.qg_packed_sizes(codec, n, k)
     groups, ksteps = -(-n // 32), -(-k // 64)
-    code_bytes = 8 if codec == 3 else 16
+    code_bytes = {1: 16, 2: 16, 3: 8, 4: 32}[codec]
     assert qs == groups * ksteps * 64 * code_bytes
-    if codec == 1:
+    if codec in (1, 4):
         assert sc == groups * ksteps * 64 * 2
     elif codec == 2:
         assert sc == groups * ksteps * 32 * 4
@@ -57,11 +58,20 @@ def test_sizes(codec, n, k):
 def _read_planar(codec, n, k, qs, sc):
     """Independent reader of the planar layout -> (codes [n,k], scale, bias)."""
     groups, ksteps = -(-n // 32), -(-k // 64)
-    cb = 8 if codec == 3 else 16
-    lanes = qs.reshape(groups, ksteps, 64, cb)
+    cb = {1: 16, 2: 16, 3: 8, 4: 32}[codec]
+    if codec == 4:
+        halves = qs.reshape(groups, ksteps, 2, 64, 16)
+    else:
+        lanes = qs.reshape(groups, ksteps, 64, cb)
     codes = np.zeros((groups * 32, ksteps * 64), np.int64)
     for j in range(32):
-        if codec == 3:
+        if codec == 4:
+            # dword 2 s + h' (h' = e // 4) of the lane; dwords 4 h .. 4 h + 3 in half h
+            word = 2 * (j // 8) + (j % 8) // 4
+            e4 = (j % 8) % 4
+            bit = 8 * (e4 // 2) + 16 * (e4 % 2)
+            q = halves[:, :, word // 4, :, (word % 4) * 4 + bit // 8].astype(np.int64) - 128
+        elif codec == 3:
             dw, e = divmod(j, 16)
             bit = 2 * (e // 2) + 16 * (e % 2)
             byte = lanes[..., 4 * dw + bit // 8].astype(np.int64)
@@ -79,7 +89,7 @@ def _read_planar(codec, n, k, qs, sc):
     codes = codes[:n, :k]
     kk = np.arange(k)
     rr = np.arange(n)
-    if codec == 1:
+    if codec in (1, 4):
         d = sc.view(np.float16).reshape(groups, ksteps, 2, 32)
         blk = kk // 32
         scale = d[rr[:, None] // 32, blk[None, :] // 2, blk[None, :] % 2, rr[:, None] % 32]
@@ -97,12 +107,15 @@ def _read_planar(codec, n, k, qs, sc):
 def _value(codec, codes, scale, bias):
     if codec == 1:
         return (codes - 8) * scale
+    if codec == 4:
+        return codes * scale
     if codec == 2:
         return codes * scale + bias
     return (codes - 1) * scale
 
 
-@pytest.mark.parametrize("codec,n,k", [(1, 40, 96), (1, 64, 64), (2, 33, 192), (3, 37, 256), (3, 32, 128)])
+@pytest.mark.parametrize("codec,n,k", [(1, 40, 96), (1, 64, 64), (2, 33, 192), (3, 37, 256), (3, 32, 128),
+                                     (4, 40, 96), (4, 64, 128)])
 def test_pack_roundtrip_random(codec, n, k):
     canon = synth.gen_weight(codec, n, k, 77)
     qs, sc = qg.qg_pack_host(codec, n, k, canon)

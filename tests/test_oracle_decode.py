@@ -3,8 +3,9 @@
 * Hand-worked fixtures (tests/golden/*.txt): byte strings whose weights follow
   from the formulas on the pages by hand -- Q2_0 w = (q - 1) d with q = 3 -> +2d
   in 34-byte, 128-weight blocks; Q4_0 w = (q - 8) d in 18-byte, 32-weight
-  blocks; MLX w = q s + b per 64-weight group.  They fix the offsets, signs,
-  nibble / bit order, block strides and row strides.
+  blocks; MLX w = q s + b per 64-weight group; Q8_0 w = q d with q a signed
+  byte (GGUF block_q8_0, a reading).  They fix the offsets, signs, nibble / bit
+  order, block strides and row strides.
 * Geometry printed on the pages: Q2_0 is 2.125 bits per weight.
 * Closed forms: MLX q = 0 gives the bias bit for bit; the fp16 image of each
   weight equals numpy's correctly rounded conversion of the exact value.
@@ -40,6 +41,12 @@ def test_q4_0_geometry():
     assert oracle.block_geometry(oracle.Q4_0) == (32, 18)
 
 
+def test_q8_0_geometry():
+    weights, nbytes = oracle.block_geometry(oracle.Q8_0)
+    assert (weights, nbytes) == (32, 34)
+    assert nbytes * 8 / weights == 8.5
+
+
 def test_decode_rejects_bad_shapes():
     with pytest.raises(ValueError):
         oracle.decode(oracle.Q4_0, np.zeros(18, np.uint8), 1, 48)
@@ -64,7 +71,7 @@ def _random_canon(codec, n, k, seed):
     return synth.gen_weight(codec, n, k, seed)
 
 
-@pytest.mark.parametrize("codec", [1, 2, 3])
+@pytest.mark.parametrize("codec", [1, 2, 3, 4])
 def test_dequant_f16_matches_numpy_rounding(codec):
     n, k = 16, 512
     canon = _random_canon(codec, n, k, 99)
@@ -101,6 +108,16 @@ def test_generator_q2_0_encoding_matches_decode():
     d = rng.uniform(0.01, 0.05, (n, k // 128)).astype(np.float16)
     w = oracle.decode(3, synth.encode_q2_0(codes, d), n, k)
     want = (codes.astype(np.float64) - 1) * np.repeat(d.astype(np.float64), 128, axis=1)
+    assert np.array_equal(w, want)
+
+
+def test_generator_q8_0_encoding_matches_decode():
+    rng = np.random.default_rng(6)
+    n, k = 3, 128
+    codes = rng.integers(-128, 128, (n, k)).astype(np.int8)
+    d = rng.uniform(0.0005, 0.0015, (n, k // 32)).astype(np.float16)
+    w = oracle.decode(4, synth.encode_q8_0(codes, d), n, k)
+    want = codes.astype(np.float64) * np.repeat(d.astype(np.float64), 32, axis=1)
     assert np.array_equal(w, want)
 
 
