@@ -318,7 +318,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     constexpr int FM = TM / 32, FN = TN / 32;
     constexpr int NMAT = SWIGLU ? 2 : 1;
     constexpr int RG = BN / 32;                            // row groups per matrix per tile
-    constexpr int CB = CODEC == Q2_0 ? 8 : 16;             // code bytes per lane per chunk
+    constexpr int CB = CODEC == Q2_0 ? 8 : CODEC == Q8_0 ? 32 : 16;   // code bytes per lane per chunk
     constexpr int WCH = 64 * CB;                           // bytes per (row group, k-step) chunk
     constexpr int SB = CODEC == Q2_0 ? 64 : 128;           // scale bytes per (row group, k-step)
     constexpr int X_OFF = 0, X_BYTES = BM * 128;
@@ -376,17 +376,19 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
         xvt[u] = (ch * 8 < ktail) ? xv[u] : OOB;
     }
     // codes: instruction j covers chunk bytes [1024 j, 1024 j + 1024) of the
-    // stage's code area (one 4-bit chunk, or two 2-bit chunks)
+    // stage's code area (one 4-bit chunk, two 2-bit chunks, or one half of an
+    // 8-bit chunk)
     uint32_t wv[WPW];
     int wmat[WPW];
 #pragma unroll
     for (int u = 0; u < WPW; ++u) {
         const int j = wr + NWT * u;
-        const int c = (CB == 16) ? j : 2 * j + (lane >> 5);
-        const int mt = c / RG, rg = c % RG;
-        const uint32_t lo = (CB == 16) ? uint32_t(lane) * 16 : uint32_t(lane & 31) * 16;
-        wmat[u] = ((CB == 16) ? j : 2 * j) / RG;     // wave-uniform: RG is even
-        (void)mt;
+        const int c = CB == 16 ? j : CB == 32 ? (j >> 1) : 2 * j + (lane >> 5);
+        const int rg = c % RG;
+        const uint32_t lo = CB == 16 ? uint32_t(lane) * 16
+                          : CB == 32 ? uint32_t(j & 1) * 1024 + uint32_t(lane) * 16
+                                     : uint32_t(lane & 31) * 16;
+        wmat[u] = (CB == 16 ? j : CB == 32 ? (j >> 1) : 2 * j) / RG;     // wave-uniform: RG is even
         wv[u] = (j < NWI && rg0 + rg < a.groups) ? uint32_t(rg0 + rg) * uint32_t(a.ksteps) * WCH + lo : OOB;
     }
     // scales: dword instruction j covers bytes [256 j, 256 j + 256) of the
@@ -451,9 +453,13 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
                 const int c = mt * RG + wn * FN + fn;
-                const char *wp = st + W_OFF + c * WCH + lane * CB;
+                const char *wp = st + W_OFF + c * WCH + lane * (CB == 32 ? 16 : CB);
                 const char *sp = st + S_OFF + c * SB;
-                if constexpr (CODEC == Q2_0) {
+                if constexpr (CODEC == Q8_0) {
+                    cw[mt][fn].lo = *reinterpret_cast<const u32x4 *>(wp);
+                    cw[mt][fn].hi = *reinterpret_cast<const u32x4 *>(wp + 1024);
+                    cw[mt][fn].d = *reinterpret_cast<const _Float16 *>(sp + lane * 2);
+                } else if constexpr (CODEC == Q2_0) {
                     cw[mt][fn].c = *reinterpret_cast<const u32x2 *>(wp);
                     cw[mt][fn].d = *reinterpret_cast<const _Float16 *>(sp + i * 2);
                 } else {
@@ -708,6 +714,7 @@ hipError_t launch_gemm(const GemmProblem &p, bool swiglu, hipStream_t stream)
     case Q4_0: return launch_codec<Q4_0>(p, swiglu, stream);
     case MLX4_G64: return launch_codec<MLX4_G64>(p, swiglu, stream);
     case Q2_0: return launch_codec<Q2_0>(p, swiglu, stream);
+    case Q8_0: return launch_codec<Q8_0>(p, swiglu, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -55,7 +55,9 @@ __device__ __forceinline__ void slice_correction(const u32x4 *chunks, float *out
         for (int p = 0; p < 4; ++p)
             sp[p] += float(v[2 * p]) + float(v[2 * p + 1]);
     }
-    if constexpr (CODEC == Q4_0) {
+    if constexpr (CODEC == Q8_0) {
+        out[0] = -1152.0f * ((sp[0] + sp[1]) + (sp[2] + sp[3]));
+    } else if constexpr (CODEC == Q4_0) {
         out[0] = -1032.0f * (sp[0] + sp[2]) - 72.0f * (sp[1] + sp[3]);
     } else if constexpr (CODEC == MLX4_G64) {
         out[0] = -1024.0f * (sp[0] + sp[2]) - 64.0f * (sp[1] + sp[3]);
@@ -66,9 +68,6 @@ __device__ __forceinline__ void slice_correction(const u32x4 *chunks, float *out
     }
 }
 
-template <int CODEC> struct CodeWords { using type = u32x4; };
-template <> struct CodeWords<Q2_0> { using type = u32x2; };
-
 // Dot products of a lane's 32 codes with the matching X values, taken on the
 // codes as they sit in the packed word: OR-ing a code field into the mantissa
 // of binary16 1024 gives 1024 + 2^f q for a field at bit f of the half-word
@@ -77,13 +76,31 @@ template <> struct CodeWords<Q2_0> { using type = u32x2; };
 // fp32; per class of fields with the same factor 2^f one fp32 partial sum:
 //   Q4_0 / MLX4:  d[0] (fields at bits 0, 8 -> factor 1), d[1] (bits 4, 12 -> 16)
 //   Q2_0:         d[p] (fields at bits 2p, 8 + 2p -> factor 4^p), p = 0..3
+//   Q8_0:         d[0] (bytes at bits 0, 8 -> factor 1; stored q + 128)
 // block_sum then removes the 1024 offsets (and the codec zero point) with the
 // precomputed X term: sum_k (q_k - z) x_k = sum_c d[c] / 2^f_c + corr.
 template <int CODEC, int MM>
-__device__ __forceinline__ void slice_dots(const typename CodeWords<CODEC>::type &c, const u32x4 *const (&xrow)[MM],
+__device__ __forceinline__ void slice_dots(const LaneCodes<CODEC> &lc, const u32x4 *const (&xrow)[MM],
                                            uint32_t magic, float (&d)[4][MM])
 {
-    if constexpr (CODEC == Q2_0) {
+    if constexpr (CODEC == Q8_0) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const u32x4 h = (s < 2) ? lc.lo : lc.hi;
+            const uint32_t a = h[2 * (s & 1)], b = h[2 * (s & 1) + 1];
+            const uint32_t h0 = (a & 0x00FF00FFu) | magic, h1 = ((a >> 8) & 0x00FF00FFu) | magic;
+            const uint32_t h2 = (b & 0x00FF00FFu) | magic, h3 = ((b >> 8) & 0x00FF00FFu) | magic;
+#pragma unroll
+            for (int mr = 0; mr < MM; ++mr) {
+                const u32x4 xv = xrow[mr][s];
+                d[0][mr] = __builtin_amdgcn_fdot2(as_f16x2(h0), as_f16x2(xv[0]), d[0][mr], false);
+                d[0][mr] = __builtin_amdgcn_fdot2(as_f16x2(h1), as_f16x2(xv[1]), d[0][mr], false);
+                d[0][mr] = __builtin_amdgcn_fdot2(as_f16x2(h2), as_f16x2(xv[2]), d[0][mr], false);
+                d[0][mr] = __builtin_amdgcn_fdot2(as_f16x2(h3), as_f16x2(xv[3]), d[0][mr], false);
+            }
+        }
+    } else if constexpr (CODEC == Q2_0) {
+        const u32x2 c = lc.c;
 #pragma unroll
         for (int wi = 0; wi < 2; ++wi) {
             const uint32_t wv = c[wi];
@@ -101,6 +118,7 @@ __device__ __forceinline__ void slice_dots(const typename CodeWords<CODEC>::type
             }
         }
     } else {
+        const u32x4 c = lc.c;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const uint32_t wv = c[s], w8 = wv >> 8;
@@ -124,7 +142,9 @@ template <int CODEC>
 __device__ __forceinline__ float block_sum(uint32_t sc, const float (&d)[4], const float *corr, float acc)
 {
     const f16x2 sb = as_f16x2(sc);
-    if constexpr (CODEC == Q2_0) {
+    if constexpr (CODEC == Q8_0) {
+        return __builtin_fmaf(float(sb[0]), d[0] + corr[0], acc);
+    } else if constexpr (CODEC == Q2_0) {
         const float v = __builtin_fmaf(d[3], 0.015625f, __builtin_fmaf(d[2], 0.0625f, __builtin_fmaf(d[1], 0.25f, d[0])));
         return __builtin_fmaf(float(sb[0]), v + corr[0], acc);
     } else if constexpr (CODEC == Q4_0) {
@@ -199,7 +219,7 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
 #pragma unroll
                     for (int mr = 0; mr < MM; ++mr)
                         dots[c][mr] = 0.0f;
-                slice_dots<CODEC, MM>(lc[u].c, xrow, magic, dots);
+                slice_dots<CODEC, MM>(lc[u], xrow, magic, dots);
                 uint32_t sc;
                 if constexpr (CODEC == MLX4_G64)
                     sc = lc[u].sb;
@@ -328,6 +348,7 @@ hipError_t launch_gemv(const GemmProblem &p, hipStream_t stream)
     case Q4_0: return launch_gemv_codec<Q4_0>(p, stream);
     case MLX4_G64: return launch_gemv_codec<MLX4_G64>(p, stream);
     case Q2_0: return launch_gemv_codec<Q2_0>(p, stream);
+    case Q8_0: return launch_gemv_codec<Q8_0>(p, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -346,6 +367,7 @@ hipError_t launch_dequant(const GemmProblem &p, _Float16 *out, int64_t ldw, hipS
     case Q4_0: fn = reinterpret_cast<const void *>(&dequant_kernel<Q4_0>); break;
     case MLX4_G64: fn = reinterpret_cast<const void *>(&dequant_kernel<MLX4_G64>); break;
     case Q2_0: fn = reinterpret_cast<const void *>(&dequant_kernel<Q2_0>); break;
+    case Q8_0: fn = reinterpret_cast<const void *>(&dequant_kernel<Q8_0>); break;
     default: return hipErrorInvalidValue;
     }
     return hipLaunchKernel(fn, grid, block, args, 0, stream);

@@ -16,6 +16,7 @@
 //   Q4_0      w = (q - 8) * d              (v_pk_add_f16, v_pk_mul_f16)
 //   MLX4-G64  w = fma(q, s, b)             (v_pk_add_f16, v_pk_fma_f16)
 //   Q2_0      w = (q - 1) * d, q=3 -> +2d  (v_pk_add_f16, v_pk_mul_f16)
+//   Q8_0      w = q * d, stored q + 128    (v_pk_add_f16, v_pk_mul_f16)
 // (Q2_0 values are exact; Q4_0 and MLX round once.  fp16 subnormals are kept:
 // an MLX weight with q = 0 is its bias, which may be subnormal.)
 #pragma once
@@ -72,12 +73,17 @@ template <> struct LaneCodes<Q2_0> {
     u32x2 c;
     _Float16 d;
 };
+template <> struct LaneCodes<Q8_0> {
+    u32x4 lo, hi;    // dwords 0..3 (sub-steps 0, 1) and 4..7 (sub-steps 2, 3)
+    _Float16 d;
+};
 
 // Codec zero point: the weight factor is q - z.
 template <int CODEC> struct CodeZero;
 template <> struct CodeZero<Q4_0> { static constexpr int v = 8; };
 template <> struct CodeZero<MLX4_G64> { static constexpr int v = 0; };
 template <> struct CodeZero<Q2_0> { static constexpr int v = 1; };
+template <> struct CodeZero<Q8_0> { static constexpr int v = 128; };   // codes are stored as q + 128
 
 // (2^E + q_even, 2^E + q_odd) -> exact fp16 (q_even - z, q_odd - z)
 template <int CODEC, int E>
@@ -94,7 +100,16 @@ template <int CODEC>
 __device__ __forceinline__ f16x8 unpack_substep(const LaneCodes<CODEC> &lc, int s, const Magics &mg)
 {
     f16x2 q[4];
-    if constexpr (CODEC == Q2_0) {
+    if constexpr (CODEC == Q8_0) {
+        // sub-step s: dwords 2s (elements 0..3) and 2s + 1 (4..7), bytes at
+        // bits 0, 16 (pair 0 / 2) and 8, 24 (pair 1 / 3 after one shift)
+        const u32x4 h = (s < 2) ? lc.lo : lc.hi;
+        const uint32_t a = h[2 * (s & 1)], b = h[2 * (s & 1) + 1];
+        q[0] = factor<CODEC, 10>((a & 0x00FF00FFu) | mg.m1024);
+        q[1] = factor<CODEC, 10>(((a >> 8) & 0x00FF00FFu) | mg.m1024);
+        q[2] = factor<CODEC, 10>((b & 0x00FF00FFu) | mg.m1024);
+        q[3] = factor<CODEC, 10>(((b >> 8) & 0x00FF00FFu) | mg.m1024);
+    } else if constexpr (CODEC == Q2_0) {
         // word s/2 holds sub-steps 2 (s/2) (fields at bits 0..7 of each half)
         // and 2 (s/2) + 1 (bits 8..15, brought down by one shift)
         const uint32_t src = (s & 1) ? (lc.c[s >> 1] >> 8) : lc.c[s >> 1];
@@ -183,7 +198,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int rg, int groups, int lane
     } else if constexpr (CODEC == Q2_0) {
         o.q = uint32_t(lane) * 8;
         o.s = i * 2;
-    } else if constexpr (CODEC == Q4_0) {
+    } else if constexpr (CODEC == Q4_0 || CODEC == Q8_0) {
         o.q = uint32_t(lane) * 16;
         o.s = uint32_t(lane) * 2;
     } else {
@@ -203,7 +218,11 @@ __device__ __forceinline__ LaneCodes<CODEC> load_lane(const PlaneRsrc &w, LaneOf
 {
     LaneCodes<CODEC> lc;
     const uint32_t chunk = uint32_t(rg) * uint32_t(ksteps) + uint32_t(t);
-    if constexpr (CODEC == Q2_0) {
+    if constexpr (CODEC == Q8_0) {
+        lc.lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 2048, 0));
+        lc.hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 2048 + 1024, 0));
+        lc.d = load_f16(w.sc, o.s, chunk * 128);
+    } else if constexpr (CODEC == Q2_0) {
         lc.c = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(w.qs, o.q, chunk * 512, 0));
         lc.d = load_f16(w.sc, o.s, (uint32_t(rg) * kb128 + uint32_t(t >> 1)) * 64);
     } else {
