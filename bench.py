@@ -41,7 +41,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 MALL_BYTES = 256 << 20
 HEADLINE = "q4_0_prefill_2048x2048x8192"
 SECONDARY = ["mlx4_swiglu_2048x4096x14336", "q2_0_prefill_2048x4096x4096",
-             "q4_0_gemv_1x4096x14336", "q4_0_gemv_64x4096x14336", "q8_0_prefill_2048x2048x8192"]
+             "q4_0_gemv_1x4096x14336", "q4_0_gemv_64x4096x14336", "q8_0_prefill_2048x2048x8192",
+             "mlx4_geglu_2048x4096x14336"]
 KERNEL_SOURCES = ["gemm.hip", "gemv.hip", "unpack.h", "planar.h", "lds_dma.h"]
 
 
@@ -85,8 +86,9 @@ class Prepared:
         stream = qg._stream(None)
         self.calls = []
         for ws, xd, y, ldy in self.sets:
-            if wl.op == "swiglu":
-                self.calls.append((L.qgemm_swiglu, (ws[0].desc, ws[1].desc, xd.data_ptr(), wl.m, wl.k,
+            if wl.op in synth.GATED:
+                fn = L.qgemm_swiglu if wl.op == "swiglu" else L.qgemm_geglu
+                self.calls.append((fn, (ws[0].desc, ws[1].desc, xd.data_ptr(), wl.m, wl.k,
                                                     y.data_ptr(), ldy, stream)))
             elif wl.op == "gemv":
                 self.calls.append((L.qgemv_decode, (ws[0].desc, xd.data_ptr(), wl.m, wl.k, y.data_ptr(), ldy, stream)))
@@ -148,13 +150,13 @@ def cpu_baseline(torch, prep, target_s=12.0):
     import oracle
     wl = prep.wl
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count() or 1
-    per_row_flops = 2 * wl.n * wl.k * (2 if wl.op == "swiglu" else 1)
+    per_row_flops = 2 * wl.n * wl.k * (2 if wl.op in synth.GATED else 1)
 
     def run(rows):
         t0 = time.perf_counter()
-        if wl.op == "swiglu":
-            ref = oracle.swiglu_ref(wl.codec, prep.canon[0], prep.canon[1], wl.n, wl.k, prep.x_host[:rows],
-                                    threads=threads)
+        if wl.op in synth.GATED:
+            fn = oracle.swiglu_ref if wl.op == "swiglu" else oracle.geglu_ref
+            ref = fn(wl.codec, prep.canon[0], prep.canon[1], wl.n, wl.k, prep.x_host[:rows], threads=threads)
         else:
             ref = oracle.gemm_ref(wl.codec, prep.canon[0], wl.n, wl.k, prep.x_host[:rows], threads=threads)
         return ref, time.perf_counter() - t0

@@ -111,6 +111,15 @@ qg_status qgemm_prefill(const qg_weight *w, const void *x, int64_t m, int64_t ld
 qg_status qgemm_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x,
                        int64_t m, int64_t ldx, void *out, int64_t ldo, void *stream);
 
+/* Fused gate/up projection with the GeGLU epilogue: the SwiGLU entry point
+ * with GELU in place of SiLU (releases page, v0.3.0, TransformerBlock: SwiGLU /
+ * GeGLU activations).  GELU is the tanh form used by the Gemma family that
+ * page names: GELU(g) = 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))),
+ * evaluated in fp32 on the accumulators and rounded once to fp16.  Arguments,
+ * layouts and errors as for qgemm_swiglu. */
+qg_status qgemm_geglu(const qg_weight *wg, const qg_weight *wu, const void *x,
+                      int64_t m, int64_t ldx, void *out, int64_t ldo, void *stream);
+
 /* Weight-streaming small-M projection (decode, M = 1, and speculative
  * verification of up to 64 candidate rows): Y = X W^T as for qgemm_prefill,
  * for 1 <= m <= 64 (else QG_ERR_SHAPE).  Each weight byte is read from device

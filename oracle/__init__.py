@@ -7,7 +7,7 @@ two share no code: this side decodes the canonical codec bytes itself
 
 Functions follow the plain definitions stated in ``qgemm_oracle.c``:
 exact fp64 decode of Q4_0 / MLX4-G64 / Q2_0 / Q8_0 weights, ``ref = X * W^T`` with
-``k`` ascending into one fp64 accumulator, and ``SiLU(g) * u`` in fp64.
+``k`` ascending into one fp64 accumulator, ``SiLU(g) * u`` and ``GELU(g) * u`` (tanh form) in fp64.
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 library routines (numpy's correctly rounded float16 conversion, BLAS fp64
 matmul), exact rational brute force and the codec facts printed on the pages.
@@ -61,6 +61,7 @@ def lib():
         L.orc_dequant_f16_rows.restype = i32
         L.orc_matmul_xwt.argtypes = [p, i64, p, i64, i64, i64, p, i32]
         L.orc_swiglu.argtypes = [p, p, p, i64]
+        L.orc_geglu.argtypes = [p, p, p, i64]
         L.orc_num_threads.restype = i32
         _lib = L
     return _lib
@@ -139,6 +140,14 @@ def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     return out
 
 
+def geglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    out = np.empty(g.shape, dtype=np.float64)
+    lib().orc_geglu(_ptr(g), _ptr(u), _ptr(out), g.size)
+    return out
+
+
 def num_threads() -> int:
     return int(lib().orc_num_threads())
 
@@ -172,3 +181,10 @@ def swiglu_ref(codec: int, canon_g: np.ndarray, canon_u: np.ndarray, n: int, k: 
     g = gemm_ref(codec, canon_g, n, k, x, rows_n, threads)
     u = gemm_ref(codec, canon_u, n, k, x, rows_n, threads)
     return swiglu(g, u)
+
+
+def geglu_ref(codec: int, canon_g: np.ndarray, canon_u: np.ndarray, n: int, k: int,
+              x: np.ndarray, rows_n=None, threads: int = 0) -> np.ndarray:
+    g = gemm_ref(codec, canon_g, n, k, x, rows_n, threads)
+    u = gemm_ref(codec, canon_u, n, k, x, rows_n, threads)
+    return geglu(g, u)

@@ -9,7 +9,9 @@
  *   1. decode every weight of the canonical codec bytes exactly in fp64;
  *   2. ref[m][n] = sum_k x[m][k] * w[n][k], k ascending, one fp64 accumulator
  *      (Y = X * W^T with fp16 activations X [M,K] and weights W [N,K]);
- *   3. for the fused gate/up projection: out = g / (1 + exp(-g)) * u, fp64.
+ *   3. for the fused gate/up projection: out = g / (1 + exp(-g)) * u, fp64
+ *      (SwiGLU), or out = 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))) * u
+ *      (GeGLU with the tanh form of GELU).
  *
  * Sources on the pages (m4-prefill-engine):
  *   - releases page, v0.3.0, "PrismML Q2_0 Ternary Codec": 128-weight block of
@@ -19,6 +21,8 @@
  *   - releases page, v0.3.0, "Quantization Registry Extension": Q8_0 is one of
  *     the registry's built-in formats (no layout given there).
  *   - comparison page, section 2.2: SwiGLU is SiLU(Gate) x Up on one input X.
+ *   - releases page, v0.3.0, TransformerBlock: SwiGLU / GeGLU activations, in
+ *     the same line as the Gemma 2 RMSNorm variant; GeGLU = GELU(Gate) x Up.
  *   - releases page, v0.2 "Honest Verification Labeling": the check is a CPU
  *     double-precision gold computation.
  * Q4_0 w = (q - 8) * d over 32-weight blocks and MLX w = q * s + b over
@@ -33,6 +37,7 @@
  *     2 * (i % 4); q = 3 is applied without clamping.
  *   - Q8_0: GGUF block_q8_0, 34 bytes per 32 weights: fp16 d, then weight j
  *     as the two's-complement byte 2 + j; w = q * d.
+ *   - GELU in GeGLU: the tanh form (the Gemma family's activation).
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fopenmp -fPIC -shared -lm
  * (no fast-math: every operation is a correctly rounded IEEE fp64 operation).
@@ -296,6 +301,16 @@ void orc_swiglu(const double *g, const double *u, double *out, int64_t count)
 {
     for (int64_t i = 0; i < count; ++i)
         out[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
+}
+
+/* out = GELU(g) * u with GELU(g) = 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))). */
+void orc_geglu(const double *g, const double *u, double *out, int64_t count)
+{
+    const double c = sqrt(2.0 / 3.14159265358979323846);
+    for (int64_t i = 0; i < count; ++i) {
+        const double x = g[i];
+        out[i] = 0.5 * x * (1.0 + tanh(c * (x + 0.044715 * x * x * x))) * u[i];
+    }
 }
 
 int orc_num_threads(void)

@@ -28,7 +28,7 @@ QG_OK = 0
 STATUS = {0: "QG_OK", -1: "QG_ERR_NULL", -2: "QG_ERR_CODEC", -3: "QG_ERR_SHAPE", -4: "QG_ERR_ALIGN",
           -5: "QG_ERR_MISMATCH", -6: "QG_ERR_LAUNCH", -7: "QG_ERR_SIZE"}
 
-EXPORTS = ("qgemm_prefill", "qgemm_swiglu", "qgemv_decode", "qg_packed_sizes", "qg_canonical_size",
+EXPORTS = ("qgemm_prefill", "qgemm_swiglu", "qgemm_geglu", "qgemv_decode", "qg_packed_sizes", "qg_canonical_size",
            "qg_pack_host", "qg_dequant", "qg_status_str", "qg_version")
 
 
@@ -58,6 +58,7 @@ def lib():
         W = ctypes.POINTER(qg_weight)
         L.qgemm_prefill.argtypes = [W, p, i64, i64, p, i64, p]
         L.qgemm_swiglu.argtypes = [W, W, p, i64, i64, p, i64, p]
+        L.qgemm_geglu.argtypes = [W, W, p, i64, i64, p, i64, p]
         L.qgemv_decode.argtypes = [W, p, i64, i64, p, i64, p]
         L.qg_packed_sizes.argtypes = [i32, i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
         L.qg_canonical_size.argtypes = [i32, i64, i64, ctypes.POINTER(sz)]
@@ -66,7 +67,7 @@ def lib():
         L.qg_status_str.argtypes = [ctypes.c_int]
         L.qg_status_str.restype = ctypes.c_char_p
         L.qg_version.restype = i32
-        for f in ("qgemm_prefill", "qgemm_swiglu", "qgemv_decode", "qg_packed_sizes", "qg_canonical_size",
+        for f in ("qgemm_prefill", "qgemm_swiglu", "qgemm_geglu", "qgemv_decode", "qg_packed_sizes", "qg_canonical_size",
                   "qg_pack_host", "qg_dequant"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -191,6 +192,16 @@ def qgemm_swiglu(wg: QWeight, wu: QWeight, x, out=None, stream=None):
     ybuf, ldy, y = _out(m, wg.n, x.device, out)
     _check(lib().qgemm_swiglu(wg.desc, wu.desc, x2.data_ptr(), m, ldx, ybuf.data_ptr(), ldy, _stream(stream)),
            "qgemm_swiglu")
+    return y.reshape(*lead, wg.n) if out is None else out
+
+
+def qgemm_geglu(wg: QWeight, wu: QWeight, x, out=None, stream=None):
+    """GELU(X Wg^T) * (X Wu^T) (tanh-form GELU) for fp16 X [..., K]; returns fp16 [..., N]."""
+    x2, lead, ldx = _as_rows(x, wg.k)
+    m = x2.shape[0]
+    ybuf, ldy, y = _out(m, wg.n, x.device, out)
+    _check(lib().qgemm_geglu(wg.desc, wu.desc, x2.data_ptr(), m, ldx, ybuf.data_ptr(), ldy, _stream(stream)),
+           "qgemm_geglu")
     return y.reshape(*lead, wg.n) if out is None else out
 
 

@@ -97,11 +97,12 @@ qg_status qgemm_prefill(const qg_weight *w, const void *x, int64_t m, int64_t ld
         return st;
     const GemmProblem p = problem(w, x, m, ldx, y, ldy);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return launched(m <= 4 ? launch_gemv(p, s) : launch_gemm(p, false, s));
+    return launched(m <= 4 ? launch_gemv(p, s) : launch_gemm(p, 0, s));
 }
 
-qg_status qgemm_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x, int64_t m, int64_t ldx, void *out,
-                       int64_t ldo, void *stream)
+// gate/up projection pair with a gated epilogue (glu 1 = SwiGLU, 2 = GeGLU)
+static qg_status gated(const qg_weight *wg, const qg_weight *wu, const void *x, int64_t m, int64_t ldx, void *out,
+                       int64_t ldo, void *stream, int glu)
 {
     qg_status st = check_gemm(wg, x, m, ldx, out, ldo);
     if (st != QG_OK)
@@ -112,7 +113,19 @@ qg_status qgemm_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x, 
         return QG_ERR_MISMATCH;
     GemmProblem p = problem(wg, x, m, ldx, out, ldo);
     p.w1 = planes_of(wu);
-    return launched(launch_gemm(p, true, static_cast<hipStream_t>(stream)));
+    return launched(launch_gemm(p, glu, static_cast<hipStream_t>(stream)));
+}
+
+qg_status qgemm_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x, int64_t m, int64_t ldx, void *out,
+                       int64_t ldo, void *stream)
+{
+    return gated(wg, wu, x, m, ldx, out, ldo, stream, 1);
+}
+
+qg_status qgemm_geglu(const qg_weight *wg, const qg_weight *wu, const void *x, int64_t m, int64_t ldx, void *out,
+                      int64_t ldo, void *stream)
+{
+    return gated(wg, wu, x, m, ldx, out, ldo, stream, 2);
 }
 
 qg_status qgemv_decode(const qg_weight *w, const void *x, int64_t m, int64_t ldx, void *y, int64_t ldy,

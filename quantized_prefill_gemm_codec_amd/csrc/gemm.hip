@@ -56,23 +56,36 @@ struct GemmArgs {
     int tiles_m, tiles_n;
 };
 
-__device__ __forceinline__ float silu_mul(float g, float u)
+__device__ __forceinline__ float sigmoid_mul(float g, float z, float u)
 {
-    // SiLU(g) * u = g / (1 + exp(-g)) * u with exp(-g) = 2^(-g log2 e)
-    const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+    // g * sigmoid(z) * u = g / (1 + exp(-z)) * u with exp(-z) = 2^(-z log2 e)
+    const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
     return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+// Gated epilogues on the (gate, up) accumulator pair, in fp32:
+//   GLU 1 (SwiGLU): SiLU(g) * u = g * sigmoid(g) * u
+//   GLU 2 (GeGLU):  GELU(g) * u with the tanh form of GELU, written as
+//                   g * sigmoid(2 sqrt(2/pi) (g + 0.044715 g^3)) * u
+//                   (0.5 (1 + tanh(t)) = sigmoid(2 t)).
+template <int GLU> __device__ __forceinline__ float glu_mul(float g, float u)
+{
+    if constexpr (GLU == 1)
+        return sigmoid_mul(g, g, u);
+    else
+        return sigmoid_mul(g, 1.5957691216057308f * __builtin_fmaf(0.044715f * g, g * g, g), u);
 }
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100, SG_DS_WR = 0x200;
 
-template <int CODEC, int BM, int BN, int WM, int WN, bool SWIGLU>
+template <int CODEC, int BM, int BN, int WM, int WN, int GLU>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
 {
     constexpr int NT = 64 * WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr int NMAT = SWIGLU ? 2 : 1;
+    constexpr int NMAT = GLU ? 2 : 1;
     constexpr int XCH = BM * 8 / NT;        // 16-byte X chunks per thread per k-step
     constexpr int STAGE = BM * 128;         // bytes of one X stage in LDS
     static_assert(FM >= 1 && FN >= 1 && XCH >= 1 && (BM * 8) % NT == 0 && (TM % 64 == 0 || FM == 1), "tile");
@@ -95,7 +108,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
 
     const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, a.x_bytes);
     const PlaneRsrc w0 = plane_rsrc(a.w0);
-    const PlaneRsrc w1 = plane_rsrc(SWIGLU ? a.w1 : a.w0);
+    const PlaneRsrc w1 = plane_rsrc(GLU ? a.w1 : a.w0);
 
     // X staging: thread chunk c covers tile row r = (tid + NT c) / 8 and the
     // 16-byte column ch = tid % 8; rows past M and the K tail get out-of-range
@@ -147,7 +160,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             dst[0][fn] = load_lane<CODEC>(w0, lo[fn], rg0 + fn, t, a.ksteps, a.kb128);
-            if constexpr (SWIGLU)
+            if constexpr (GLU != 0)
                 dst[NMAT - 1][fn] = load_lane<CODEC>(w1, lo[fn], rg0 + fn, t, a.ksteps, a.kb128);
         }
     };
@@ -251,8 +264,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if constexpr (SWIGLU)
-                        v[e] = silu_mul(acc[0][fm][fn][4 * q + e], acc[1][fm][fn][4 * q + e]);
+                    if constexpr (GLU != 0)
+                        v[e] = glu_mul<GLU>(acc[0][fm][fn][4 * q + e], acc[1][fm][fn][4 * q + e]);
                     else
                         v[e] = acc[0][fm][fn][4 * q + e];
                 }
@@ -309,14 +322,14 @@ __device__ __forceinline__ void grouped_tile(int bid, int tiles_m, int tiles_n, 
 // every stage, and the WK fp32 partial tiles are summed in LDS (fixed order)
 // in the epilogue.  Used for small M, where the tiles alone would leave most
 // SIMDs idle.  NSTAGE stages are in flight (loads run NSTAGE-1 steps ahead).
-template <int CODEC, int BM, int BN, int WM, int WN, int WK, bool SWIGLU, int NSTAGE>
+template <int CODEC, int BM, int BN, int WM, int WN, int WK, int GLU, int NSTAGE>
 __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs a)
 {
     constexpr int NWT = WM * WN;                           // waves per k-slice
     constexpr int NW = NWT * WK, NT = 64 * NW;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr int NMAT = SWIGLU ? 2 : 1;
+    constexpr int NMAT = GLU ? 2 : 1;
     constexpr int RG = BN / 32;                            // row groups per matrix per tile
     constexpr int CB = CODEC == Q2_0 ? 8 : CODEC == Q8_0 ? 32 : 16;   // code bytes per lane per chunk
     constexpr int WCH = 64 * CB;                           // bytes per (row group, k-step) chunk
@@ -336,7 +349,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     constexpr int VWAIT = (AHEAD - 1) * VMIN;               // DMA ops that may stay in flight
     static_assert(NX % NWT == 0 && W_BYTES % 1024 == 0 && SLICE % 256 == 0, "dma tiling");
     static_assert((FM == 1 || FM % 2 == 0) && VMIN >= 1 && NSTAGE >= 3 && VWAIT < 64, "tile");
-    static_assert(!(SWIGLU && WK > 1), "the split-K epilogue sums plain GEMM partials");
+    static_assert(!(GLU && WK > 1), "the split-K epilogue sums plain GEMM partials");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
     __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
@@ -361,8 +374,8 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
 
     const u32x4 xr = rsrc_words(a.x, a.x_bytes);
     const u32x4 q0 = rsrc_words(a.w0.qs, a.w0.qs_bytes), s0 = rsrc_words(a.w0.scales, a.w0.scale_bytes);
-    const u32x4 q1 = SWIGLU ? rsrc_words(a.w1.qs, a.w1.qs_bytes) : q0;
-    const u32x4 s1 = SWIGLU ? rsrc_words(a.w1.scales, a.w1.scale_bytes) : s0;
+    const u32x4 q1 = GLU ? rsrc_words(a.w1.qs, a.w1.qs_bytes) : q0;
+    const u32x4 s1 = GLU ? rsrc_words(a.w1.scales, a.w1.scale_bytes) : s0;
 
     // ---- per-lane DMA source offsets (fixed across k-steps) ----
     // X: instruction j fills LDS slots 64j..64j+63; slot p holds tile row
@@ -603,8 +616,8 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if constexpr (SWIGLU)
-                        v[e] = silu_mul(acc[0][fm][fn][4 * q + e], acc[1][fm][fn][4 * q + e]);
+                    if constexpr (GLU != 0)
+                        v[e] = glu_mul<GLU>(acc[0][fm][fn][4 * q + e], acc[1][fm][fn][4 * q + e]);
                     else
                         v[e] = acc[0][fm][fn][4 * q + e];
                 }
@@ -632,7 +645,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     }
 }
 
-template <int CODEC, int BM, int BN, int WM, int WN, int WK, bool SWIGLU, int NSTAGE>
+template <int CODEC, int BM, int BN, int WM, int WN, int WK, int GLU, int NSTAGE>
 hipError_t launch_dma(const GemmProblem &p, hipStream_t stream)
 {
     GemmArgs a;
@@ -654,11 +667,11 @@ hipError_t launch_dma(const GemmProblem &p, hipStream_t stream)
     void *args[] = {&a};
     const dim3 grid(unsigned(a.tiles_m * a.tiles_n)), block(64 * WM * WN * WK);
     return hipLaunchKernel(
-        reinterpret_cast<const void *>(&gemm_dma_kernel<CODEC, BM, BN, WM, WN, WK, SWIGLU, NSTAGE>), grid, block,
+        reinterpret_cast<const void *>(&gemm_dma_kernel<CODEC, BM, BN, WM, WN, WK, GLU, NSTAGE>), grid, block,
         args, 0, stream);
 }
 
-template <int CODEC, int BM, int BN, int WM, int WN, bool SWIGLU>
+template <int CODEC, int BM, int BN, int WM, int WN, int GLU>
 hipError_t launch_tile(const GemmProblem &p, hipStream_t stream)
 {
     GemmArgs a;
@@ -679,42 +692,51 @@ hipError_t launch_tile(const GemmProblem &p, hipStream_t stream)
     a.tiles_n = int(ceil_div(p.n, BN));
     void *args[] = {&a};
     const dim3 grid(unsigned(a.tiles_m * a.tiles_n)), block(64 * WM * WN);
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<CODEC, BM, BN, WM, WN, SWIGLU>), grid,
+    return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<CODEC, BM, BN, WM, WN, GLU>), grid,
                            block, args, 0, stream);
 }
 
 int64_t tiles(const GemmProblem &p, int bm, int bn) { return ceil_div(p.m, bm) * ceil_div(p.n, bn); }
 
-template <int CODEC>
-hipError_t launch_codec(const GemmProblem &p, bool swiglu, hipStream_t stream)
+// gate/up projections with a gated epilogue (GLU 1 = SwiGLU, 2 = GeGLU)
+template <int CODEC, int GLU>
+hipError_t launch_glu(const GemmProblem &p, hipStream_t stream)
 {
+    if (p.m > 128)
+        return launch_dma<CODEC, 256, 128, 2, 4, 1, GLU, 3>(p, stream);
+    return p.m > 64 ? launch_tile<CODEC, 128, 128, 2, 2, GLU>(p, stream)
+                    : launch_tile<CODEC, 64, 64, 2, 2, GLU>(p, stream);
+}
+
+template <int CODEC>
+hipError_t launch_codec(const GemmProblem &p, int glu, hipStream_t stream)
+{
+    if (glu == 1)
+        return launch_glu<CODEC, 1>(p, stream);
+    if (glu == 2)
+        return launch_glu<CODEC, 2>(p, stream);
     constexpr int64_t FILL = 256;   // compute units on MI355X
     if (p.m > 128) {
-        if (swiglu)
-            return launch_dma<CODEC, 256, 128, 2, 4, 1, true, 3>(p, stream);
         if (tiles(p, 256, 256) >= FILL)
-            return launch_dma<CODEC, 256, 256, 2, 4, 1, false, 3>(p, stream);
-        return launch_dma<CODEC, 256, 128, 2, 4, 1, false, 3>(p, stream);
+            return launch_dma<CODEC, 256, 256, 2, 4, 1, 0, 3>(p, stream);
+        return launch_dma<CODEC, 256, 128, 2, 4, 1, 0, 3>(p, stream);
     }
     // small M: 64 x 64 tiles with the k-steps split four ways inside the
     // workgroup (eight waves), so that N / 64 tiles keep the SIMDs busy
-    if (!swiglu && p.m <= 64)
-        return launch_dma<CODEC, 64, 64, 1, 2, 4, false, 3>(p, stream);
-    if (swiglu)
-        return p.m > 64 ? launch_tile<CODEC, 128, 128, 2, 2, true>(p, stream)
-                        : launch_tile<CODEC, 64, 64, 2, 2, true>(p, stream);
-    return launch_tile<CODEC, 128, 128, 2, 2, false>(p, stream);
+    if (p.m <= 64)
+        return launch_dma<CODEC, 64, 64, 1, 2, 4, 0, 3>(p, stream);
+    return launch_tile<CODEC, 128, 128, 2, 2, 0>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmProblem &p, bool swiglu, hipStream_t stream)
+hipError_t launch_gemm(const GemmProblem &p, int glu, hipStream_t stream)
 {
     switch (p.codec) {
-    case Q4_0: return launch_codec<Q4_0>(p, swiglu, stream);
-    case MLX4_G64: return launch_codec<MLX4_G64>(p, swiglu, stream);
-    case Q2_0: return launch_codec<Q2_0>(p, swiglu, stream);
-    case Q8_0: return launch_codec<Q8_0>(p, swiglu, stream);
+    case Q4_0: return launch_codec<Q4_0>(p, glu, stream);
+    case MLX4_G64: return launch_codec<MLX4_G64>(p, glu, stream);
+    case Q2_0: return launch_codec<Q2_0>(p, glu, stream);
+    case Q8_0: return launch_codec<Q8_0>(p, glu, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -343,7 +343,7 @@ hipError_t launch_gemv(const GemmProblem &p, hipStream_t stream)
     // beyond 4 rows, or an X too large to stage, the tiled MFMA kernel serves small M
     const int64_t mm = p.m == 1 ? 1 : p.m == 2 ? 2 : 4;
     if (p.m > 4 || mm * p.ksteps * 128 > GEMV_X_LDS_MAX || gemv_lds(p.codec, mm, p.ksteps).bytes > 64 * 1024)
-        return launch_gemm(p, false, stream);
+        return launch_gemm(p, 0, stream);
     switch (p.codec) {
     case Q4_0: return launch_gemv_codec<Q4_0>(p, stream);
     case MLX4_G64: return launch_gemv_codec<MLX4_G64>(p, stream);

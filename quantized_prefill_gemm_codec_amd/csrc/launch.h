@@ -17,7 +17,7 @@ struct GemmProblem {
 };
 
 // Tiled MFMA kernels.  Return a hipError_t of the launch.
-hipError_t launch_gemm(const GemmProblem &p, bool swiglu, hipStream_t stream);
+hipError_t launch_gemm(const GemmProblem &p, int glu, hipStream_t stream);   // glu: 0 none, 1 SwiGLU, 2 GeGLU
 // Weight-streaming small-M kernels (1 <= m <= 64).
 hipError_t launch_gemv(const GemmProblem &p, hipStream_t stream);
 // fp16 image of the weights, [n, ldw].

@@ -174,11 +174,14 @@ def gen_weight(codec: int, n: int, k: int, seed: int, tensor_id: int = T_W) -> n
     return GEN[codec](n, k, seed, tensor_id)
 
 
+GATED = ("swiglu", "geglu")     # gate/up pairs with a gated epilogue
+
+
 @dataclasses.dataclass(frozen=True)
 class Workload:
     """One of the five workloads: shapes, codec and which entry point runs it."""
     name: str
-    op: str          # "prefill" | "swiglu" | "gemv"
+    op: str          # "prefill" | "swiglu" | "geglu" | "gemv"
     codec: int
     m: int
     k: int
@@ -189,17 +192,17 @@ class Workload:
         return gen_x(self.m, self.k, self.seed)
 
     def weights(self):
-        if self.op == "swiglu":
+        if self.op in GATED:
             return (gen_weight(self.codec, self.n, self.k, self.seed, T_WG),
                     gen_weight(self.codec, self.n, self.k, self.seed, T_WU))
         return (gen_weight(self.codec, self.n, self.k, self.seed, T_W),)
 
     def flops(self) -> int:
-        mats = 2 if self.op == "swiglu" else 1
+        mats = 2 if self.op in GATED else 1
         return 2 * self.m * self.n * self.k * mats
 
     def algorithmic_bytes(self) -> int:
-        mats = 2 if self.op == "swiglu" else 1
+        mats = 2 if self.op in GATED else 1
         return mats * canonical_bytes(self.codec, self.n, self.k) + 2 * self.m * self.k + 2 * self.m * self.n
 
 
@@ -212,4 +215,6 @@ WORKLOADS = {
     "q4_0_gemv_64x4096x14336": Workload("q4_0_gemv_64x4096x14336", "gemv", CODEC_Q4_0, 64, 4096, 14336, BASE_SEED + 5),
     # next-step codec on the 1B-shape up-projection
     "q8_0_prefill_2048x2048x8192": Workload("q8_0_prefill_2048x2048x8192", "prefill", CODEC_Q8_0, 2048, 2048, 8192, BASE_SEED + 6),
+    # next-step epilogue: the 8B-shape gate/up pair with GeGLU instead of SwiGLU
+    "mlx4_geglu_2048x4096x14336": Workload("mlx4_geglu_2048x4096x14336", "geglu", CODEC_MLX4_G64, 2048, 4096, 14336, BASE_SEED + 7),
 }

@@ -207,6 +207,37 @@ def test_swiglu_one_hot_probe(torch):
     assert np.all(np.abs(y.astype(np.float64) - ref) <= 2.0 ** -10 * np.abs(ref) + 2.0 ** -24)
 
 
+# -------------------------------------------------------------------- GeGLU --
+
+GEGLU_SHAPES = [(2, 300, 264, 256), (2, 70, 136, 128), (1, 33, 200, 192), (4, 200, 128, 256), (3, 129, 256, 256)]
+
+
+@pytest.mark.parametrize("codec,m,n,k", GEGLU_SHAPES)
+def test_geglu_parity(torch, codec, m, n, k):
+    seed = 4500 + m + n
+    cg = synth.gen_weight(codec, n, k, seed, synth.T_WG)
+    cu = synth.gen_weight(codec, n, k, seed, synth.T_WU)
+    x = synth.gen_x(m, k, seed)
+    y = qg.qgemm_geglu(_weight(torch, codec, n, k, cg), _weight(torch, codec, n, k, cu), _dev(torch, x)).cpu().numpy()
+    ref = oracle.geglu_ref(codec, cg, cu, n, k, x)
+    assert _err_beyond_fp16_rounding(y, ref) <= TOL
+
+
+def test_geglu_one_hot_probe(torch):
+    """One-hot X rows and an up matrix of exact ones: out = GELU(wg[n, k_m])."""
+    m, n, k = 64, 256, 128
+    cg = synth.gen_weight(2, n, k, 12, synth.T_WG)
+    ones = synth.encode_mlx4(np.zeros((n, k), np.uint8), np.full((n, 2), 0.25, np.float16),
+                             np.ones((n, 2), np.float16))
+    km = np.arange(m) * 2 % k
+    x = np.zeros((m, k), np.float16)
+    x[np.arange(m), km] = 1
+    y = qg.qgemm_geglu(_weight(torch, 2, n, k, cg), _weight(torch, 2, n, k, ones), _dev(torch, x)).cpu().numpy()
+    g = oracle.dequant_f16_bits(2, cg, n, k).view(np.float16).astype(np.float64)[:, km].T
+    ref = oracle.geglu(g, np.ones_like(g))
+    assert np.all(np.abs(y.astype(np.float64) - ref) <= 2.0 ** -10 * np.abs(ref) + 2.0 ** -24)
+
+
 # ---------------------------------------------------------------------- GEMV --
 
 GEMV_SHAPES = [(1, 1, 1000, 512), (1, 2, 256, 96), (1, 3, 520, 256), (1, 4, 200, 1024), (1, 5, 256, 256),
@@ -255,6 +286,8 @@ def test_full_workload_sampled(torch, name):
     xd = _dev(torch, x)
     if wl.op == "swiglu":
         y = qg.qgemm_swiglu(ws[0], ws[1], xd)
+    elif wl.op == "geglu":
+        y = qg.qgemm_geglu(ws[0], ws[1], xd)
     elif wl.op == "gemv":
         y = qg.qgemv_decode(ws[0], xd)
     else:
@@ -265,8 +298,9 @@ def test_full_workload_sampled(torch, name):
     rows_m = _sample(rng, wl.m, 12)
     rows_n = _sample(rng, wl.n, 384)
     ys = y.cpu().numpy()[np.ix_(rows_m, rows_n)]
-    if wl.op == "swiglu":
-        ref = oracle.swiglu_ref(wl.codec, mats[0], mats[1], wl.n, wl.k, x[rows_m], rows_n=rows_n)
+    if wl.op in synth.GATED:
+        fn = oracle.swiglu_ref if wl.op == "swiglu" else oracle.geglu_ref
+        ref = fn(wl.codec, mats[0], mats[1], wl.n, wl.k, x[rows_m], rows_n=rows_n)
         assert _err_beyond_fp16_rounding(ys, ref) <= TOL
     else:
         ref = oracle.gemm_ref(wl.codec, mats[0], wl.n, wl.k, x[rows_m], rows_n=rows_n)

@@ -32,7 +32,7 @@ def _header_functions():
 def test_library_exports_every_declared_symbol():
     L = qg.lib()
     names = _header_functions()
-    assert set(names) >= {"qgemm_prefill", "qgemm_swiglu", "qgemv_decode", "qg_pack_host", "qg_dequant"}
+    assert set(names) >= {"qgemm_prefill", "qgemm_swiglu", "qgemm_geglu", "qgemv_decode", "qg_pack_host", "qg_dequant"}
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(qg.EXPORTS)
@@ -190,6 +190,7 @@ def test_gemm_argument_errors(args, status):
     assert L.qgemm_prefill(ctypes.byref(w), x, m, ldx, y, ldy, None) == status
     assert L.qgemv_decode(ctypes.byref(w), x, m, ldx, y, ldy, None) == status
     assert L.qgemm_swiglu(ctypes.byref(w), ctypes.byref(w), x, m, ldx, y, ldy, None) == status
+    assert L.qgemm_geglu(ctypes.byref(w), ctypes.byref(w), x, m, ldx, y, ldy, None) == status
 
 
 def test_gemv_rejects_large_m_and_swiglu_mismatch():
@@ -200,6 +201,7 @@ def test_gemv_rejects_large_m_and_swiglu_mismatch():
     for wg, wu in pairs:
         assert (wg.codec, wg.n, wg.k) != (wu.codec, wu.n, wu.k)
         assert L.qgemm_swiglu(ctypes.byref(wg), ctypes.byref(wu), FAKE, 4, wg.k, FAKE, 128, None) == -5
+        assert L.qgemm_geglu(ctypes.byref(wg), ctypes.byref(wu), FAKE, 4, wg.k, FAKE, 128, None) == -5
     assert L.qg_dequant(ctypes.byref(_w()), FAKE, 60, None) == -3
     assert L.qg_dequant(ctypes.byref(_w(codec=0)), FAKE, 64, None) == -2
 

@@ -110,3 +110,26 @@ def test_swiglu_identities():
     odd = oracle.swiglu(g, ones) - oracle.swiglu(-g, ones)
     assert np.allclose(odd, g, rtol=1e-13, atol=1e-13)
     assert np.all(np.isfinite(got))
+
+
+def test_geglu_identities():
+    """GELU in GeGLU is the tanh form.  Pins: GELU(0) = 0; the odd part of the
+    tanh form is exactly the identity (0.5 g (1 + tanh t) + 0.5 g (1 - tanh t));
+    GELU(g) -> g and -> 0 far out; and it stays within 1e-3 of the exact
+    erf-based GELU everywhere (a dropped cubic term, a wrong sqrt(2/pi) or a
+    sign slip all break that by an order of magnitude)."""
+    from scipy.special import erf
+    rng = np.random.default_rng(6)
+    g = np.concatenate([rng.normal(0, 3, 20000), np.linspace(-8, 8, 4001), [0.0, -0.0, 30.0, -30.0]])
+    ones = np.ones_like(g)
+    got = oracle.geglu(g, ones)
+    assert oracle.geglu(np.array([0.0]), np.array([5.0]))[0] == 0.0
+    odd = got - oracle.geglu(-g, ones)
+    assert np.allclose(odd, g, rtol=1e-13, atol=1e-13)
+    exact = 0.5 * g * (1.0 + erf(g / np.sqrt(2.0)))
+    assert np.max(np.abs(got - exact)) < 1e-3
+    far = oracle.geglu(np.array([20.0, -20.0]), np.ones(2))
+    assert abs(far[0] - 20.0) < 1e-12 and abs(far[1]) < 1e-12
+    u = rng.normal(0, 2, g.size)
+    assert np.allclose(oracle.geglu(g, u), got * u, rtol=1e-15, atol=0)
+
