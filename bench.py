@@ -42,7 +42,7 @@ MALL_BYTES = 256 << 20
 HEADLINE = "q4_0_prefill_2048x2048x8192"
 SECONDARY = ["mlx4_swiglu_2048x4096x14336", "q2_0_prefill_2048x4096x4096",
              "q4_0_gemv_1x4096x14336", "q4_0_gemv_64x4096x14336", "q8_0_prefill_2048x2048x8192",
-             "mlx4_geglu_2048x4096x14336"]
+             "mlx4_geglu_2048x4096x14336", "q4_0_qproj_heads_2048x4096x4096"]
 KERNEL_SOURCES = ["gemm.hip", "gemv.hip", "unpack.h", "planar.h", "lds_dma.h"]
 
 
@@ -90,6 +90,9 @@ class Prepared:
                 fn = L.qgemm_swiglu if wl.op == "swiglu" else L.qgemm_geglu
                 self.calls.append((fn, (ws[0].desc, ws[1].desc, xd.data_ptr(), wl.m, wl.k,
                                                     y.data_ptr(), ldy, stream)))
+            elif wl.op == "heads":
+                self.calls.append((L.qgemm_prefill_heads, (ws[0].desc, xd.data_ptr(), wl.m, wl.k, y.data_ptr(),
+                                                           wl.head_dim, stream)))
             elif wl.op == "gemv":
                 self.calls.append((L.qgemv_decode, (ws[0].desc, xd.data_ptr(), wl.m, wl.k, y.data_ptr(), ldy, stream)))
             else:

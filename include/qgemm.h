@@ -102,6 +102,17 @@ typedef struct {
 qg_status qgemm_prefill(const qg_weight *w, const void *x, int64_t m, int64_t ldx,
                         void *y, int64_t ldy, void *stream);
 
+/* The same projection written in the direct-head layout [H, M, D]: output
+ * element (m, h D + d) goes to y[(h M + m) D + d], so per-head Q, K or V
+ * tiles come out ready for attention with no transposition pass (comparison
+ * page, section 4, and releases page, v0.2.1: "Direct-Head Multi-Head
+ * Layout").
+ *  head_dim  D: a multiple of 8 that divides N (else QG_ERR_SHAPE)
+ *  y         device fp16, M * N contiguous elements, 16-byte aligned
+ * Other arguments and errors as for qgemm_prefill. */
+qg_status qgemm_prefill_heads(const qg_weight *w, const void *x, int64_t m, int64_t ldx,
+                              void *y, int64_t head_dim, void *stream);
+
 /* Fused gate/up projection with the SwiGLU epilogue (comparison page, section
  * 2.2): out[m, n] = SiLU(g) * u with g = (X Wg^T)[m, n], u = (X Wu^T)[m, n],
  * SiLU(g) = g / (1 + exp(-g)), evaluated in fp32 on the accumulators and

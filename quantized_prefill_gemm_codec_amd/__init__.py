@@ -28,7 +28,7 @@ QG_OK = 0
 STATUS = {0: "QG_OK", -1: "QG_ERR_NULL", -2: "QG_ERR_CODEC", -3: "QG_ERR_SHAPE", -4: "QG_ERR_ALIGN",
           -5: "QG_ERR_MISMATCH", -6: "QG_ERR_LAUNCH", -7: "QG_ERR_SIZE"}
 
-EXPORTS = ("qgemm_prefill", "qgemm_swiglu", "qgemm_geglu", "qgemv_decode", "qg_packed_sizes", "qg_canonical_size",
+EXPORTS = ("qgemm_prefill", "qgemm_prefill_heads", "qgemm_swiglu", "qgemm_geglu", "qgemv_decode", "qg_packed_sizes", "qg_canonical_size",
            "qg_pack_host", "qg_dequant", "qg_status_str", "qg_version")
 
 
@@ -58,6 +58,7 @@ def lib():
         W = ctypes.POINTER(qg_weight)
         L.qgemm_prefill.argtypes = [W, p, i64, i64, p, i64, p]
         L.qgemm_swiglu.argtypes = [W, W, p, i64, i64, p, i64, p]
+        L.qgemm_prefill_heads.argtypes = [W, p, i64, i64, p, i64, p]
         L.qgemm_geglu.argtypes = [W, W, p, i64, i64, p, i64, p]
         L.qgemv_decode.argtypes = [W, p, i64, i64, p, i64, p]
         L.qg_packed_sizes.argtypes = [i32, i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
@@ -67,7 +68,7 @@ def lib():
         L.qg_status_str.argtypes = [ctypes.c_int]
         L.qg_status_str.restype = ctypes.c_char_p
         L.qg_version.restype = i32
-        for f in ("qgemm_prefill", "qgemm_swiglu", "qgemm_geglu", "qgemv_decode", "qg_packed_sizes", "qg_canonical_size",
+        for f in ("qgemm_prefill", "qgemm_prefill_heads", "qgemm_swiglu", "qgemm_geglu", "qgemv_decode", "qg_packed_sizes", "qg_canonical_size",
                   "qg_pack_host", "qg_dequant"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -193,6 +194,22 @@ def qgemm_swiglu(wg: QWeight, wu: QWeight, x, out=None, stream=None):
     _check(lib().qgemm_swiglu(wg.desc, wu.desc, x2.data_ptr(), m, ldx, ybuf.data_ptr(), ldy, _stream(stream)),
            "qgemm_swiglu")
     return y.reshape(*lead, wg.n) if out is None else out
+
+
+def qgemm_prefill_heads(w: QWeight, x, head_dim: int, out=None, stream=None):
+    """Y = X W^T for fp16 X [M, K] written head-major: returns fp16 [N / head_dim, M, head_dim]."""
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("qgemm_prefill_heads takes a 2-D X [M, K]")
+    x2, _, ldx = _as_rows(x, w.k)
+    m = x2.shape[0]
+    if out is None:
+        out = torch.empty((w.n // head_dim if head_dim else 0, m, head_dim), dtype=torch.float16, device=x.device)
+    if out.dtype != torch.float16 or not out.is_contiguous() or out.numel() != m * w.n:
+        raise ValueError("out must be a contiguous fp16 tensor of M * N elements")
+    _check(lib().qgemm_prefill_heads(w.desc, x2.data_ptr(), m, ldx, out.data_ptr(), head_dim, _stream(stream)),
+           "qgemm_prefill_heads")
+    return out
 
 
 def qgemm_geglu(wg: QWeight, wu: QWeight, x, out=None, stream=None):

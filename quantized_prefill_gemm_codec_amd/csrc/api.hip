@@ -100,6 +100,23 @@ qg_status qgemm_prefill(const qg_weight *w, const void *x, int64_t m, int64_t ld
     return launched(m <= 4 ? launch_gemv(p, s) : launch_gemm(p, 0, s));
 }
 
+qg_status qgemm_prefill_heads(const qg_weight *w, const void *x, int64_t m, int64_t ldx, void *y, int64_t head_dim,
+                              void *stream)
+{
+    qg_status st = check_weight(w);
+    if (st != QG_OK)
+        return st;
+    if (head_dim < 8 || head_dim % 8 != 0 || w->n % head_dim != 0)
+        return QG_ERR_SHAPE;
+    // y holds M x N elements: validated as a dense [M, N] buffer
+    if ((st = check_gemm(w, x, m, ldx, y, w->n)) != QG_OK)
+        return st;
+    GemmProblem p = problem(w, x, m, ldx, y, w->n);
+    p.head_dim = head_dim;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return launched(m <= 4 ? launch_gemv(p, s) : launch_gemm(p, 0, s));
+}
+
 // gate/up projection pair with a gated epilogue (glu 1 = SwiGLU, 2 = GeGLU)
 static qg_status gated(const qg_weight *wg, const qg_weight *wu, const void *x, int64_t m, int64_t ldx, void *out,
                        int64_t ldo, void *stream, int glu)

@@ -54,6 +54,7 @@ struct GemmArgs {
     int m, n, k, ldx, ldy;
     int groups, ksteps, kb128;
     int tiles_m, tiles_n;
+    int head_dim;            // 0: row-major Y; > 0: direct-head [N / head_dim, M, head_dim]
 };
 
 __device__ __forceinline__ float sigmoid_mul(float g, float z, float u)
@@ -255,7 +256,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
         const int m = m0 + wm * TM + fm * 32 + i;
         if (m >= a.m)
             continue;
-        _Float16 *yrow = a.y + int64_t(m) * a.ldy;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
@@ -269,15 +269,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
                     else
                         v[e] = acc[0][fm][fn][4 * q + e];
                 }
+                _Float16 *dst = out_at(a.y, a.ldy, a.head_dim, a.m, m, n);
                 if (n + 3 < a.n) {
                     f16x2 lo2 = {_Float16(v[0]), _Float16(v[1])};
                     f16x2 hi2 = {_Float16(v[2]), _Float16(v[3])};
-                    *reinterpret_cast<u32x2 *>(yrow + n) = u32x2{as_u32(lo2), as_u32(hi2)};
+                    *reinterpret_cast<u32x2 *>(dst) = u32x2{as_u32(lo2), as_u32(hi2)};
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         if (n + e < a.n)
-                            yrow[n + e] = _Float16(v[e]);
+                            dst[e] = _Float16(v[e]);
                 }
             }
         }
@@ -594,7 +595,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
             }
             const f16x8 h = {_Float16(lo[0]), _Float16(lo[1]), _Float16(lo[2]), _Float16(lo[3]),
                              _Float16(hi[0]), _Float16(hi[1]), _Float16(hi[2]), _Float16(hi[3])};
-            _Float16 *dst = a.y + int64_t(m) * a.ldy + n;
+            _Float16 *dst = out_at(a.y, a.ldy, a.head_dim, a.m, m, n);
             if (n + 7 < a.n) {
                 *reinterpret_cast<f16x8 *>(dst) = h;
             } else {
@@ -634,7 +635,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
         if (m >= a.m || n >= a.n)
             continue;
         const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + ml * (BN * 2) + ((c ^ (ml & 15)) * 16));
-        _Float16 *dst = a.y + int64_t(m) * a.ldy + n;
+        _Float16 *dst = out_at(a.y, a.ldy, a.head_dim, a.m, m, n);
         if (n + 7 < a.n) {
             *reinterpret_cast<u32x4 *>(dst) = v;
         } else {
@@ -664,6 +665,7 @@ hipError_t launch_dma(const GemmProblem &p, hipStream_t stream)
     a.kb128 = int(p.kb128);
     a.tiles_m = int(ceil_div(p.m, BM));
     a.tiles_n = int(ceil_div(p.n, BN));
+    a.head_dim = int(p.head_dim);
     void *args[] = {&a};
     const dim3 grid(unsigned(a.tiles_m * a.tiles_n)), block(64 * WM * WN * WK);
     return hipLaunchKernel(
@@ -690,6 +692,7 @@ hipError_t launch_tile(const GemmProblem &p, hipStream_t stream)
     a.kb128 = int(p.kb128);
     a.tiles_m = int(ceil_div(p.m, BM));
     a.tiles_n = int(ceil_div(p.n, BN));
+    a.head_dim = int(p.head_dim);
     void *args[] = {&a};
     const dim3 grid(unsigned(a.tiles_m * a.tiles_n)), block(64 * WM * WN);
     return hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<CODEC, BM, BN, WM, WN, GLU>), grid,

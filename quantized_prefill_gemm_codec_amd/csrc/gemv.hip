@@ -37,6 +37,7 @@ struct GemvArgs {
     uint32_t x_bytes;
     int m, n, k, ldx, ldy;
     int groups, ksteps, kb128;
+    int head_dim;            // 0: row-major Y; > 0: direct-head layout
     int per;                 // k-steps per wave
     int x_lds;               // bytes of the X region
 };
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
 #pragma unroll
                     for (int w = 1; w < GEMV_NW; ++w)
                         v += red[(w * MM + mr) * 32 + i];
-                    a.y[int64_t(mr) * a.ldy + n] = _Float16(v);
+                    *out_at(a.y, a.ldy, a.head_dim, a.m, mr, n) = _Float16(v);
                 }
             }
         }
@@ -315,6 +316,7 @@ hipError_t launch_gemv_mm(const GemmProblem &p, hipStream_t stream)
     a.k = int(p.k);
     a.ldx = int(p.ldx);
     a.ldy = int(p.ldy);
+    a.head_dim = int(p.head_dim);
     a.groups = int(p.groups);
     a.ksteps = int(p.ksteps);
     a.kb128 = int(p.kb128);

@@ -14,7 +14,20 @@ struct GemmProblem {
     _Float16 *y;
     int64_t m, n, k, ldx, ldy;
     int64_t groups, ksteps, kb128;
+    int64_t head_dim = 0;      // > 0: Y is written head-major [N / head_dim, M, head_dim]
 };
+
+// Address of output element (m, n): row-major [M, ldy], or, with head_dim = D
+// > 0, the direct-head layout [N / D, M, D] (element (m, h D + d) at
+// (h M + m) D + d).  Callers pass n at a multiple of the store width, which
+// divides D, so a store never crosses heads.
+__device__ __forceinline__ _Float16 *out_at(_Float16 *y, int ldy, int head_dim, int rows, int m, int n)
+{
+    if (head_dim == 0)
+        return y + int64_t(m) * ldy + n;
+    const int h = n / head_dim;
+    return y + (int64_t(h) * rows + m) * head_dim + (n - h * head_dim);
+}
 
 // Tiled MFMA kernels.  Return a hipError_t of the launch.
 hipError_t launch_gemm(const GemmProblem &p, int glu, hipStream_t stream);   // glu: 0 none, 1 SwiGLU, 2 GeGLU

@@ -181,12 +181,13 @@ GATED = ("swiglu", "geglu")     # gate/up pairs with a gated epilogue
 class Workload:
     """One of the five workloads: shapes, codec and which entry point runs it."""
     name: str
-    op: str          # "prefill" | "swiglu" | "geglu" | "gemv"
+    op: str          # "prefill" | "heads" | "swiglu" | "geglu" | "gemv"
     codec: int
     m: int
     k: int
     n: int
     seed: int
+    head_dim: int = 0   # "heads": Y written as [N / head_dim, M, head_dim]
 
     def x(self) -> np.ndarray:
         return gen_x(self.m, self.k, self.seed)
@@ -215,6 +216,9 @@ WORKLOADS = {
     "q4_0_gemv_64x4096x14336": Workload("q4_0_gemv_64x4096x14336", "gemv", CODEC_Q4_0, 64, 4096, 14336, BASE_SEED + 5),
     # next-step codec on the 1B-shape up-projection
     "q8_0_prefill_2048x2048x8192": Workload("q8_0_prefill_2048x2048x8192", "prefill", CODEC_Q8_0, 2048, 2048, 8192, BASE_SEED + 6),
+    # next-step layout: 8B-shape Q projection written per head ([32, 2048, 128])
+    "q4_0_qproj_heads_2048x4096x4096": Workload("q4_0_qproj_heads_2048x4096x4096", "heads", CODEC_Q4_0, 2048, 4096, 4096,
+                                                BASE_SEED + 8, head_dim=128),
     # next-step epilogue: the 8B-shape gate/up pair with GeGLU instead of SwiGLU
     "mlx4_geglu_2048x4096x14336": Workload("mlx4_geglu_2048x4096x14336", "geglu", CODEC_MLX4_G64, 2048, 4096, 14336, BASE_SEED + 7),
 }

@@ -175,6 +175,27 @@ def test_prefill_row_permutation_and_determinism(torch):
     assert np.array_equal(yp.view(np.uint16), y[perm].view(np.uint16))
 
 
+HEADS_SHAPES = [(1, 2, 256, 128, 64), (2, 37, 192, 256, 64), (1, 300, 512, 256, 128), (3, 64, 384, 256, 96),
+                (4, 129, 256, 160, 32), (1, 2048, 8192, 128, 128)]
+
+
+@pytest.mark.parametrize("codec,m,n,k,d", HEADS_SHAPES)
+def test_prefill_heads_layout(torch, codec, m, n, k, d):
+    """[H, M, D] output is the row-major output with n = h D + d moved, bit for bit."""
+    seed = 3500 + m + n + k
+    canon = synth.gen_weight(codec, n, k, seed)
+    x = synth.gen_x(m, k, seed)
+    w = _weight(torch, codec, n, k, canon)
+    xd = _dev(torch, x)
+    yh = qg.qgemm_prefill_heads(w, xd, d).cpu().numpy()
+    y = qg.qgemm_prefill(w, xd).cpu().numpy()
+    assert yh.shape == (n // d, m, d)
+    assert np.array_equal(yh.view(np.uint16), y.reshape(m, n // d, d).transpose(1, 0, 2).view(np.uint16))
+    if m <= 300:
+        ref = oracle.gemm_ref(codec, canon, n, k, x)
+        assert _err(yh.transpose(1, 0, 2).reshape(m, n), ref) <= TOL
+
+
 # -------------------------------------------------------------------- SwiGLU --
 
 SWIGLU_SHAPES = [(2, 33, 200, 192), (2, 130, 256, 128), (2, 300, 264, 256), (1, 70, 136, 96), (3, 200, 128, 256),
@@ -288,6 +309,8 @@ def test_full_workload_sampled(torch, name):
         y = qg.qgemm_swiglu(ws[0], ws[1], xd)
     elif wl.op == "geglu":
         y = qg.qgemm_geglu(ws[0], ws[1], xd)
+    elif wl.op == "heads":
+        y = qg.qgemm_prefill_heads(ws[0], xd, wl.head_dim).permute(1, 0, 2).reshape(wl.m, wl.n)
     elif wl.op == "gemv":
         y = qg.qgemv_decode(ws[0], xd)
     else:

@@ -206,6 +206,16 @@ def test_gemv_rejects_large_m_and_swiglu_mismatch():
     assert L.qg_dequant(ctypes.byref(_w(codec=0)), FAKE, 64, None) == -2
 
 
+def test_prefill_heads_argument_errors():
+    L = qg.lib()
+    w = _w(n=128)
+    for head_dim in (0, 4, 12, 48, 256):        # not a multiple of 8, or not dividing N = 128
+        assert L.qgemm_prefill_heads(ctypes.byref(w), FAKE, 4, 64, FAKE, head_dim, None) == -3
+    assert L.qgemm_prefill_heads(ctypes.byref(w), 0, 4, 64, FAKE, 64, None) == -1
+    assert L.qgemm_prefill_heads(ctypes.byref(_w(codec=9)), FAKE, 4, 64, FAKE, 64, None) == -2
+    assert L.qgemm_prefill_heads(ctypes.byref(w), FAKE + 8, 4, 64, FAKE, 64, None) == -4
+
+
 def test_status_strings():
     for st in qg.STATUS:
         assert qg.lib().qg_status_str(st)
