@@ -53,6 +53,9 @@ extern "C" {
  *  QG_CODEC_Q2_0     128-weight blocks of 34 bytes: fp16 d, then 32 bytes of
  *                    2-bit codes, weight i in byte i/4 at bit 2*(i%4);
  *                    w = (q - 1) * d, so q = 3 gives +2d.
+ *  QG_CODEC_MLX4_G32 as QG_CODEC_MLX4_G64 with one fp16 scale and bias per 32
+ *                    weights ([N, K/32] each): the group of the pages'
+ *                    20-byte block_mlx_4bit (comparison page, section 4).
  *  QG_CODEC_Q8_0     32-weight blocks of 34 bytes: fp16 d, then weight j as
  *                    the two's-complement byte 2 + j; w = q * d.  (Q8_0 is in
  *                    the quantization registry of the releases page, v0.3.0;
@@ -61,7 +64,8 @@ typedef enum {
     QG_CODEC_Q4_0 = 1,
     QG_CODEC_MLX4_G64 = 2,
     QG_CODEC_Q2_0 = 3,
-    QG_CODEC_Q8_0 = 4
+    QG_CODEC_Q8_0 = 4,
+    QG_CODEC_MLX4_G32 = 5
 } qg_codec;
 
 typedef enum {

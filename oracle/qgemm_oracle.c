@@ -32,7 +32,9 @@
  *   - Q4_0 byte order: GGUF convention, fp16 d first, then byte j holds weight
  *     j (low nibble) and weight j + 16 (high nibble).
  *   - MLX4 codes: little-endian uint32 words of 8 codes, element 0 in the low
- *     nibble; scales and biases are fp16; one group per 64 weights along K.
+ *     nibble; scales and biases are fp16; one group per 64 weights along K
+ *     (MLX4-G32: per 32 weights, the group of the pages' 20-byte
+ *     block_mlx_4bit, comparison page section 4).
  *   - Q2_0 code order: weight i sits in byte i / 4 of the code field at bit
  *     2 * (i % 4); q = 3 is applied without clamping.
  *   - Q8_0: GGUF block_q8_0, 34 bytes per 32 weights: fp16 d, then weight j
@@ -55,6 +57,7 @@
 #define ORC_MLX4_G64 2
 #define ORC_Q2_0 3
 #define ORC_Q8_0 4
+#define ORC_MLX4_G32 5
 
 /* ---------------------------------------------------------------- fp16 --- */
 
@@ -148,6 +151,7 @@ int orc_block_geometry(int codec, int64_t *weights, int64_t *bytes)
     case ORC_MLX4_G64: *weights = 64;  *bytes = 36; return 1;
     case ORC_Q2_0:     *weights = 128; *bytes = 34; return 1;
     case ORC_Q8_0:     *weights = 32;  *bytes = 34; return 1;
+    case ORC_MLX4_G32: *weights = 32;  *bytes = 20; return 1;
     default: return 0;
     }
 }
@@ -201,21 +205,22 @@ static void decode_q8_0_row(const uint8_t *row, int64_t k, double *w)
     }
 }
 
-/* MLX4-G64 row n: q = (word[n][k/8] >> 4*(k%8)) & 15, g = k / 64,
- * w = q * s[n][g] + b[n][g].  Exact in fp64: q*s has at most 15 significant
- * bits and the sum of two fp16-derived values spans far fewer than 53. */
+/* MLX4 row n with group size G (64 or 32): q = (word[n][k/8] >> 4*(k%8)) & 15,
+ * g = k / G, w = q * s[n][g] + b[n][g].  Exact in fp64: q*s has at most 15
+ * significant bits and the sum of two fp16-derived values spans far fewer
+ * than 53. */
 static void decode_mlx4_row(const uint8_t *codes, const uint8_t *scales,
                             const uint8_t *biases, int64_t n_idx, int64_t k,
-                            double *w)
+                            int64_t group, double *w)
 {
     const uint8_t *crow = codes + n_idx * (k / 2);
-    const uint8_t *srow = scales + n_idx * (k / 64) * 2;
-    const uint8_t *brow = biases + n_idx * (k / 64) * 2;
+    const uint8_t *srow = scales + n_idx * (k / group) * 2;
+    const uint8_t *brow = biases + n_idx * (k / group) * 2;
     for (int64_t kk = 0; kk < k; ++kk) {
         uint32_t word = rd_u32le(crow + (kk / 8) * 4);
         int q = (int)((word >> (4 * (kk % 8))) & 0xF);
-        double s = orc_f16_to_f64(rd_u16le(srow + (kk / 64) * 2));
-        double b = orc_f16_to_f64(rd_u16le(brow + (kk / 64) * 2));
+        double s = orc_f16_to_f64(rd_u16le(srow + (kk / group) * 2));
+        double b = orc_f16_to_f64(rd_u16le(brow + (kk / group) * 2));
         w[kk] = (double)q * s + b;
     }
 }
@@ -241,10 +246,11 @@ int orc_decode_rows(int codec, const uint8_t *canon, int64_t n, int64_t k,
         else if (codec == ORC_Q8_0)
             decode_q8_0_row(canon + nn * (k / 32) * 34, k, wr);
         else {
+            const int64_t group = codec == ORC_MLX4_G32 ? 32 : 64;
             const uint8_t *codes = canon;
             const uint8_t *scales = canon + n * (k / 2);
-            const uint8_t *biases = scales + n * (k / 64) * 2;
-            decode_mlx4_row(codes, scales, biases, nn, k, wr);
+            const uint8_t *biases = scales + n * (k / group) * 2;
+            decode_mlx4_row(codes, scales, biases, nn, k, group, wr);
         }
     }
     return 0;

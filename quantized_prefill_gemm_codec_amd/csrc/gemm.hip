@@ -334,7 +334,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     constexpr int RG = BN / 32;                            // row groups per matrix per tile
     constexpr int CB = CODEC == Q2_0 ? 8 : CODEC == Q8_0 ? 32 : 16;   // code bytes per lane per chunk
     constexpr int WCH = 64 * CB;                           // bytes per (row group, k-step) chunk
-    constexpr int SB = CODEC == Q2_0 ? 64 : 128;           // scale bytes per (row group, k-step)
+    constexpr int SB = CODEC == Q2_0 ? 64 : CODEC == MLX4_G32 ? 256 : 128;   // scale bytes per (row group, k-step)
     constexpr int X_OFF = 0, X_BYTES = BM * 128;
     constexpr int W_OFF = X_BYTES, W_BYTES = NMAT * RG * WCH;
     constexpr int S_OFF = W_OFF + W_BYTES, S_BYTES = NMAT * RG * SB;
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
         const int c = b / SB, o = b % SB;
         const int rg = c % RG;
         smat[u] = (256 * j / SB) / RG;              // wave-uniform: chunks never straddle matrices
-        const uint32_t pitch = CODEC == Q2_0 ? uint32_t(a.kb128) * 64u : uint32_t(a.ksteps) * 128u;
+        const uint32_t pitch = CODEC == Q2_0 ? uint32_t(a.kb128) * 64u : uint32_t(a.ksteps) * uint32_t(SB);
         sv[u] = (j < NSI && b < S_BYTES && rg0 + rg < a.groups) ? uint32_t(rg0 + rg) * pitch + uint32_t(o) : OOB;
     }
 
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
 #pragma unroll
         for (int u = 0; u < SPW; ++u) {
             const int j = wr + NWT * u;
-            const uint32_t so = CODEC == Q2_0 ? uint32_t(t >> 1) * 64u : uint32_t(t) * 128u;
+            const uint32_t so = CODEC == Q2_0 ? uint32_t(t >> 1) * 64u : uint32_t(t) * uint32_t(SB);
             if (j < NSI)
                 dma_b32(smat[u] ? s1 : s0, in ? sv[u] : OOB, so, base + S_OFF + uint32_t(j * 256));
         }
@@ -480,6 +480,8 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
                     cw[mt][fn].c = *reinterpret_cast<const u32x4 *>(wp);
                     if constexpr (CODEC == Q4_0)
                         cw[mt][fn].d = *reinterpret_cast<const _Float16 *>(sp + lane * 2);
+                    else if constexpr (CODEC == MLX4_G32)
+                        cw[mt][fn].sb = *reinterpret_cast<const uint32_t *>(sp + lane * 4);
                     else
                         cw[mt][fn].sb = *reinterpret_cast<const uint32_t *>(sp + i * 4);
                 }
@@ -738,6 +740,7 @@ hipError_t launch_gemm(const GemmProblem &p, int glu, hipStream_t stream)
     switch (p.codec) {
     case Q4_0: return launch_codec<Q4_0>(p, glu, stream);
     case MLX4_G64: return launch_codec<MLX4_G64>(p, glu, stream);
+    case MLX4_G32: return launch_codec<MLX4_G32>(p, glu, stream);
     case Q2_0: return launch_codec<Q2_0>(p, glu, stream);
     case Q8_0: return launch_codec<Q8_0>(p, glu, stream);
     }

@@ -42,7 +42,7 @@ struct GemvArgs {
     int x_lds;               // bytes of the X region
 };
 
-template <int CODEC> constexpr int corr_floats() { return CODEC == MLX4_G64 ? 2 : 1; }
+template <int CODEC> constexpr int corr_floats() { return CODEC == MLX4_G64 || CODEC == MLX4_G32 ? 2 : 1; }
 
 // x_s[p] = x_{2p} + x_{2p+1} summed over the 4 sub-step chunks of the slice.
 template <int CODEC>
@@ -60,7 +60,7 @@ __device__ __forceinline__ void slice_correction(const u32x4 *chunks, float *out
         out[0] = -1152.0f * ((sp[0] + sp[1]) + (sp[2] + sp[3]));
     } else if constexpr (CODEC == Q4_0) {
         out[0] = -1032.0f * (sp[0] + sp[2]) - 72.0f * (sp[1] + sp[3]);
-    } else if constexpr (CODEC == MLX4_G64) {
+    } else if constexpr (CODEC == MLX4_G64 || CODEC == MLX4_G32) {
         out[0] = -1024.0f * (sp[0] + sp[2]) - 64.0f * (sp[1] + sp[3]);
         out[1] = (sp[0] + sp[1]) + (sp[2] + sp[3]);
     } else {
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
                         dots[c][mr] = 0.0f;
                 slice_dots<CODEC, MM>(lc[u], xrow, magic, dots);
                 uint32_t sc;
-                if constexpr (CODEC == MLX4_G64)
+                if constexpr (CODEC == MLX4_G64 || CODEC == MLX4_G32)
                     sc = lc[u].sb;
                 else
                     sc = __builtin_bit_cast(unsigned short, lc[u].d);
@@ -298,7 +298,7 @@ inline GemvLds gemv_lds(int codec, int64_t mm, int64_t ksteps)
     l.per = int((ksteps + GEMV_NW - 1) / GEMV_NW);
     const int64_t x = mm * ksteps * 128;
     l.x_lds = int(x);
-    const int64_t nc = codec == MLX4_G64 ? 2 : 1;
+    const int64_t nc = is_mlx(codec) ? 2 : 1;
     l.bytes = size_t(l.x_lds + mm * ksteps * 2 * nc * 4 + GEMV_NW * mm * 32 * 4);
     return l;
 }
@@ -349,6 +349,7 @@ hipError_t launch_gemv(const GemmProblem &p, hipStream_t stream)
     switch (p.codec) {
     case Q4_0: return launch_gemv_codec<Q4_0>(p, stream);
     case MLX4_G64: return launch_gemv_codec<MLX4_G64>(p, stream);
+    case MLX4_G32: return launch_gemv_codec<MLX4_G32>(p, stream);
     case Q2_0: return launch_gemv_codec<Q2_0>(p, stream);
     case Q8_0: return launch_gemv_codec<Q8_0>(p, stream);
     }
@@ -368,6 +369,7 @@ hipError_t launch_dequant(const GemmProblem &p, _Float16 *out, int64_t ldw, hipS
     switch (p.codec) {
     case Q4_0: fn = reinterpret_cast<const void *>(&dequant_kernel<Q4_0>); break;
     case MLX4_G64: fn = reinterpret_cast<const void *>(&dequant_kernel<MLX4_G64>); break;
+    case MLX4_G32: fn = reinterpret_cast<const void *>(&dequant_kernel<MLX4_G32>); break;
     case Q2_0: fn = reinterpret_cast<const void *>(&dequant_kernel<Q2_0>); break;
     case Q8_0: fn = reinterpret_cast<const void *>(&dequant_kernel<Q8_0>); break;
     default: return hipErrorInvalidValue;

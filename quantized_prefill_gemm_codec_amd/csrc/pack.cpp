@@ -11,7 +11,7 @@ using namespace qg;
 
 namespace {
 
-bool valid_codec(int32_t c) { return c == Q4_0 || c == MLX4_G64 || c == Q2_0 || c == Q8_0; }
+bool valid_codec(int32_t c) { return c == Q4_0 || c == MLX4_G64 || c == Q2_0 || c == Q8_0 || c == MLX4_G32; }
 
 qg_status check_shape(int32_t codec, int64_t n, int64_t k)
 {
@@ -32,7 +32,8 @@ size_t canonical_size(int32_t codec, int64_t n, int64_t k)
         return size_t(n) * size_t(k / 128) * 34;
     if (codec == Q8_0)
         return size_t(n) * size_t(k / 32) * 34;
-    return size_t(n) * size_t(k / 2) + 2 * size_t(n) * size_t(k / 64) * 2;
+    const int64_t group = codec == MLX4_G32 ? 32 : 64;
+    return size_t(n) * size_t(k / 2) + 2 * size_t(n) * size_t(k / group) * 2;
 }
 
 inline uint16_t rd16(const uint8_t *p) { return uint16_t(p[0] | (p[1] << 8)); }
@@ -126,7 +127,7 @@ qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonica
     uint8_t *s = static_cast<uint8_t *>(scales);
     Geometry g = geometry(codec, n, k);
     const int cb = lane_code_bytes(codec);
-    const bool four_bit = codec == Q4_0 || codec == MLX4_G64;
+    const bool four_bit = codec == Q4_0 || is_mlx(codec);
     // zero-weight code for padding: Q4_0 q = 8, Q2_0 q = 1, Q8_0 q = 0 (stored
     // 128), MLX q = 0 (s = b = 0)
     const int pad_code = codec == Q4_0 ? 8 : codec == Q2_0 ? 1 : codec == Q8_0 ? 128 : 0;
@@ -183,11 +184,15 @@ qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonica
             for (int64_t blk = 0; blk < nb; ++blk)
                 wr16(s + ((r * nb + blk) * 32 + i) * 2, rd16(c + (row * nb + blk) * 34));
         } else {
-            const int64_t ng = k / 64;
+            const int64_t group = codec == MLX4_G32 ? 32 : 64;
+            const int64_t ng = k / group;
             const uint8_t *sc = c + size_t(n) * size_t(k / 2);
             const uint8_t *bi = sc + size_t(n) * size_t(ng) * 2;
             for (int64_t grp = 0; grp < ng; ++grp) {
-                uint8_t *e = s + ((r * g.ksteps + grp) * 32 + i) * 4;
+                // G64: record (t, i); G32: record (t, g, i) with group = 2t + g
+                const int64_t rec = codec == MLX4_G32 ? ((r * g.ksteps + grp / 2) * 2 + grp % 2) * 32 + i
+                                                      : (r * g.ksteps + grp) * 32 + i;
+                uint8_t *e = s + rec * 4;
                 wr16(e, rd16(sc + (row * ng + grp) * 2));
                 wr16(e + 2, rd16(bi + (row * ng + grp) * 2));
             }

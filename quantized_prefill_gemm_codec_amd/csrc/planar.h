@@ -33,6 +33,7 @@
 // Scale planes, one 64-lane (Q4_0) or 32-lane record per chunk:
 //  * Q4_0:     fp16 [N/32][K/64][2][32]  -- d of block 2t+g for lane (g, i)
 //  * Q8_0:     same as Q4_0
+//  * MLX4-G32: u32  [N/32][K/64][2][32]  -- (s, b) of group 2t+g for lane (g, i)
 //  * MLX4-G64: u32  [N/32][K/64][32]     -- (s, b) of group t as two fp16
 //                                           (scale low half, bias high half),
 //                                           so one 32-bit load brings both
@@ -52,13 +53,15 @@
 
 namespace qg {
 
-enum Codec : int32_t { Q4_0 = 1, MLX4_G64 = 2, Q2_0 = 3, Q8_0 = 4 };
+enum Codec : int32_t { Q4_0 = 1, MLX4_G64 = 2, Q2_0 = 3, Q8_0 = 4, MLX4_G32 = 5 };
+
+QG_HD inline bool is_mlx(int codec) { return codec == MLX4_G64 || codec == MLX4_G32; }
 
 QG_HD inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 QG_HD inline int block_size(int codec)
 {
-    return codec == Q4_0 ? 32 : codec == MLX4_G64 ? 64 : codec == Q2_0 ? 128 : codec == Q8_0 ? 32 : 0;
+    return codec == Q4_0 ? 32 : codec == MLX4_G64 ? 64 : codec == Q2_0 ? 128 : codec == Q8_0 ? 32 : codec == MLX4_G32 ? 32 : 0;
 }
 
 // bytes of codes a lane holds per chunk
@@ -78,6 +81,8 @@ QG_HD inline Geometry geometry(int codec, int64_t n, int64_t k)
     g.qs_bytes = g.groups * g.ksteps * 64 * lane_code_bytes(codec);
     if (codec == Q4_0 || codec == Q8_0)
         g.scale_bytes = g.groups * g.ksteps * 64 * 2;
+    else if (codec == MLX4_G32)
+        g.scale_bytes = g.groups * g.ksteps * 64 * 4;
     else if (codec == MLX4_G64)
         g.scale_bytes = g.groups * g.ksteps * 32 * 4;
     else

@@ -15,6 +15,7 @@
 // handed to the MFMA is the correctly rounded value of the exact codec weight:
 //   Q4_0      w = (q - 8) * d              (v_pk_add_f16, v_pk_mul_f16)
 //   MLX4-G64  w = fma(q, s, b)             (v_pk_add_f16, v_pk_fma_f16)
+//   MLX4-G32  the same, one (s, b) per 32 weights
 //   Q2_0      w = (q - 1) * d, q=3 -> +2d  (v_pk_add_f16, v_pk_mul_f16)
 //   Q8_0      w = q * d, stored q + 128    (v_pk_add_f16, v_pk_mul_f16)
 // (Q2_0 values are exact; Q4_0 and MLX round once.  fp16 subnormals are kept:
@@ -69,6 +70,10 @@ template <> struct LaneCodes<MLX4_G64> {
     u32x4 c;
     uint32_t sb;   // fp16 scale (low half) and fp16 bias (high half)
 };
+template <> struct LaneCodes<MLX4_G32> {
+    u32x4 c;
+    uint32_t sb;   // the lane's own group (2t + g): fp16 scale low, fp16 bias high
+};
 template <> struct LaneCodes<Q2_0> {
     u32x2 c;
     _Float16 d;
@@ -82,6 +87,7 @@ template <> struct LaneCodes<Q8_0> {
 template <int CODEC> struct CodeZero;
 template <> struct CodeZero<Q4_0> { static constexpr int v = 8; };
 template <> struct CodeZero<MLX4_G64> { static constexpr int v = 0; };
+template <> struct CodeZero<MLX4_G32> { static constexpr int v = 0; };
 template <> struct CodeZero<Q2_0> { static constexpr int v = 1; };
 template <> struct CodeZero<Q8_0> { static constexpr int v = 128; };   // codes are stored as q + 128
 
@@ -129,7 +135,7 @@ __device__ __forceinline__ f16x8 unpack_substep(const LaneCodes<CODEC> &lc, int 
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         f16x2 w;
-        if constexpr (CODEC == MLX4_G64) {
+        if constexpr (CODEC == MLX4_G64 || CODEC == MLX4_G32) {
             const f16x2 sb = as_f16x2(lc.sb);
             const f16x2 sc = {sb[0], sb[0]};
             const f16x2 bi = {sb[1], sb[1]};
@@ -201,6 +207,9 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int rg, int groups, int lane
     } else if constexpr (CODEC == Q4_0 || CODEC == Q8_0) {
         o.q = uint32_t(lane) * 16;
         o.s = uint32_t(lane) * 2;
+    } else if constexpr (CODEC == MLX4_G32) {
+        o.q = uint32_t(lane) * 16;
+        o.s = uint32_t(lane) * 4;
     } else {
         o.q = uint32_t(lane) * 16;
         o.s = i * 4;
@@ -229,6 +238,8 @@ __device__ __forceinline__ LaneCodes<CODEC> load_lane(const PlaneRsrc &w, LaneOf
         lc.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 1024, 0));
         if constexpr (CODEC == Q4_0)
             lc.d = load_f16(w.sc, o.s, chunk * 128);
+        else if constexpr (CODEC == MLX4_G32)
+            lc.sb = __builtin_amdgcn_raw_buffer_load_b32(w.sc, o.s, chunk * 256, 0);
         else
             lc.sb = __builtin_amdgcn_raw_buffer_load_b32(w.sc, o.s, chunk * 128, 0);
     }

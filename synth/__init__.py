@@ -19,6 +19,8 @@ Canonical byte formats (the input contract both sides read):
   Ternary Codec"): blocks of 128 weights, 34 bytes: fp16 ``d`` in bytes 0-1,
   then 32 bytes of 2-bit codes, weight ``i`` in byte ``2 + i // 4`` at bit
   ``2 * (i % 4)``.  Weight value ``(q - 1) * d``.
+* MLX4-G32: as MLX4-G64 with one scale and bias per 32 weights (the group of
+  the pages' 20-byte block_mlx_4bit, comparison page section 4).
 * Q8_0 (GGUF block_q8_0; the registry of the releases page, v0.3.0, lists Q8_0
   without a layout): blocks of 32 weights, 34 bytes: fp16 ``d`` in bytes 0-1,
   then weight ``j`` as the two's-complement byte ``2 + j``.  Weight value
@@ -44,10 +46,12 @@ CODEC_Q4_0 = 1
 CODEC_MLX4_G64 = 2
 CODEC_Q2_0 = 3
 CODEC_Q8_0 = 4
+CODEC_MLX4_G32 = 5
 
-CODEC_NAMES = {CODEC_Q4_0: "q4_0", CODEC_MLX4_G64: "mlx4_g64", CODEC_Q2_0: "q2_0", CODEC_Q8_0: "q8_0"}
+CODEC_NAMES = {CODEC_Q4_0: "q4_0", CODEC_MLX4_G64: "mlx4_g64", CODEC_Q2_0: "q2_0", CODEC_Q8_0: "q8_0",
+               CODEC_MLX4_G32: "mlx4_g32"}
 # weights per block (scale group) along K
-BLOCK = {CODEC_Q4_0: 32, CODEC_MLX4_G64: 64, CODEC_Q2_0: 128, CODEC_Q8_0: 32}
+BLOCK = {CODEC_Q4_0: 32, CODEC_MLX4_G64: 64, CODEC_Q2_0: 128, CODEC_Q8_0: 32, CODEC_MLX4_G32: 32}
 
 BASE_SEED = 0x51C0DEC0
 
@@ -68,6 +72,8 @@ def canonical_bytes(codec: int, n: int, k: int) -> int:
         return n * (k // 32) * 18
     if codec == CODEC_MLX4_G64:
         return n * (k // 2) + 2 * (n * (k // 64) * 2)
+    if codec == CODEC_MLX4_G32:
+        return n * (k // 2) + 2 * (n * (k // 32) * 2)
     if codec == CODEC_Q2_0:
         return n * (k // 128) * 34
     if codec == CODEC_Q8_0:
@@ -96,7 +102,7 @@ def encode_q4_0(codes: np.ndarray, d: np.ndarray) -> np.ndarray:
 
 
 def encode_mlx4(codes: np.ndarray, s: np.ndarray, b: np.ndarray) -> np.ndarray:
-    """Lay out codes [n, k] (0..15), fp16 scales and biases [n, k/64] in MLX order."""
+    """Lay out codes [n, k] (0..15), fp16 scales and biases [n, k/group] in MLX order."""
     n, k = codes.shape
     q = codes.reshape(n, k // 8, 8).astype(np.uint32)
     words = np.zeros((n, k // 8), dtype=np.uint32)
@@ -146,6 +152,15 @@ def gen_mlx4(n: int, k: int, seed: int, tensor_id: int = T_W,
     return encode_mlx4(codes, s, b)
 
 
+def gen_mlx4_g32(n: int, k: int, seed: int, tensor_id: int = T_W,
+                 s_range=(0.002, 0.01), b_sigma=0.02) -> np.ndarray:
+    rng = _rng(seed, tensor_id)
+    codes = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
+    s = fp16_uniform(rng, s_range[0], s_range[1], (n, k // 32))
+    b = (b_sigma * rng.standard_normal((n, k // 32))).astype(np.float16)
+    return encode_mlx4(codes, s, b)
+
+
 Q2_0_PROBS = (0.30, 0.35, 0.30, 0.05)
 
 
@@ -167,7 +182,8 @@ def gen_q8_0(n: int, k: int, seed: int, tensor_id: int = T_W,
     return encode_q8_0(codes, d)
 
 
-GEN = {CODEC_Q4_0: gen_q4_0, CODEC_MLX4_G64: gen_mlx4, CODEC_Q2_0: gen_q2_0, CODEC_Q8_0: gen_q8_0}
+GEN = {CODEC_Q4_0: gen_q4_0, CODEC_MLX4_G64: gen_mlx4, CODEC_Q2_0: gen_q2_0, CODEC_Q8_0: gen_q8_0,
+       CODEC_MLX4_G32: gen_mlx4_g32}
 
 
 def gen_weight(codec: int, n: int, k: int, seed: int, tensor_id: int = T_W) -> np.ndarray:
@@ -216,6 +232,9 @@ WORKLOADS = {
     "q4_0_gemv_64x4096x14336": Workload("q4_0_gemv_64x4096x14336", "gemv", CODEC_Q4_0, 64, 4096, 14336, BASE_SEED + 5),
     # next-step codec on the 1B-shape up-projection
     "q8_0_prefill_2048x2048x8192": Workload("q8_0_prefill_2048x2048x8192", "prefill", CODEC_Q8_0, 2048, 2048, 8192, BASE_SEED + 6),
+    # next-step codec variant: MLX 4-bit with group 32 on the 1B-shape up-projection
+    "mlx4_g32_prefill_2048x2048x8192": Workload("mlx4_g32_prefill_2048x2048x8192", "prefill", CODEC_MLX4_G32, 2048, 2048,
+                                                8192, BASE_SEED + 9),
     # next-step layout: 8B-shape Q projection written per head ([32, 2048, 128])
     "q4_0_qproj_heads_2048x4096x4096": Workload("q4_0_qproj_heads_2048x4096x4096", "heads", CODEC_Q4_0, 2048, 4096, 4096,
                                                 BASE_SEED + 8, head_dim=128),

@@ -67,7 +67,8 @@ def _same_value_bits(a16, b16):
 # ------------------------------------------------------------- dequantization --
 
 DEQ_SHAPES = [(1, 256, 256), (1, 40, 96), (1, 1000, 544), (2, 33, 192), (2, 300, 1024),
-              (3, 37, 256), (3, 520, 1152), (4, 256, 256), (4, 40, 96), (4, 300, 544)]
+              (3, 37, 256), (3, 520, 1152), (4, 256, 256), (4, 40, 96), (4, 300, 544),
+              (5, 256, 256), (5, 33, 96), (5, 300, 544)]
 
 
 @pytest.mark.parametrize("codec,n,k", DEQ_SHAPES)
@@ -112,6 +113,8 @@ GEMM_SHAPES = [
     (1, 48, 320, 2080), (2, 40, 72, 1152), (3, 64, 96, 1408),
     # Q8_0 through every kernel shape class
     (4, 16, 256, 256), (4, 33, 200, 288), (4, 129, 136, 160), (4, 300, 264, 352), (4, 257, 1024, 256),
+    # MLX4-G32 likewise
+    (5, 16, 256, 256), (5, 33, 200, 288), (5, 129, 136, 160), (5, 300, 264, 352), (5, 257, 1024, 256),
 ]
 
 
@@ -199,7 +202,7 @@ def test_prefill_heads_layout(torch, codec, m, n, k, d):
 # -------------------------------------------------------------------- SwiGLU --
 
 SWIGLU_SHAPES = [(2, 33, 200, 192), (2, 130, 256, 128), (2, 300, 264, 256), (1, 70, 136, 96), (3, 200, 128, 256),
-                 (4, 200, 128, 256), (4, 70, 136, 96)]
+                 (4, 200, 128, 256), (4, 70, 136, 96), (5, 200, 128, 256), (5, 70, 136, 96)]
 
 
 @pytest.mark.parametrize("codec,m,n,k", SWIGLU_SHAPES)
@@ -264,7 +267,8 @@ def test_geglu_one_hot_probe(torch):
 GEMV_SHAPES = [(1, 1, 1000, 512), (1, 2, 256, 96), (1, 3, 520, 256), (1, 4, 200, 1024), (1, 5, 256, 256),
                (1, 17, 136, 192), (1, 64, 512, 512), (2, 1, 300, 256), (2, 4, 256, 512), (2, 33, 256, 128),
                (3, 1, 264, 512), (3, 3, 256, 256), (3, 64, 200, 384),
-               (4, 1, 1000, 512), (4, 3, 264, 256), (4, 64, 200, 384)]
+               (4, 1, 1000, 512), (4, 3, 264, 256), (4, 64, 200, 384),
+               (5, 1, 1000, 512), (5, 2, 264, 96), (5, 64, 200, 384)]
 
 
 @pytest.mark.parametrize("codec,m,n,k", GEMV_SHAPES)

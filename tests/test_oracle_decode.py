@@ -41,6 +41,12 @@ def test_q4_0_geometry():
     assert oracle.block_geometry(oracle.Q4_0) == (32, 18)
 
 
+def test_mlx4_g32_is_the_pages_20_byte_block():
+    # comparison page, section 4: block_mlx_4bit is 20 bytes (20 mod 16 = 4)
+    weights, nbytes = oracle.block_geometry(oracle.MLX4_G32)
+    assert (weights, nbytes) == (32, 20) and nbytes % 16 == 4
+
+
 def test_q8_0_geometry():
     weights, nbytes = oracle.block_geometry(oracle.Q8_0)
     assert (weights, nbytes) == (32, 34)
@@ -71,7 +77,7 @@ def _random_canon(codec, n, k, seed):
     return synth.gen_weight(codec, n, k, seed)
 
 
-@pytest.mark.parametrize("codec", [1, 2, 3, 4])
+@pytest.mark.parametrize("codec", [1, 2, 3, 4, 5])
 def test_dequant_f16_matches_numpy_rounding(codec):
     n, k = 16, 512
     canon = _random_canon(codec, n, k, 99)
@@ -98,6 +104,17 @@ def test_generator_mlx4_encoding_matches_decode():
     b = (0.02 * rng.standard_normal((n, k // 64))).astype(np.float16)
     w = oracle.decode(2, synth.encode_mlx4(codes, s, b), n, k)
     want = codes * np.repeat(s.astype(np.float64), 64, axis=1) + np.repeat(b.astype(np.float64), 64, axis=1)
+    assert np.array_equal(w, want)
+
+
+def test_generator_mlx4_g32_encoding_matches_decode():
+    rng = np.random.default_rng(8)
+    n, k = 3, 160
+    codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    s = rng.uniform(0.002, 0.01, (n, k // 32)).astype(np.float16)
+    b = (0.02 * rng.standard_normal((n, k // 32))).astype(np.float16)
+    w = oracle.decode(5, synth.encode_mlx4(codes, s, b), n, k)
+    want = codes * np.repeat(s.astype(np.float64), 32, axis=1) + np.repeat(b.astype(np.float64), 32, axis=1)
     assert np.array_equal(w, want)
 
 
