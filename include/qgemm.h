@@ -59,13 +59,22 @@ extern "C" {
  *  QG_CODEC_Q8_0     32-weight blocks of 34 bytes: fp16 d, then weight j as
  *                    the two's-complement byte 2 + j; w = q * d.  (Q8_0 is in
  *                    the quantization registry of the releases page, v0.3.0;
- *                    the byte layout is GGUF's block_q8_0.) */
+ *                    the byte layout is GGUF's block_q8_0.)
+ *  QG_CODEC_Q4_K     256-weight super-blocks of 144 bytes: fp16 d, fp16 dmin,
+ *                    12 bytes of eight 6-bit sub-block scales sc[j] and mins
+ *                    m[j], then 128 code bytes in four 32-byte runs (byte l
+ *                    of run u: weight 64u + l in the low nibble, 64u + 32 + l
+ *                    in the high); w = d * sc[j] * q - dmin * m[j] over
+ *                    sub-block j = weights 32j .. 32j + 31.  (The pages list
+ *                    "Q4_K (GGUF Super-Blocks)" among the router's formats,
+ *                    releases page v0.2; the layout is the public GGUF one.) */
 typedef enum {
     QG_CODEC_Q4_0 = 1,
     QG_CODEC_MLX4_G64 = 2,
     QG_CODEC_Q2_0 = 3,
     QG_CODEC_Q8_0 = 4,
-    QG_CODEC_MLX4_G32 = 5
+    QG_CODEC_MLX4_G32 = 5,
+    QG_CODEC_Q4_K = 6
 } qg_codec;
 
 typedef enum {

@@ -40,6 +40,12 @@
  *   - Q8_0: GGUF block_q8_0, 34 bytes per 32 weights: fp16 d, then weight j
  *     as the two's-complement byte 2 + j; w = q * d.
  *   - GELU in GeGLU: the tanh form (the Gemma family's activation).
+ *   - Q4_K: the pages name "Q4_K (GGUF Super-Blocks)" among the router's
+ *     formats (releases page, v0.2 "Universal Quantization Router"; comparison
+ *     page section 2.5) but print no layout.  The layout decoded here is the
+ *     GGUF super-block of the public GGUF format description (see
+ *     decode_q4_k_row); parity with the pages' own Q4_K kernel is therefore
+ *     unpinned -- only the oracle's reading of that layout is pinned.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fopenmp -fPIC -shared -lm
  * (no fast-math: every operation is a correctly rounded IEEE fp64 operation).
@@ -58,6 +64,7 @@
 #define ORC_Q2_0 3
 #define ORC_Q8_0 4
 #define ORC_MLX4_G32 5
+#define ORC_Q4_K 6
 
 /* ---------------------------------------------------------------- fp16 --- */
 
@@ -152,6 +159,7 @@ int orc_block_geometry(int codec, int64_t *weights, int64_t *bytes)
     case ORC_Q2_0:     *weights = 128; *bytes = 34; return 1;
     case ORC_Q8_0:     *weights = 32;  *bytes = 34; return 1;
     case ORC_MLX4_G32: *weights = 32;  *bytes = 20; return 1;
+    case ORC_Q4_K:     *weights = 256; *bytes = 144; return 1;
     default: return 0;
     }
 }
@@ -205,6 +213,49 @@ static void decode_q8_0_row(const uint8_t *row, int64_t k, double *w)
     }
 }
 
+/* Q4_K: super-blocks of 256 weights in 144 bytes -- fp16 d (bytes 0-1), fp16
+ * dmin (bytes 2-3), twelve bytes of 6-bit sub-block scales and mins (bytes
+ * 4-15), then 128 code bytes.  Sub-block j (weights 32 j .. 32 j + 31) has
+ * scale sc[j] and min m[j], and
+ *     w = d * sc[j] * q - dmin * m[j].
+ * The 6-bit fields, with b = bytes 4-15: for j < 4, sc[j] = b[j] & 63 and
+ * m[j] = b[j + 4] & 63; for j >= 4, the low four bits of sc[j] are the low
+ * nibble of b[j + 4] and its top two bits are the top two bits of b[j - 4];
+ * the low four bits of m[j] are the high nibble of b[j + 4] and its top two
+ * bits are the top two bits of b[j].  The codes form four runs of 32 bytes;
+ * byte l of run c holds weight 64 c + l in its low nibble and weight
+ * 64 c + 32 + l in its high nibble.
+ * Exact in fp64 for every finite input: d * sc * q (at most 21 significant
+ * bits) and dmin * m (17) are exact products, and their difference is an
+ * integer multiple of 2^-24 below 2^27 in magnitude -- at most 51 significant
+ * bits -- so the subtraction, whose exact result is representable, returns it. */
+static void decode_q4_k_row(const uint8_t *row, int64_t k, double *w)
+{
+    for (int64_t b = 0; b < k / 256; ++b) {
+        const uint8_t *blk = row + b * 144;
+        const double d = orc_f16_to_f64(rd_u16le(blk));
+        const double dmin = orc_f16_to_f64(rd_u16le(blk + 2));
+        const uint8_t *sb = blk + 4, *qs = blk + 16;
+        int sc[8], mn[8];
+        for (int j = 0; j < 4; ++j) {
+            sc[j] = sb[j] & 63;
+            mn[j] = sb[j + 4] & 63;
+            sc[j + 4] = (sb[j + 8] & 15) | ((sb[j] >> 6) << 4);
+            mn[j + 4] = (sb[j + 8] >> 4) | ((sb[j + 4] >> 6) << 4);
+        }
+        for (int c = 0; c < 4; ++c) {
+            for (int l = 0; l < 32; ++l) {
+                const int q[2] = {qs[32 * c + l] & 15, qs[32 * c + l] >> 4};
+                for (int h = 0; h < 2; ++h) {
+                    const int j = 2 * c + h;
+                    const int64_t idx = b * 256 + 64 * c + 32 * h + l;
+                    w[idx] = d * sc[j] * q[h] - dmin * mn[j];
+                }
+            }
+        }
+    }
+}
+
 /* MLX4 row n with group size G (64 or 32): q = (word[n][k/8] >> 4*(k%8)) & 15,
  * g = k / G, w = q * s[n][g] + b[n][g].  Exact in fp64: q*s has at most 15
  * significant bits and the sum of two fp16-derived values spans far fewer
@@ -245,6 +296,8 @@ int orc_decode_rows(int codec, const uint8_t *canon, int64_t n, int64_t k,
             decode_q2_0_row(canon + nn * (k / 128) * 34, k, wr);
         else if (codec == ORC_Q8_0)
             decode_q8_0_row(canon + nn * (k / 32) * 34, k, wr);
+        else if (codec == ORC_Q4_K)
+            decode_q4_k_row(canon + nn * (k / 256) * 144, k, wr);
         else {
             const int64_t group = codec == ORC_MLX4_G32 ? 32 : 64;
             const uint8_t *codes = canon;

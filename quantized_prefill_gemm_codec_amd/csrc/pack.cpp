@@ -11,7 +11,7 @@ using namespace qg;
 
 namespace {
 
-bool valid_codec(int32_t c) { return c == Q4_0 || c == MLX4_G64 || c == Q2_0 || c == Q8_0 || c == MLX4_G32; }
+bool valid_codec(int32_t c) { return c == Q4_0 || c == MLX4_G64 || c == Q2_0 || c == Q8_0 || c == MLX4_G32 || c == Q4_K; }
 
 qg_status check_shape(int32_t codec, int64_t n, int64_t k)
 {
@@ -32,6 +32,8 @@ size_t canonical_size(int32_t codec, int64_t n, int64_t k)
         return size_t(n) * size_t(k / 128) * 34;
     if (codec == Q8_0)
         return size_t(n) * size_t(k / 32) * 34;
+    if (codec == Q4_K)
+        return size_t(n) * size_t(k / 256) * 144;
     const int64_t group = codec == MLX4_G32 ? 32 : 64;
     return size_t(n) * size_t(k / 2) + 2 * size_t(n) * size_t(k / group) * 2;
 }
@@ -54,6 +56,13 @@ inline int canonical_code(int32_t codec, const uint8_t *c, int64_t row, int64_t 
         const uint8_t *blk = c + (row * (k / 32) + kk / 32) * 18;
         int j = int(kk % 32);
         return j < 16 ? (blk[2 + j] & 0xF) : (blk[2 + j - 16] >> 4);
+    }
+    if (codec == Q4_K) {
+        // four 32-byte runs; byte l of run u: weight 64 u + l (low nibble), 64 u + 32 + l (high)
+        const uint8_t *blk = c + (row * (k / 256) + kk / 256) * 144;
+        const int w = int(kk % 256), l = w % 64;
+        const uint8_t b = blk[16 + 32 * (w / 64) + l % 32];
+        return l < 32 ? (b & 0xF) : (b >> 4);
     }
     if (codec == Q2_0) {
         const uint8_t *blk = c + (row * (k / 128) + kk / 128) * 34;
@@ -127,9 +136,9 @@ qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonica
     uint8_t *s = static_cast<uint8_t *>(scales);
     Geometry g = geometry(codec, n, k);
     const int cb = lane_code_bytes(codec);
-    const bool four_bit = codec == Q4_0 || is_mlx(codec);
+    const bool four_bit = codec == Q4_0 || is_mlx(codec) || codec == Q4_K;
     // zero-weight code for padding: Q4_0 q = 8, Q2_0 q = 1, Q8_0 q = 0 (stored
-    // 128), MLX q = 0 (s = b = 0)
+    // 128), MLX and Q4_K q = 0 (zero scale records)
     const int pad_code = codec == Q4_0 ? 8 : codec == Q2_0 ? 1 : codec == Q8_0 ? 128 : 0;
 
     memset(q, 0, size_t(g.qs_bytes));
@@ -178,6 +187,31 @@ qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonica
             for (int64_t blk = 0; blk < k / 32; ++blk) {
                 const int64_t t = blk / 2, gh = blk % 2;
                 wr16(s + (((r * g.ksteps + t) * 2 + gh) * 32 + i) * 2, rd16(c + (row * (k / 32) + blk) * bb));
+            }
+        } else if (codec == Q4_K) {
+            // unpack the twelve bytes of 6-bit fields: for j < 4, sc[j] and
+            // m[j] are the low 6 bits of bytes j and j + 4; for j >= 4 the low
+            // nibble / high nibble of byte j + 4 give the low 4 bits of sc[j] /
+            // m[j], and the top 2 bits of bytes j - 4 / j their top 2 bits
+            const int64_t nsb = k / 256;
+            for (int64_t sbk = 0; sbk < nsb; ++sbk) {
+                const uint8_t *blk = c + (row * nsb + sbk) * 144;
+                const uint8_t *f = blk + 4;
+                uint8_t scv[8], mv[8];
+                for (int j = 0; j < 4; ++j) {
+                    scv[j] = uint8_t(f[j] & 63);
+                    mv[j] = uint8_t(f[j + 4] & 63);
+                    scv[j + 4] = uint8_t((f[j + 8] & 15) | ((f[j] >> 6) << 4));
+                    mv[j + 4] = uint8_t((f[j + 8] >> 4) | ((f[j + 4] >> 6) << 4));
+                }
+                uint8_t *rec = s + (r * nsb + sbk) * 640;
+                for (int u = 0; u < 4; ++u)
+                    for (int gh = 0; gh < 2; ++gh) {
+                        uint8_t *e = rec + u * 128 + (gh * 32 + i) * 2;
+                        e[0] = scv[2 * u + gh];
+                        e[1] = mv[2 * u + gh];
+                    }
+                memcpy(rec + 512 + i * 4, blk, 4);     // fp16 d, fp16 dmin
             }
         } else if (codec == Q2_0) {
             const int64_t nb = k / 128;

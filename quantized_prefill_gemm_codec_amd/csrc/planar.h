@@ -18,7 +18,7 @@
 //
 // Code order inside a lane's bytes (chosen so that unpacking needs one shift,
 // one and-or per pair of weights and no byte shuffles):
-//  * 4-bit (Q4_0, MLX4-G64): 16 bytes = 4 dwords; dword s holds j = 8 s + e,
+//  * 4-bit (Q4_0, MLX4-G64, MLX4-G32, Q4_K): 16 bytes = 4 dwords; dword s holds j = 8 s + e,
 //    with e = 2p at bits [4p, 4p+4) and e = 2p + 1 at bits [16+4p, 20+4p).
 //  * 2-bit (Q2_0): 8 bytes = 2 dwords; dword h holds j = 16 h + e, with
 //    e = 2p at bits [2p, 2p+2) and e = 2p + 1 at bits [16+2p, 18+2p).
@@ -38,6 +38,12 @@
 //                                           (scale low half, bias high half),
 //                                           so one 32-bit load brings both
 //  * Q2_0:     fp16 [N/32][K/128][32]    -- d of block t/2
+//  * Q4_K:     [N/32][K/256][640 bytes], one record per (row group,
+//              super-block): bytes 128 u .. 128 u + 127 are u16 [64 lanes]
+//              for k-step 4 sb + u, lane (g, i) holding sc | m << 8 of its
+//              sub-block 2 u + g (the 6-bit fields unpacked to bytes); bytes
+//              512..639 are u32 [32 rows], fp16 d low and fp16 dmin high.
+//              4.625 bits per weight (canonical: 4.5).
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -53,7 +59,7 @@
 
 namespace qg {
 
-enum Codec : int32_t { Q4_0 = 1, MLX4_G64 = 2, Q2_0 = 3, Q8_0 = 4, MLX4_G32 = 5 };
+enum Codec : int32_t { Q4_0 = 1, MLX4_G64 = 2, Q2_0 = 3, Q8_0 = 4, MLX4_G32 = 5, Q4_K = 6 };
 
 QG_HD inline bool is_mlx(int codec) { return codec == MLX4_G64 || codec == MLX4_G32; }
 
@@ -61,7 +67,8 @@ QG_HD inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 QG_HD inline int block_size(int codec)
 {
-    return codec == Q4_0 ? 32 : codec == MLX4_G64 ? 64 : codec == Q2_0 ? 128 : codec == Q8_0 ? 32 : codec == MLX4_G32 ? 32 : 0;
+    return codec == Q4_0 ? 32 : codec == MLX4_G64 ? 64 : codec == Q2_0 ? 128 : codec == Q8_0 ? 32 : codec == MLX4_G32 ? 32
+         : codec == Q4_K ? 256 : 0;
 }
 
 // bytes of codes a lane holds per chunk
@@ -85,6 +92,8 @@ QG_HD inline Geometry geometry(int codec, int64_t n, int64_t k)
         g.scale_bytes = g.groups * g.ksteps * 64 * 4;
     else if (codec == MLX4_G64)
         g.scale_bytes = g.groups * g.ksteps * 32 * 4;
+    else if (codec == Q4_K)
+        g.scale_bytes = g.groups * (g.ksteps / 4) * 640;
     else
         g.scale_bytes = g.groups * ceil_div(k, 128) * 32 * 2;
     return g;

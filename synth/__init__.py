@@ -25,6 +25,16 @@ Canonical byte formats (the input contract both sides read):
   without a layout): blocks of 32 weights, 34 bytes: fp16 ``d`` in bytes 0-1,
   then weight ``j`` as the two's-complement byte ``2 + j``.  Weight value
   ``q * d``.
+* Q4_K (GGUF super-block; the pages list "Q4_K (GGUF Super-Blocks)" among the
+  router's formats without a layout, so this is the public GGUF layout):
+  256 weights in 144 bytes: fp16 ``d`` (bytes 0-1), fp16 ``dmin`` (2-3), 12
+  bytes of 6-bit sub-block scales ``sc[j]`` and mins ``m[j]`` (4-15), then 128
+  code bytes in four 32-byte runs, byte ``l`` of run ``c`` holding weight
+  ``64 c + l`` (low nibble) and ``64 c + 32 + l`` (high nibble).  For
+  ``j < 4``: byte ``4 + j`` = ``sc[j]`` plus the top two bits of ``sc[j + 4]``
+  at bits 6-7, byte ``8 + j`` = ``m[j]`` plus the top two bits of ``m[j + 4]``;
+  byte ``12 + j`` = low nibbles of ``sc[j + 4]`` and ``m[j + 4]``.  Weight
+  value ``d * sc[j] * q - dmin * m[j]`` in sub-block ``j`` (32 weights).
 
 Distributions and shapes follow the five workloads of the method: fp16
 activations ~N(0,1); Q4_0 scales ~U(0.005, 0.02) with codes ~U{0..15}; MLX
@@ -32,6 +42,8 @@ scales ~U(0.002, 0.01), biases ~N(0, 0.02), codes ~U{0..15}; Q2_0 scales
 ~U(0.01, 0.05) with P(q=0,1,2,3) = 0.30, 0.35, 0.30, 0.05.  The Q8_0 workload
 (a next-step codec, not one of the five) uses codes ~U{-127..127} and scales
 ~U(0.0005, 0.0015), which keeps its weights in the Q4_0 workload's range.
+The Q4_K workloads (next-step codec) draw codes ~U{0..15}, sub-block scales
+and mins ~U{0..63} and super-block d, dmin ~U(0.0001, 0.0004).
 
 Random streams: numpy PCG64 seeded from ``SeedSequence([seed, tensor_id])``
 so every tensor of every workload has its own reproducible stream.
@@ -47,11 +59,12 @@ CODEC_MLX4_G64 = 2
 CODEC_Q2_0 = 3
 CODEC_Q8_0 = 4
 CODEC_MLX4_G32 = 5
+CODEC_Q4_K = 6
 
 CODEC_NAMES = {CODEC_Q4_0: "q4_0", CODEC_MLX4_G64: "mlx4_g64", CODEC_Q2_0: "q2_0", CODEC_Q8_0: "q8_0",
-               CODEC_MLX4_G32: "mlx4_g32"}
+               CODEC_MLX4_G32: "mlx4_g32", CODEC_Q4_K: "q4_k"}
 # weights per block (scale group) along K
-BLOCK = {CODEC_Q4_0: 32, CODEC_MLX4_G64: 64, CODEC_Q2_0: 128, CODEC_Q8_0: 32, CODEC_MLX4_G32: 32}
+BLOCK = {CODEC_Q4_0: 32, CODEC_MLX4_G64: 64, CODEC_Q2_0: 128, CODEC_Q8_0: 32, CODEC_MLX4_G32: 32, CODEC_Q4_K: 256}
 
 BASE_SEED = 0x51C0DEC0
 
@@ -78,6 +91,8 @@ def canonical_bytes(codec: int, n: int, k: int) -> int:
         return n * (k // 128) * 34
     if codec == CODEC_Q8_0:
         return n * (k // 32) * 34
+    if codec == CODEC_Q4_K:
+        return n * (k // 256) * 144
     raise ValueError(codec)
 
 
@@ -135,6 +150,25 @@ def encode_q8_0(codes: np.ndarray, d: np.ndarray) -> np.ndarray:
     return out.reshape(-1)
 
 
+def encode_q4_k(codes: np.ndarray, sc: np.ndarray, mn: np.ndarray, d: np.ndarray,
+                dmin: np.ndarray) -> np.ndarray:
+    """Lay out codes [n, k] (0..15), 6-bit sub-block scales and mins [n, k/32]
+    (0..63) and fp16 super-block d, dmin [n, k/256] as Q4_K super-blocks."""
+    n, k = codes.shape
+    nb = k // 256
+    s = sc.reshape(n, nb, 8).astype(np.uint8)
+    m = mn.reshape(n, nb, 8).astype(np.uint8)
+    q = codes.reshape(n, nb, 4, 2, 32).astype(np.uint8)      # run, nibble half, byte
+    out = np.empty((n, nb, 144), dtype=np.uint8)
+    out[:, :, 0:2] = d.astype("<f2").reshape(n, nb, 1).view(np.uint8).reshape(n, nb, 2)
+    out[:, :, 2:4] = dmin.astype("<f2").reshape(n, nb, 1).view(np.uint8).reshape(n, nb, 2)
+    out[:, :, 4:8] = (s[:, :, 0:4] & 63) | ((s[:, :, 4:8] >> 4) << 6)
+    out[:, :, 8:12] = (m[:, :, 0:4] & 63) | ((m[:, :, 4:8] >> 4) << 6)
+    out[:, :, 12:16] = (s[:, :, 4:8] & 15) | ((m[:, :, 4:8] & 15) << 4)
+    out[:, :, 16:144] = (q[:, :, :, 0, :] | (q[:, :, :, 1, :] << 4)).reshape(n, nb, 128)
+    return out.reshape(-1)
+
+
 def gen_q4_0(n: int, k: int, seed: int, tensor_id: int = T_W,
              d_range=(0.005, 0.02)) -> np.ndarray:
     rng = _rng(seed, tensor_id)
@@ -182,8 +216,19 @@ def gen_q8_0(n: int, k: int, seed: int, tensor_id: int = T_W,
     return encode_q8_0(codes, d)
 
 
+def gen_q4_k(n: int, k: int, seed: int, tensor_id: int = T_W,
+             d_range=(0.0001, 0.0004)) -> np.ndarray:
+    rng = _rng(seed, tensor_id)
+    codes = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
+    sc = rng.integers(0, 64, size=(n, k // 32), dtype=np.uint8)
+    mn = rng.integers(0, 64, size=(n, k // 32), dtype=np.uint8)
+    d = fp16_uniform(rng, d_range[0], d_range[1], (n, k // 256))
+    dmin = fp16_uniform(rng, d_range[0], d_range[1], (n, k // 256))
+    return encode_q4_k(codes, sc, mn, d, dmin)
+
+
 GEN = {CODEC_Q4_0: gen_q4_0, CODEC_MLX4_G64: gen_mlx4, CODEC_Q2_0: gen_q2_0, CODEC_Q8_0: gen_q8_0,
-       CODEC_MLX4_G32: gen_mlx4_g32}
+       CODEC_MLX4_G32: gen_mlx4_g32, CODEC_Q4_K: gen_q4_k}
 
 
 def gen_weight(codec: int, n: int, k: int, seed: int, tensor_id: int = T_W) -> np.ndarray:
@@ -240,4 +285,8 @@ WORKLOADS = {
                                                 BASE_SEED + 8, head_dim=128),
     # next-step epilogue: the 8B-shape gate/up pair with GeGLU instead of SwiGLU
     "mlx4_geglu_2048x4096x14336": Workload("mlx4_geglu_2048x4096x14336", "geglu", CODEC_MLX4_G64, 2048, 4096, 14336, BASE_SEED + 7),
+    # next-step codec: GGUF Q4_K super-blocks on the 1B-shape up-projection and the 8B decode shape
+    "q4_k_prefill_2048x2048x8192": Workload("q4_k_prefill_2048x2048x8192", "prefill", CODEC_Q4_K, 2048, 2048, 8192,
+                                            BASE_SEED + 10),
+    "q4_k_gemv_1x4096x14336": Workload("q4_k_gemv_1x4096x14336", "gemv", CODEC_Q4_K, 1, 4096, 14336, BASE_SEED + 11),
 }

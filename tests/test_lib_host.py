@@ -40,11 +40,12 @@ def test_library_exports_every_declared_symbol():
 
 
 @pytest.mark.parametrize("codec,n,k", [(1, 8192, 2048), (1, 40, 96), (2, 14336, 4096), (3, 4096, 4096), (3, 33, 128),
-                                     (4, 8192, 2048), (4, 40, 96), (5, 14336, 4096), (5, 33, 96)])
+                                     (4, 8192, 2048), (4, 40, 96), (5, 14336, 4096), (5, 33, 96),
+                                     (6, 8192, 2048), (6, 40, 256)])
 def test_sizes(codec, n, k):
     qs, sc = qg.qg_packed_sizes(codec, n, k)
     groups, ksteps = -(-n // 32), -(-k // 64)
-    code_bytes = {1: 16, 2: 16, 3: 8, 4: 32, 5: 16}[codec]
+    code_bytes = {1: 16, 2: 16, 3: 8, 4: 32, 5: 16, 6: 16}[codec]
     assert qs == groups * ksteps * 64 * code_bytes
     if codec in (1, 4):
         assert sc == groups * ksteps * 64 * 2
@@ -52,6 +53,8 @@ def test_sizes(codec, n, k):
         assert sc == groups * ksteps * 32 * 4
     elif codec == 5:
         assert sc == groups * ksteps * 64 * 4
+    elif codec == 6:
+        assert sc == groups * (k // 256) * 640
     else:
         assert sc == groups * (k // 128) * 32 * 2
     assert qg.qg_canonical_size(codec, n, k) == synth.canonical_bytes(codec, n, k)
@@ -60,7 +63,7 @@ def test_sizes(codec, n, k):
 def _read_planar(codec, n, k, qs, sc):
     """Independent reader of the planar layout -> (codes [n,k], scale, bias)."""
     groups, ksteps = -(-n // 32), -(-k // 64)
-    cb = {1: 16, 2: 16, 3: 8, 4: 32, 5: 16}[codec]
+    cb = {1: 16, 2: 16, 3: 8, 4: 32, 5: 16, 6: 16}[codec]
     if codec == 4:
         halves = qs.reshape(groups, ksteps, 2, 64, 16)
     else:
@@ -96,6 +99,19 @@ def _read_planar(codec, n, k, qs, sc):
         blk = kk // 32
         scale = d[rr[:, None] // 32, blk[None, :] // 2, blk[None, :] % 2, rr[:, None] % 32]
         return codes, scale.astype(np.float64), None
+    if codec == 6:
+        # [groups][K/256][640 B]: u16 [4 k-steps][64 lanes] (sc, m bytes), then u32 [32 rows] (d, dmin)
+        rec = sc.reshape(groups, k // 256, 640)
+        scm = rec[:, :, :512].reshape(groups, k // 256, 4, 2, 32, 2).astype(np.int64)
+        dd = rec[:, :, 512:].copy().view(np.float16).reshape(groups, k // 256, 32, 2).astype(np.float64)
+        sub = kk // 32                                          # sub-block index along K
+        sbk, u, gh = sub // 8, (sub % 8) // 2, sub % 2
+        ri, rr32 = rr[:, None] // 32, rr[:, None] % 32
+        scv = scm[ri, sbk[None, :], u[None, :], gh[None, :], rr32, 0]
+        mv = scm[ri, sbk[None, :], u[None, :], gh[None, :], rr32, 1]
+        d = dd[ri, sbk[None, :], rr32, 0]
+        dmin = dd[ri, sbk[None, :], rr32, 1]
+        return codes, d * scv, -(dmin * mv)
     if codec == 5:
         sb = sc.view(np.float16).reshape(groups, ksteps, 2, 32, 2)
         grp = kk // 32
@@ -117,13 +133,14 @@ def _value(codec, codes, scale, bias):
         return (codes - 8) * scale
     if codec == 4:
         return codes * scale
-    if codec in (2, 5):
+    if codec in (2, 5, 6):
         return codes * scale + bias
     return (codes - 1) * scale
 
 
 @pytest.mark.parametrize("codec,n,k", [(1, 40, 96), (1, 64, 64), (2, 33, 192), (3, 37, 256), (3, 32, 128),
-                                     (4, 40, 96), (4, 64, 128), (5, 33, 96), (5, 64, 256)])
+                                     (4, 40, 96), (4, 64, 128), (5, 33, 96), (5, 64, 256), (6, 40, 512),
+                                     (6, 64, 256)])
 def test_pack_roundtrip_random(codec, n, k):
     canon = synth.gen_weight(codec, n, k, 77)
     qs, sc = qg.qg_pack_host(codec, n, k, canon)

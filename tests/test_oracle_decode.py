@@ -4,14 +4,21 @@
   from the formulas on the pages by hand -- Q2_0 w = (q - 1) d with q = 3 -> +2d
   in 34-byte, 128-weight blocks; Q4_0 w = (q - 8) d in 18-byte, 32-weight
   blocks; MLX w = q s + b per 64-weight group; Q8_0 w = q d with q a signed
-  byte (GGUF block_q8_0, a reading).  They fix the offsets, signs, nibble / bit
-  order, block strides and row strides.
+  byte (GGUF block_q8_0, a reading); Q4_K w = d sc q - dmin m over 256-weight,
+  144-byte super-blocks with 6-bit sub-block fields (public GGUF layout, a
+  reading).  They fix the offsets, signs, nibble / bit order, block strides and
+  row strides.
+* Q4_K is further pinned by a special case that reduces to the fixture-pinned
+  Q4_0 decode, an exhaustive sweep of its 6-bit fields and exact rational
+  arithmetic at extreme scale ratios.
 * Geometry printed on the pages: Q2_0 is 2.125 bits per weight.
 * Closed forms: MLX q = 0 gives the bias bit for bit; the fp16 image of each
   weight equals numpy's correctly rounded conversion of the exact value.
 * The seeded generator's encoders agree with the oracle's reading of the
   canonical bytes (so GPU parity inputs mean what the fixtures say).
 """
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -53,6 +60,63 @@ def test_q8_0_geometry():
     assert nbytes * 8 / weights == 8.5
 
 
+def test_q4_k_geometry():
+    weights, nbytes = oracle.block_geometry(oracle.Q4_K)
+    assert (weights, nbytes) == (256, 144)
+    assert nbytes * 8 / weights == 4.5
+
+
+def test_q4_k_with_unit_scales_is_q4_0():
+    # sc = 1, m = 8 and dmin = d make every Q4_K weight d q - 8 d, the Q4_0
+    # formula with that d in each of the super-block's eight 32-weight blocks
+    rng = np.random.default_rng(21)
+    n, k = 3, 512
+    codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    d = rng.uniform(0.005, 0.02, (n, k // 256)).astype(np.float16)
+    q4k = synth.encode_q4_k(codes, np.ones((n, k // 32), np.uint8), np.full((n, k // 32), 8, np.uint8), d, d)
+    q40 = synth.encode_q4_0(codes, np.repeat(d, 8, axis=1))
+    assert np.array_equal(oracle.decode(oracle.Q4_K, q4k, n, k), oracle.decode(oracle.Q4_0, q40, n, k))
+
+
+def test_q4_k_six_bit_fields_exhaustive():
+    # every value 0..63 in every sub-block position, for scales (d = 1, dmin = 0,
+    # q = 1: w = sc) and for mins (d = 0, dmin = -1: w = m)
+    n, k = 64, 256
+    vals = (np.arange(n)[:, None] + 7 * np.arange(8)[None, :]) % 64
+    ones = np.ones((n, k), np.uint8)
+    zeros8 = np.zeros((n, 8), np.uint8)
+    unit, zero, neg = (np.full((n, 1), v, np.float16) for v in (1.0, 0.0, -1.0))
+    w_sc = oracle.decode(oracle.Q4_K, synth.encode_q4_k(ones, vals, zeros8, unit, zero), n, k)
+    w_m = oracle.decode(oracle.Q4_K, synth.encode_q4_k(ones, zeros8, vals, zero, neg), n, k)
+    assert np.array_equal(w_sc, np.repeat(vals, 32, axis=1).astype(np.float64))
+    assert np.array_equal(w_m, np.repeat(vals, 32, axis=1).astype(np.float64))
+
+
+def test_q4_k_decode_exact_at_extreme_ratios():
+    # d and dmin from the largest normal to the smallest subnormal binary16:
+    # the fp64 decode must equal the exact rational d sc q - dmin m
+    pats = np.array([0x7BFF, 0x0001, 0x03FF, 0x0400, 0x3C00, 0x3555, 0xFBFF, 0x8001, 0x1234, 0x6A5A],
+                    dtype=np.uint16)
+    pairs = [(a, b) for a in pats for b in pats]
+    n, k = len(pairs), 256
+    rng = np.random.default_rng(22)
+    codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    sc = rng.integers(0, 64, (n, 8)).astype(np.uint8)
+    mn = rng.integers(0, 64, (n, 8)).astype(np.uint8)
+    sc[:, 0] = 63
+    mn[:, 0] = 63
+    codes[:, :32] = 15
+    d = np.array([a for a, _ in pairs], np.uint16).view(np.float16).reshape(n, 1)
+    dmin = np.array([b for _, b in pairs], np.uint16).view(np.float16).reshape(n, 1)
+    w = oracle.decode(oracle.Q4_K, synth.encode_q4_k(codes, sc, mn, d, dmin), n, k)
+    for r in range(n):
+        fd, fm = Fraction(float(d[r, 0])), Fraction(float(dmin[r, 0]))
+        for kk in range(0, k, 7):
+            j = kk // 32
+            exact = fd * int(sc[r, j]) * int(codes[r, kk]) - fm * int(mn[r, j])
+            assert Fraction(w[r, kk]) == exact
+
+
 def test_decode_rejects_bad_shapes():
     with pytest.raises(ValueError):
         oracle.decode(oracle.Q4_0, np.zeros(18, np.uint8), 1, 48)
@@ -77,7 +141,7 @@ def _random_canon(codec, n, k, seed):
     return synth.gen_weight(codec, n, k, seed)
 
 
-@pytest.mark.parametrize("codec", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("codec", [1, 2, 3, 4, 5, 6])
 def test_dequant_f16_matches_numpy_rounding(codec):
     n, k = 16, 512
     canon = _random_canon(codec, n, k, 99)
@@ -135,6 +199,21 @@ def test_generator_q8_0_encoding_matches_decode():
     d = rng.uniform(0.0005, 0.0015, (n, k // 32)).astype(np.float16)
     w = oracle.decode(4, synth.encode_q8_0(codes, d), n, k)
     want = codes.astype(np.float64) * np.repeat(d.astype(np.float64), 32, axis=1)
+    assert np.array_equal(w, want)
+
+
+def test_generator_q4_k_encoding_matches_decode():
+    rng = np.random.default_rng(9)
+    n, k = 3, 512
+    codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    sc = rng.integers(0, 64, (n, k // 32)).astype(np.uint8)
+    mn = rng.integers(0, 64, (n, k // 32)).astype(np.uint8)
+    d = rng.uniform(0.0001, 0.0004, (n, k // 256)).astype(np.float16)
+    dmin = rng.uniform(0.0001, 0.0004, (n, k // 256)).astype(np.float16)
+    w = oracle.decode(6, synth.encode_q4_k(codes, sc, mn, d, dmin), n, k)
+    dd = np.repeat(d.astype(np.float64), 256, axis=1)
+    mm = np.repeat(dmin.astype(np.float64), 256, axis=1)
+    want = dd * np.repeat(sc, 32, axis=1) * codes - mm * np.repeat(mn, 32, axis=1)
     assert np.array_equal(w, want)
 
 
