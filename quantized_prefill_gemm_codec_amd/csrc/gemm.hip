@@ -193,16 +193,24 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
         u32x4 xr[XCH];
         load_x(tnx, xr);
         load_w(tnx, cn);
+        LaneCodes<CODEC> cp[NMAT][FN];
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                cp[mt][fn] = cw[mt][fn];
+                prepare_lane<CODEC>(cp[mt][fn]);
+            }
         f16x8 xf[2][FM];
         f16x8 wf[2][NMAT][FN];
         read_x(buf, 0, xf[0]);
-        unpack(cw, 0, wf[0]);
+        unpack(cp, 0, wf[0]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int cur = s & 1;
             if (s < 3) {
                 read_x(buf, s + 1, xf[cur ^ 1]);
-                unpack(cw, s + 1, wf[cur ^ 1]);
+                unpack(cp, s + 1, wf[cur ^ 1]);
             }
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
@@ -334,7 +342,9 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     constexpr int RG = BN / 32;                            // row groups per matrix per tile
     constexpr int CB = CODEC == Q2_0 ? 8 : CODEC == Q8_0 ? 32 : 16;   // code bytes per lane per chunk
     constexpr int WCH = 64 * CB;                           // bytes per (row group, k-step) chunk
-    constexpr int SB = CODEC == Q2_0 ? 64 : CODEC == MLX4_G32 ? 256 : 128;   // scale bytes per (row group, k-step)
+    // scale bytes staged per (row group, k-step); Q4_K: the k-step's u16 (sc, m)
+    // lane records, then the super-block's (d, dmin) row records
+    constexpr int SB = CODEC == Q2_0 ? 64 : (CODEC == MLX4_G32 || CODEC == Q4_K) ? 256 : 128;
     constexpr int X_OFF = 0, X_BYTES = BM * 128;
     constexpr int W_OFF = X_BYTES, W_BYTES = NMAT * RG * WCH;
     constexpr int S_OFF = W_OFF + W_BYTES, S_BYTES = NMAT * RG * SB;
@@ -416,8 +426,13 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
         const int c = b / SB, o = b % SB;
         const int rg = c % RG;
         smat[u] = (256 * j / SB) / RG;              // wave-uniform: chunks never straddle matrices
-        const uint32_t pitch = CODEC == Q2_0 ? uint32_t(a.kb128) * 64u : uint32_t(a.ksteps) * uint32_t(SB);
-        sv[u] = (j < NSI && b < S_BYTES && rg0 + rg < a.groups) ? uint32_t(rg0 + rg) * pitch + uint32_t(o) : OOB;
+        const uint32_t pitch = CODEC == Q2_0   ? uint32_t(a.kb128) * 64u
+                             : CODEC == Q4_K ? uint32_t(a.ksteps) * 160u      // 640 B per 4 k-steps
+                                             : uint32_t(a.ksteps) * uint32_t(SB);
+        // Q4_K: bytes [0, 128) of a chunk come from the k-step's lane records
+        // (+ 128 (t % 4) at issue), bytes [128, 256) from the row records at 512
+        const uint32_t src = CODEC == Q4_K && o >= 128 ? uint32_t(o) - 128u + 512u : uint32_t(o);
+        sv[u] = (j < NSI && b < S_BYTES && rg0 + rg < a.groups) ? uint32_t(rg0 + rg) * pitch + src : OOB;
     }
 
     // iteration i of this wave's slice = k-step kbase + i; past the end of K
@@ -441,9 +456,14 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
 #pragma unroll
         for (int u = 0; u < SPW; ++u) {
             const int j = wr + NWT * u;
-            const uint32_t so = CODEC == Q2_0 ? uint32_t(t >> 1) * 64u : uint32_t(t) * uint32_t(SB);
+            const uint32_t so = CODEC == Q2_0   ? uint32_t(t >> 1) * 64u
+                              : CODEC == Q4_K ? uint32_t(t >> 2) * 640u
+                                              : uint32_t(t) * uint32_t(SB);
+            uint32_t v = in ? sv[u] : OOB;
+            if constexpr (CODEC == Q4_K)
+                v = (v != OOB && lane < 32) ? v + uint32_t(t & 3) * 128u : v;
             if (j < NSI)
-                dma_b32(smat[u] ? s1 : s0, in ? sv[u] : OOB, so, base + S_OFF + uint32_t(j * 256));
+                dma_b32(smat[u] ? s1 : s0, v, so, base + S_OFF + uint32_t(j * 256));
         }
     };
 
@@ -469,7 +489,12 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
                 const int c = mt * RG + wn * FN + fn;
                 const char *wp = st + W_OFF + c * WCH + lane * (CB == 32 ? 16 : CB);
                 const char *sp = st + S_OFF + c * SB;
-                if constexpr (CODEC == Q8_0) {
+                if constexpr (CODEC == Q4_K) {
+                    cw[mt][fn].c = *reinterpret_cast<const u32x4 *>(wp);
+                    cw[mt][fn].scm = *reinterpret_cast<const unsigned short *>(sp + lane * 2);
+                    cw[mt][fn].dd = *reinterpret_cast<const uint32_t *>(sp + 128 + i * 4);
+                    prepare_lane<CODEC>(cw[mt][fn]);
+                } else if constexpr (CODEC == Q8_0) {
                     cw[mt][fn].lo = *reinterpret_cast<const u32x4 *>(wp);
                     cw[mt][fn].hi = *reinterpret_cast<const u32x4 *>(wp + 1024);
                     cw[mt][fn].d = *reinterpret_cast<const _Float16 *>(sp + lane * 2);
@@ -743,6 +768,7 @@ hipError_t launch_gemm(const GemmProblem &p, int glu, hipStream_t stream)
     case MLX4_G32: return launch_codec<MLX4_G32>(p, glu, stream);
     case Q2_0: return launch_codec<Q2_0>(p, glu, stream);
     case Q8_0: return launch_codec<Q8_0>(p, glu, stream);
+    case Q4_K: return launch_codec<Q4_K>(p, glu, stream);
     }
     return hipErrorInvalidValue;
 }

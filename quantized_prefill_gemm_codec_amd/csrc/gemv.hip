@@ -42,7 +42,7 @@ struct GemvArgs {
     int x_lds;               // bytes of the X region
 };
 
-template <int CODEC> constexpr int corr_floats() { return CODEC == MLX4_G64 || CODEC == MLX4_G32 ? 2 : 1; }
+template <int CODEC> constexpr int corr_floats() { return CODEC == MLX4_G64 || CODEC == MLX4_G32 || CODEC == Q4_K ? 2 : 1; }
 
 // x_s[p] = x_{2p} + x_{2p+1} summed over the 4 sub-step chunks of the slice.
 template <int CODEC>
@@ -60,7 +60,7 @@ __device__ __forceinline__ void slice_correction(const u32x4 *chunks, float *out
         out[0] = -1152.0f * ((sp[0] + sp[1]) + (sp[2] + sp[3]));
     } else if constexpr (CODEC == Q4_0) {
         out[0] = -1032.0f * (sp[0] + sp[2]) - 72.0f * (sp[1] + sp[3]);
-    } else if constexpr (CODEC == MLX4_G64 || CODEC == MLX4_G32) {
+    } else if constexpr (CODEC == MLX4_G64 || CODEC == MLX4_G32 || CODEC == Q4_K) {
         out[0] = -1024.0f * (sp[0] + sp[2]) - 64.0f * (sp[1] + sp[3]);
         out[1] = (sp[0] + sp[1]) + (sp[2] + sp[3]);
     } else {
@@ -75,7 +75,7 @@ __device__ __forceinline__ void slice_correction(const u32x4 *chunks, float *out
 // (f < 10), so no shift per field is needed -- only one 8-bit shift per word
 // for the fields above bit 7.  v_dot2_f32_f16 multiplies exactly and sums in
 // fp32; per class of fields with the same factor 2^f one fp32 partial sum:
-//   Q4_0 / MLX4:  d[0] (fields at bits 0, 8 -> factor 1), d[1] (bits 4, 12 -> 16)
+//   Q4_0 / MLX4 / Q4_K: d[0] (fields at bits 0, 8 -> factor 1), d[1] (bits 4, 12 -> 16)
 //   Q2_0:         d[p] (fields at bits 2p, 8 + 2p -> factor 4^p), p = 0..3
 //   Q8_0:         d[0] (bytes at bits 0, 8 -> factor 1; stored q + 128)
 // block_sum then removes the 1024 offsets (and the codec zero point) with the
@@ -137,13 +137,28 @@ __device__ __forceinline__ void slice_dots(const LaneCodes<CODEC> &lc, const u32
     }
 }
 
-// acc + scale * sum_k (q_k - z) x_k (+ bias * sum_k x_k for MLX4); `sc` is the
-// lane's scale record (fp16 d, or fp16 s | fp16 b << 16 for MLX4).
+// acc + scale * sum_k (q_k - z) x_k (+ bias * sum_k x_k for MLX4 and Q4_K),
+// with the scale and bias of the lane's 32-weight slice:
+//   Q4_0, Q2_0, Q8_0: fp16 d;  MLX4: fp16 s, b;
+//   Q4_K: d * sc and -dmin * m, both exact in fp32.
 template <int CODEC>
-__device__ __forceinline__ float block_sum(uint32_t sc, const float (&d)[4], const float *corr, float acc)
+__device__ __forceinline__ float block_sum(const LaneCodes<CODEC> &lc, const float (&d)[4], const float *corr,
+                                           float acc)
 {
+    uint32_t sc = 0;
+    if constexpr (CODEC == MLX4_G64 || CODEC == MLX4_G32)
+        sc = lc.sb;
+    else if constexpr (CODEC == Q4_K)
+        sc = lc.dd;
+    else
+        sc = __builtin_bit_cast(unsigned short, lc.d);
     const f16x2 sb = as_f16x2(sc);
-    if constexpr (CODEC == Q8_0) {
+    if constexpr (CODEC == Q4_K) {
+        const float dsc = float(sb[0]) * float(lc.scm & 0xFFu);
+        const float nm = -(float(sb[1]) * float((lc.scm >> 8) & 0xFFu));
+        const float v = __builtin_fmaf(d[1], 0.0625f, d[0]) + corr[0];
+        return __builtin_fmaf(dsc, v, __builtin_fmaf(nm, corr[1], acc));
+    } else if constexpr (CODEC == Q8_0) {
         return __builtin_fmaf(float(sb[0]), d[0] + corr[0], acc);
     } else if constexpr (CODEC == Q2_0) {
         const float v = __builtin_fmaf(d[3], 0.015625f, __builtin_fmaf(d[2], 0.0625f, __builtin_fmaf(d[1], 0.25f, d[0])));
@@ -221,15 +236,10 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
                     for (int mr = 0; mr < MM; ++mr)
                         dots[c][mr] = 0.0f;
                 slice_dots<CODEC, MM>(lc[u], xrow, magic, dots);
-                uint32_t sc;
-                if constexpr (CODEC == MLX4_G64 || CODEC == MLX4_G32)
-                    sc = lc[u].sb;
-                else
-                    sc = __builtin_bit_cast(unsigned short, lc[u].d);
 #pragma unroll
                 for (int mr = 0; mr < MM; ++mr) {
                     const float d4[4] = {dots[0][mr], dots[1][mr], dots[2][mr], dots[3][mr]};
-                    acc[mr] = block_sum<CODEC>(sc, d4, corr + ((mr * a.ksteps + t) * 2 + g) * NC, acc[mr]);
+                    acc[mr] = block_sum<CODEC>(lc[u], d4, corr + ((mr * a.ksteps + t) * 2 + g) * NC, acc[mr]);
                 }
             }
             // refill this slot with the k-step one batch ahead
@@ -275,7 +285,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(Planes wp, int n, int k, i
     const int i = lane & 31, g = lane >> 5;
     const Magics mg = make_magics();
     const PlaneRsrc w = plane_rsrc(wp);
-    const LaneCodes<CODEC> lc = load_lane<CODEC>(w, lane_offsets<CODEC>(rg, groups, lane), rg, t, ksteps, kb128);
+    LaneCodes<CODEC> lc = load_lane<CODEC>(w, lane_offsets<CODEC>(rg, groups, lane), rg, t, ksteps, kb128);
+    prepare_lane<CODEC>(lc);
     const int row = rg * 32 + i;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -298,7 +309,7 @@ inline GemvLds gemv_lds(int codec, int64_t mm, int64_t ksteps)
     l.per = int((ksteps + GEMV_NW - 1) / GEMV_NW);
     const int64_t x = mm * ksteps * 128;
     l.x_lds = int(x);
-    const int64_t nc = is_mlx(codec) ? 2 : 1;
+    const int64_t nc = is_mlx(codec) || codec == Q4_K ? 2 : 1;
     l.bytes = size_t(l.x_lds + mm * ksteps * 2 * nc * 4 + GEMV_NW * mm * 32 * 4);
     return l;
 }
@@ -352,6 +363,7 @@ hipError_t launch_gemv(const GemmProblem &p, hipStream_t stream)
     case MLX4_G32: return launch_gemv_codec<MLX4_G32>(p, stream);
     case Q2_0: return launch_gemv_codec<Q2_0>(p, stream);
     case Q8_0: return launch_gemv_codec<Q8_0>(p, stream);
+    case Q4_K: return launch_gemv_codec<Q4_K>(p, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -372,6 +384,7 @@ hipError_t launch_dequant(const GemmProblem &p, _Float16 *out, int64_t ldw, hipS
     case MLX4_G32: fn = reinterpret_cast<const void *>(&dequant_kernel<MLX4_G32>); break;
     case Q2_0: fn = reinterpret_cast<const void *>(&dequant_kernel<Q2_0>); break;
     case Q8_0: fn = reinterpret_cast<const void *>(&dequant_kernel<Q8_0>); break;
+    case Q4_K: fn = reinterpret_cast<const void *>(&dequant_kernel<Q4_K>); break;
     default: return hipErrorInvalidValue;
     }
     return hipLaunchKernel(fn, grid, block, args, 0, stream);

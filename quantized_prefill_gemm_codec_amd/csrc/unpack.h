@@ -18,8 +18,11 @@
 //   MLX4-G32  the same, one (s, b) per 32 weights
 //   Q2_0      w = (q - 1) * d, q=3 -> +2d  (v_pk_add_f16, v_pk_mul_f16)
 //   Q8_0      w = q * d, stored q + 128    (v_pk_add_f16, v_pk_mul_f16)
-// (Q2_0 values are exact; Q4_0 and MLX round once.  fp16 subnormals are kept:
-// an MLX weight with q = 0 is its bias, which may be subnormal.)
+//   Q4_K      w = d * (q sc) - dmin m      (v_pk_fma_f16 for the exact
+//             integer q sc, then v_fma_mix{lo,hi}_f16: fp16 d times fp16 q sc
+//             plus the fp32 value -dmin m, rounded once to fp16; see mix_pair)
+// (Q2_0 values are exact; Q4_0, MLX and Q4_K round once.  fp16 subnormals are
+// kept: an MLX weight with q = 0 is its bias, which may be subnormal.)
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -82,14 +85,53 @@ template <> struct LaneCodes<Q8_0> {
     u32x4 lo, hi;    // dwords 0..3 (sub-steps 0, 1) and 4..7 (sub-steps 2, 3)
     _Float16 d;
 };
+template <> struct LaneCodes<Q4_K> {
+    u32x4 c;
+    uint32_t scm;              // the lane's sub-block: sc | m << 8 (low 16 bits)
+    uint32_t dd;               // the super-block: fp16 d (low half), fp16 dmin (high half)
+    uint32_t sc2, o10, o6;     // from prepare_lane: fp16 pairs (sc, sc), (-1024 sc, ..), (-64 sc, ..)
+    float nm;                  // from prepare_lane: -dmin * m, exact in fp32
+};
 
-// Codec zero point: the weight factor is q - z.
+// Per-k-step values a lane derives once from its scale record before the
+// unpack (only Q4_K has any).
+template <int CODEC> __device__ __forceinline__ void prepare_lane(LaneCodes<CODEC> &lc)
+{
+    if constexpr (CODEC == Q4_K) {
+        const _Float16 sc = _Float16(float(lc.scm & 0xFFu));    // 0..63, exact
+        const f16x2 s2 = {sc, sc};
+        const f16x2 k10 = {_Float16(-1024.0f), _Float16(-1024.0f)};
+        const f16x2 k6 = {_Float16(-64.0f), _Float16(-64.0f)};
+        lc.sc2 = as_u32(s2);
+        lc.o10 = as_u32(s2 * k10);    // exact: 1024 * 63 = 64512 is a binary16
+        lc.o6 = as_u32(s2 * k6);
+        lc.nm = -(float(as_f16x2(lc.dd)[1]) * float((lc.scm >> 8) & 0xFFu));
+    }
+}
+
+// fp16 pair (d * qs.lo + nm, d * qs.hi + nm) with d the low half of `d`.
+// Written as fp16 -> fp32 widening, an fp32 FMA and a narrowing to fp16, which
+// the compiler selects as v_fma_mixlo_f16 / v_fma_mixhi_f16; on gfx950 those
+// take the fp16 operands and the fp32 addend as they are and round only the
+// fp16 result, so each weight is the correctly rounded value of the exact
+// d * (q sc) - dmin * m.  (Plain C rather than inline assembly, so that the
+// compiler sees the instructions and keeps its wait states against matrix
+// instructions still reading the registers they overwrite.)
+__device__ __forceinline__ uint32_t mix_pair(uint32_t d, uint32_t qs, float nm)
+{
+    const float df = float(as_f16x2(d)[0]);
+    const f16x2 q = as_f16x2(qs);
+    const f16x2 r = {_Float16(__builtin_fmaf(df, float(q[0]), nm)), _Float16(__builtin_fmaf(df, float(q[1]), nm))};
+    return as_u32(r);
+}
+
 template <int CODEC> struct CodeZero;
 template <> struct CodeZero<Q4_0> { static constexpr int v = 8; };
 template <> struct CodeZero<MLX4_G64> { static constexpr int v = 0; };
 template <> struct CodeZero<MLX4_G32> { static constexpr int v = 0; };
 template <> struct CodeZero<Q2_0> { static constexpr int v = 1; };
 template <> struct CodeZero<Q8_0> { static constexpr int v = 128; };   // codes are stored as q + 128
+template <> struct CodeZero<Q4_K> { static constexpr int v = 0; };
 
 // (2^E + q_even, 2^E + q_odd) -> exact fp16 (q_even - z, q_odd - z)
 template <int CODEC, int E>
@@ -106,7 +148,19 @@ template <int CODEC>
 __device__ __forceinline__ f16x8 unpack_substep(const LaneCodes<CODEC> &lc, int s, const Magics &mg)
 {
     f16x2 q[4];
-    if constexpr (CODEC == Q8_0) {
+    if constexpr (CODEC == Q4_K) {
+        // (2^E + q) sc - 2^E sc = q sc exactly (at most 15 * 63 = 945), then
+        // one rounding: d (q sc) - dmin m
+        const uint32_t w = lc.c[s], w8 = w >> 8;
+        const f16x2 sc2 = as_f16x2(lc.sc2), o10 = as_f16x2(lc.o10), o6 = as_f16x2(lc.o6);
+        const f16x2 qs0 = __builtin_elementwise_fma(as_f16x2((w & 0x000F000Fu) | mg.m1024), sc2, o10);
+        const f16x2 qs1 = __builtin_elementwise_fma(as_f16x2((w & 0x00F000F0u) | mg.m64), sc2, o6);
+        const f16x2 qs2 = __builtin_elementwise_fma(as_f16x2((w8 & 0x000F000Fu) | mg.m1024), sc2, o10);
+        const f16x2 qs3 = __builtin_elementwise_fma(as_f16x2((w8 & 0x00F000F0u) | mg.m64), sc2, o6);
+        const u32x4 r = {mix_pair(lc.dd, as_u32(qs0), lc.nm), mix_pair(lc.dd, as_u32(qs1), lc.nm),
+                         mix_pair(lc.dd, as_u32(qs2), lc.nm), mix_pair(lc.dd, as_u32(qs3), lc.nm)};
+        return __builtin_bit_cast(f16x8, r);
+    } else if constexpr (CODEC == Q8_0) {
         // sub-step s: dwords 2s (elements 0..3) and 2s + 1 (4..7), bytes at
         // bits 0, 16 (pair 0 / 2) and 8, 24 (pair 1 / 3 after one shift)
         const u32x4 h = (s < 2) ? lc.lo : lc.hi;
@@ -140,7 +194,7 @@ __device__ __forceinline__ f16x8 unpack_substep(const LaneCodes<CODEC> &lc, int 
             const f16x2 sc = {sb[0], sb[0]};
             const f16x2 bi = {sb[1], sb[1]};
             w = __builtin_elementwise_fma(q[p], sc, bi);
-        } else {
+        } else if constexpr (CODEC != Q4_K) {
             const f16x2 dd = {lc.d, lc.d};
             w = q[p] * dd;
         }
@@ -190,7 +244,7 @@ __device__ __forceinline__ _Float16 load_f16(__amdgpu_buffer_rsrc_t r, uint32_t 
 // range-checks, so the chunk-dependent part that goes in the scalar offset
 // must itself stay inside the plane (callers keep 0 <= t < ksteps).
 struct LaneOffsets {
-    uint32_t q, s;
+    uint32_t q, s, s2;    // s2: Q4_K's super-block record
 };
 
 template <int CODEC>
@@ -198,9 +252,14 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int rg, int groups, int lane
 {
     LaneOffsets o;
     const uint32_t i = uint32_t(lane & 31);
+    o.s2 = OOB;
     if (rg >= groups) {
         o.q = OOB;
         o.s = OOB;
+    } else if constexpr (CODEC == Q4_K) {
+        o.q = uint32_t(lane) * 16;
+        o.s = uint32_t(lane) * 2;
+        o.s2 = 512u + i * 4;
     } else if constexpr (CODEC == Q2_0) {
         o.q = uint32_t(lane) * 8;
         o.s = i * 2;
@@ -231,6 +290,12 @@ __device__ __forceinline__ LaneCodes<CODEC> load_lane(const PlaneRsrc &w, LaneOf
         lc.lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 2048, 0));
         lc.hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 2048 + 1024, 0));
         lc.d = load_f16(w.sc, o.s, chunk * 128);
+    } else if constexpr (CODEC == Q4_K) {
+        // record of (row group, super-block): u16 [4 k-steps][64 lanes], then u32 [32 rows]
+        lc.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 1024, 0));
+        const uint32_t rec = (uint32_t(rg) * uint32_t(ksteps >> 2) + uint32_t(t >> 2)) * 640u;
+        lc.scm = __builtin_amdgcn_raw_buffer_load_b16(w.sc, o.s, rec + uint32_t(t & 3) * 128u, 0);
+        lc.dd = __builtin_amdgcn_raw_buffer_load_b32(w.sc, o.s2, rec, 0);
     } else if constexpr (CODEC == Q2_0) {
         lc.c = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(w.qs, o.q, chunk * 512, 0));
         lc.d = load_f16(w.sc, o.s, (uint32_t(rg) * kb128 + uint32_t(t >> 1)) * 64);

@@ -68,7 +68,7 @@ def _same_value_bits(a16, b16):
 
 DEQ_SHAPES = [(1, 256, 256), (1, 40, 96), (1, 1000, 544), (2, 33, 192), (2, 300, 1024),
               (3, 37, 256), (3, 520, 1152), (4, 256, 256), (4, 40, 96), (4, 300, 544),
-              (5, 256, 256), (5, 33, 96), (5, 300, 544)]
+              (5, 256, 256), (5, 33, 96), (5, 300, 544), (6, 256, 256), (6, 40, 512), (6, 300, 768)]
 
 
 @pytest.mark.parametrize("codec,n,k", DEQ_SHAPES)
@@ -90,7 +90,52 @@ def test_dequant_keeps_subnormal_bias(torch):
     assert np.array_equal(got.view(np.uint16), np.repeat(b.view(np.uint16), 64, axis=1))
 
 
-@pytest.mark.parametrize("codec", [1, 2, 3])
+def test_dequant_q4_k_extreme_scales(torch):
+    """d and dmin from the largest normal to the smallest subnormal binary16:
+    every weight is the correctly rounded fp16 of d sc q - dmin m (one rounding)."""
+    pats = np.array([0x7BFF, 0x0001, 0x03FF, 0x0400, 0x3C00, 0x3555, 0xFBFF, 0x8001, 0x1234, 0x6A5A], np.uint16)
+    pairs = [(a, b) for a in pats for b in pats]
+    n, k = len(pairs), 512
+    rng = np.random.default_rng(61)
+    codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    sc = rng.integers(0, 64, (n, k // 32)).astype(np.uint8)
+    mn = rng.integers(0, 64, (n, k // 32)).astype(np.uint8)
+    d = np.repeat(np.array([a for a, _ in pairs], np.uint16).view(np.float16)[:, None], 2, axis=1)
+    dmin = np.repeat(np.array([b for _, b in pairs], np.uint16).view(np.float16)[:, None], 2, axis=1)
+    canon = synth.encode_q4_k(codes, sc, mn, d, dmin)
+    got = qg.qg_dequant(_weight(torch, 6, n, k, canon)).cpu().numpy()
+    want = oracle.dequant_f16_bits(6, canon, n, k).view(np.float16)
+    assert _same_value_bits(got, want)
+
+
+def _q4_k_tie_weights(n, k):
+    """d = 1 + 2^-10 and a tiny dmin: d sc q lands exactly halfway between two
+    binary16 values whenever sc q = 3 * 2^j, and -dmin m moves it just off the
+    tie.  One rounding of the exact value and a detour through fp32 (which
+    drops the tiny term, then rounds the tie to even) disagree there."""
+    rng = np.random.default_rng(62)
+    codes = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    sc = rng.integers(0, 64, (n, k // 32)).astype(np.uint8)
+    mn = rng.integers(1, 64, (n, k // 32)).astype(np.uint8)
+    d = np.full((n, k // 256), 0x3C01, np.uint16).view(np.float16)
+    dmin = np.where(np.arange(n)[:, None] % 2 == 0, 0x0001, 0x8001).astype(np.uint16)
+    dmin = np.repeat(dmin, k // 256, axis=1).view(np.float16)
+    return synth.encode_q4_k(codes, sc, mn, d, dmin)
+
+
+def test_q4_k_single_rounding_through_kernels(torch):
+    n = k = 256
+    canon = _q4_k_tie_weights(n, k)
+    want = oracle.dequant_f16_bits(6, canon, n, k).view(np.float16)
+    w = _weight(torch, 6, n, k, canon)
+    assert _same_value_bits(qg.qg_dequant(w).cpu().numpy(), want)
+    eye = torch.eye(k, dtype=torch.float16, device="cuda")
+    for m in (256, 128):      # large-tile DMA kernel, register-staged kernel
+        y = qg.qgemm_prefill(w, eye[:m].contiguous()).cpu().numpy()
+        assert _same_value_bits(y, want.T[:m])
+
+
+@pytest.mark.parametrize("codec", [1, 2, 3, 4, 5, 6])
 def test_identity_probe_through_gemm(torch, codec):
     """X = I: every output is one product with 1.0, so Y = W^T exactly."""
     n = k = 256
@@ -115,6 +160,9 @@ GEMM_SHAPES = [
     (4, 16, 256, 256), (4, 33, 200, 288), (4, 129, 136, 160), (4, 300, 264, 352), (4, 257, 1024, 256),
     # MLX4-G32 likewise
     (5, 16, 256, 256), (5, 33, 200, 288), (5, 129, 136, 160), (5, 300, 264, 352), (5, 257, 1024, 256),
+    # Q4_K likewise (K a multiple of the 256-weight super-block), and a split-k shape
+    (6, 16, 256, 256), (6, 33, 200, 512), (6, 129, 136, 256), (6, 300, 264, 768), (6, 257, 1024, 256),
+    (6, 48, 320, 2304),
 ]
 
 
@@ -179,7 +227,7 @@ def test_prefill_row_permutation_and_determinism(torch):
 
 
 HEADS_SHAPES = [(1, 2, 256, 128, 64), (2, 37, 192, 256, 64), (1, 300, 512, 256, 128), (3, 64, 384, 256, 96),
-                (4, 129, 256, 160, 32), (1, 2048, 8192, 128, 128)]
+                (4, 129, 256, 160, 32), (6, 37, 192, 256, 64), (1, 2048, 8192, 128, 128)]
 
 
 @pytest.mark.parametrize("codec,m,n,k,d", HEADS_SHAPES)
@@ -202,7 +250,8 @@ def test_prefill_heads_layout(torch, codec, m, n, k, d):
 # -------------------------------------------------------------------- SwiGLU --
 
 SWIGLU_SHAPES = [(2, 33, 200, 192), (2, 130, 256, 128), (2, 300, 264, 256), (1, 70, 136, 96), (3, 200, 128, 256),
-                 (4, 200, 128, 256), (4, 70, 136, 96), (5, 200, 128, 256), (5, 70, 136, 96)]
+                 (4, 200, 128, 256), (4, 70, 136, 96), (5, 200, 128, 256), (5, 70, 136, 96),
+                 (6, 300, 264, 256), (6, 70, 136, 512)]
 
 
 @pytest.mark.parametrize("codec,m,n,k", SWIGLU_SHAPES)
@@ -233,7 +282,8 @@ def test_swiglu_one_hot_probe(torch):
 
 # -------------------------------------------------------------------- GeGLU --
 
-GEGLU_SHAPES = [(2, 300, 264, 256), (2, 70, 136, 128), (1, 33, 200, 192), (4, 200, 128, 256), (3, 129, 256, 256)]
+GEGLU_SHAPES = [(2, 300, 264, 256), (2, 70, 136, 128), (1, 33, 200, 192), (4, 200, 128, 256), (3, 129, 256, 256),
+                (6, 129, 256, 256)]
 
 
 @pytest.mark.parametrize("codec,m,n,k", GEGLU_SHAPES)
@@ -268,7 +318,8 @@ GEMV_SHAPES = [(1, 1, 1000, 512), (1, 2, 256, 96), (1, 3, 520, 256), (1, 4, 200,
                (1, 17, 136, 192), (1, 64, 512, 512), (2, 1, 300, 256), (2, 4, 256, 512), (2, 33, 256, 128),
                (3, 1, 264, 512), (3, 3, 256, 256), (3, 64, 200, 384),
                (4, 1, 1000, 512), (4, 3, 264, 256), (4, 64, 200, 384),
-               (5, 1, 1000, 512), (5, 2, 264, 96), (5, 64, 200, 384)]
+               (5, 1, 1000, 512), (5, 2, 264, 96), (5, 64, 200, 384),
+               (6, 1, 1000, 512), (6, 2, 256, 1024), (6, 3, 264, 256), (6, 64, 200, 512)]
 
 
 @pytest.mark.parametrize("codec,m,n,k", GEMV_SHAPES)
