@@ -67,14 +67,23 @@ extern "C" {
  *                    in the high); w = d * sc[j] * q - dmin * m[j] over
  *                    sub-block j = weights 32j .. 32j + 31.  (The pages list
  *                    "Q4_K (GGUF Super-Blocks)" among the router's formats,
- *                    releases page v0.2; the layout is the public GGUF one.) */
+ *                    releases page v0.2; the layout is the public GGUF one.)
+ *  QG_CODEC_TERNARY_1_58  256-weight blocks of 54 bytes: fp16 d, then byte
+ *                    2 + j holds weights 5j .. 5j + 4 as base-3 digits t
+ *                    (weight 5j + i contributes t * 3^i; weight 255 is digit
+ *                    0 of byte 53); w = (t - 1) * d, so -d, 0 or +d.  Bytes
+ *                    above 242 (byte 53: above 2) are invalid (QG_ERR_CODE).
+ *                    (BitNet ternary: releases page v0.2, router formats;
+ *                    TERNARY_1_58 in the v0.3.0 registry.  The pages give no
+ *                    packing; 1.6875 bits per weight.) */
 typedef enum {
     QG_CODEC_Q4_0 = 1,
     QG_CODEC_MLX4_G64 = 2,
     QG_CODEC_Q2_0 = 3,
     QG_CODEC_Q8_0 = 4,
     QG_CODEC_MLX4_G32 = 5,
-    QG_CODEC_Q4_K = 6
+    QG_CODEC_Q4_K = 6,
+    QG_CODEC_TERNARY_1_58 = 7
 } qg_codec;
 
 typedef enum {
@@ -87,7 +96,8 @@ typedef enum {
     QG_ERR_ALIGN = -4,     /* pointer or stride not 16-byte aligned            */
     QG_ERR_MISMATCH = -5,  /* gate/up descriptors differ in codec, N or K      */
     QG_ERR_LAUNCH = -6,    /* the HIP launch itself failed                     */
-    QG_ERR_SIZE = -7       /* a host buffer is smaller than the format needs   */
+    QG_ERR_SIZE = -7,      /* a host buffer is smaller than the format needs   */
+    QG_ERR_CODE = -8       /* a canonical code byte outside the codec's range  */
 } qg_status;
 
 /* A packed weight matrix W [n, k] in the planar device format.
@@ -163,7 +173,8 @@ qg_status qg_canonical_size(int32_t codec, int64_t n, int64_t k, size_t *bytes);
 /* Host-side repack of canonical codec bytes into the planar device format
  * (comparison page, section 4: codes split from scales into 16-byte aligned
  * planes).  Bit moves only; every code, scale and bias keeps its value.
- *  canonical   host, canonical_bytes long (checked: QG_ERR_SIZE)
+ *  canonical   host, canonical_bytes long (checked: QG_ERR_SIZE); ternary
+ *              code bytes are range-checked first (QG_ERR_CODE, nothing written)
  *  qs, scales  host outputs of the sizes from qg_packed_sizes; fully written
  * Padding rows and columns get zero scales so that they decode to zero. */
 qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonical,

@@ -6,7 +6,7 @@ two share no code: this side decodes the canonical codec bytes itself
 (``qgemm_oracle.c``) in fp64 and contracts with a naive triple loop.
 
 Functions follow the plain definitions stated in ``qgemm_oracle.c``:
-exact fp64 decode of Q4_0 / MLX4-G64 / MLX4-G32 / Q2_0 / Q8_0 / Q4_K weights, ``ref = X * W^T`` with
+exact fp64 decode of Q4_0 / MLX4-G64 / MLX4-G32 / Q2_0 / Q8_0 / Q4_K / ternary weights, ``ref = X * W^T`` with
 ``k`` ascending into one fp64 accumulator, ``SiLU(g) * u`` and ``GELU(g) * u`` (tanh form) in fp64.
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 library routines (numpy's correctly rounded float16 conversion, BLAS fp64
@@ -24,7 +24,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "qgemm_oracle.c")
 LIB = os.path.join(HERE, "libqgemm_oracle.so")
 
-Q4_0, MLX4_G64, Q2_0, Q8_0, MLX4_G32, Q4_K = 1, 2, 3, 4, 5, 6
+Q4_0, MLX4_G64, Q2_0, Q8_0, MLX4_G32, Q4_K, TERNARY = 1, 2, 3, 4, 5, 6, 7
 
 _lib = None
 
@@ -101,6 +101,8 @@ def decode(codec: int, canon: np.ndarray, n: int, k: int, row0: int = 0, nrows: 
     canon = np.ascontiguousarray(canon, dtype=np.uint8)
     out = np.empty((nrows, k), dtype=np.float64)
     rc = lib().orc_decode_rows(codec, _ptr(canon), n, k, row0, nrows, _ptr(out))
+    if rc == -2:
+        raise ValueError("oracle decode found an invalid code byte")
     if rc:
         raise ValueError("oracle decode rejected codec/shape")
     return out
@@ -157,7 +159,7 @@ def canonical_rows(codec: int, canon: np.ndarray, n: int, k: int, rows: np.ndarr
     rows = np.asarray(rows, dtype=np.int64)
     if codec == Q4_0:
         return np.ascontiguousarray(canon.reshape(n, -1)[rows]).reshape(-1)
-    if codec in (Q2_0, Q8_0, Q4_K):
+    if codec in (Q2_0, Q8_0, Q4_K, TERNARY):
         return np.ascontiguousarray(canon.reshape(n, -1)[rows]).reshape(-1)
     group = 32 if codec == MLX4_G32 else 64
     codes = canon[: n * k // 2].reshape(n, -1)[rows]

@@ -46,6 +46,11 @@
  *     GGUF super-block of the public GGUF format description (see
  *     decode_q4_k_row); parity with the pages' own Q4_K kernel is therefore
  *     unpinned -- only the oracle's reading of that layout is pinned.
+ *   - Ternary 1.58-bit: the pages name the BitNet ternary format (releases
+ *     page v0.2 "Universal Quantization Router"; TERNARY_1_58 in the v0.3.0
+ *     registry) without a packing.  Reading: blocks of 256 weights in 54
+ *     bytes, fp16 d then five base-3 digits per byte (see
+ *     decode_ternary_row); parity with the pages' own kernel is unpinned.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fopenmp -fPIC -shared -lm
  * (no fast-math: every operation is a correctly rounded IEEE fp64 operation).
@@ -65,6 +70,7 @@
 #define ORC_Q8_0 4
 #define ORC_MLX4_G32 5
 #define ORC_Q4_K 6
+#define ORC_TERNARY 7
 
 /* ---------------------------------------------------------------- fp16 --- */
 
@@ -160,6 +166,7 @@ int orc_block_geometry(int codec, int64_t *weights, int64_t *bytes)
     case ORC_Q8_0:     *weights = 32;  *bytes = 34; return 1;
     case ORC_MLX4_G32: *weights = 32;  *bytes = 20; return 1;
     case ORC_Q4_K:     *weights = 256; *bytes = 144; return 1;
+    case ORC_TERNARY:  *weights = 256; *bytes = 54; return 1;
     default: return 0;
     }
 }
@@ -256,6 +263,33 @@ static void decode_q4_k_row(const uint8_t *row, int64_t k, double *w)
     }
 }
 
+/* Ternary 1.58-bit: blocks of 256 weights in 54 bytes -- fp16 d (bytes 0-1),
+ * then byte 2 + j holds weights 5 j .. 5 j + 4 as base-3 digits: weight
+ * 5 j + i has t = (byte / 3^i) mod 3 and value (t - 1) * d, so the digits
+ * 0, 1, 2 stand for -d, 0, +d.  The last weight (255) is digit 0 of byte 53.
+ * A byte above 242 (byte 53: above 2) is not a valid code; returns -1 then.
+ * Exact in fp64. */
+static int decode_ternary_row(const uint8_t *row, int64_t k, double *w)
+{
+    for (int64_t b = 0; b < k / 256; ++b) {
+        const uint8_t *blk = row + b * 54;
+        const double d = orc_f16_to_f64(rd_u16le(blk));
+        if (blk[53] > 2)
+            return -1;
+        for (int i = 0; i < 256; ++i) {
+            const int byte = blk[2 + i / 5];
+            if (byte > 242)
+                return -1;
+            int pw = 1;
+            for (int e = 0; e < i % 5; ++e)
+                pw *= 3;
+            const int t = (byte / pw) % 3;
+            w[b * 256 + i] = (double)(t - 1) * d;
+        }
+    }
+    return 0;
+}
+
 /* MLX4 row n with group size G (64 or 32): q = (word[n][k/8] >> 4*(k%8)) & 15,
  * g = k / G, w = q * s[n][g] + b[n][g].  Exact in fp64: q*s has at most 15
  * significant bits and the sum of two fp16-derived values spans far fewer
@@ -279,7 +313,7 @@ static void decode_mlx4_row(const uint8_t *codes, const uint8_t *scales,
 /* Decode rows [row0, row0 + nrows) of an [n, k] weight matrix held in the
  * canonical bytes `canon` into w[nrows][k].  The MLX stream is codes
  * (n*k/2 bytes), then scales (n*k/64 fp16), then biases (same).
- * Returns 0 on success, -1 on a bad codec or shape. */
+ * Returns 0 on success, -1 on a bad codec or shape, -2 on an invalid code. */
 int orc_decode_rows(int codec, const uint8_t *canon, int64_t n, int64_t k,
                     int64_t row0, int64_t nrows, double *w)
 {
@@ -298,6 +332,10 @@ int orc_decode_rows(int codec, const uint8_t *canon, int64_t n, int64_t k,
             decode_q8_0_row(canon + nn * (k / 32) * 34, k, wr);
         else if (codec == ORC_Q4_K)
             decode_q4_k_row(canon + nn * (k / 256) * 144, k, wr);
+        else if (codec == ORC_TERNARY) {
+            if (decode_ternary_row(canon + nn * (k / 256) * 54, k, wr))
+                return -2;
+        }
         else {
             const int64_t group = codec == ORC_MLX4_G32 ? 32 : 64;
             const uint8_t *codes = canon;

@@ -11,7 +11,10 @@ using namespace qg;
 
 namespace {
 
-bool valid_codec(int32_t c) { return c == Q4_0 || c == MLX4_G64 || c == Q2_0 || c == Q8_0 || c == MLX4_G32 || c == Q4_K; }
+bool valid_codec(int32_t c)
+{
+    return c == Q4_0 || c == MLX4_G64 || c == Q2_0 || c == Q8_0 || c == MLX4_G32 || c == Q4_K || c == TERNARY;
+}
 
 qg_status check_shape(int32_t codec, int64_t n, int64_t k)
 {
@@ -34,6 +37,8 @@ size_t canonical_size(int32_t codec, int64_t n, int64_t k)
         return size_t(n) * size_t(k / 32) * 34;
     if (codec == Q4_K)
         return size_t(n) * size_t(k / 256) * 144;
+    if (codec == TERNARY)
+        return size_t(n) * size_t(k / 256) * 54;
     const int64_t group = codec == MLX4_G32 ? 32 : 64;
     return size_t(n) * size_t(k / 2) + 2 * size_t(n) * size_t(k / group) * 2;
 }
@@ -64,6 +69,13 @@ inline int canonical_code(int32_t codec, const uint8_t *c, int64_t row, int64_t 
         const uint8_t b = blk[16 + 32 * (w / 64) + l % 32];
         return l < 32 ? (b & 0xF) : (b >> 4);
     }
+    if (codec == TERNARY) {
+        // base-3 digit kk % 5 of byte 2 + (kk % 256) / 5 (digits 0..2)
+        static const int pw[5] = {1, 3, 9, 27, 81};
+        const uint8_t *blk = c + (row * (k / 256) + kk / 256) * 54;
+        const int w = int(kk % 256);
+        return (blk[2 + w / 5] / pw[w % 5]) % 3;
+    }
     if (codec == Q2_0) {
         const uint8_t *blk = c + (row * (k / 128) + kk / 128) * 34;
         int i = int(kk % 128);
@@ -72,6 +84,76 @@ inline int canonical_code(int32_t codec, const uint8_t *c, int64_t row, int64_t 
     const uint8_t *word = c + (row * (k / 8) + kk / 8) * 4;
     int e = int(kk % 8);
     return (word[e / 2] >> (4 * (e % 2))) & 0xF;
+}
+
+// Fixed-point base-3 byte of up to five digits (digit 0 most significant):
+// ceil(256 v / 243) with v = sum_i t_i 3^(4 - i).
+inline uint8_t base3_fixed(const int *t, int nd)
+{
+    int v = 0;
+    for (int i = 0; i < 5; ++i)
+        v = v * 3 + (i < nd ? t[i] : 0);
+    return uint8_t((256 * v + 242) / 243);
+}
+
+bool ternary_codes_valid(const uint8_t *c, int64_t n, int64_t k)
+{
+    const int64_t blocks = n * (k / 256);
+    for (int64_t b = 0; b < blocks; ++b) {
+        const uint8_t *blk = c + b * 54;
+        for (int j = 2; j < 53; ++j)
+            if (blk[j] > 242)
+                return false;
+        if (blk[53] > 2)
+            return false;
+    }
+    return true;
+}
+
+// Ternary digit plane: per chunk A[64] u32, B[64] u16, T[32] u8 (planar.h).
+void pack_ternary_codes(const uint8_t *c, int64_t n, int64_t k, const Geometry &g, uint8_t *q)
+{
+    for (int64_t r = 0; r < g.groups; ++r)
+        for (int64_t t = 0; t < g.ksteps; ++t) {
+            uint8_t *chunk = q + (r * g.ksteps + t) * TERNARY_CHUNK;
+            for (int l = 0; l < 64; ++l) {
+                const int gh = l / 32, i = l % 32;
+                const int64_t row = r * 32 + i;
+                int dig[32];
+                for (int j = 0; j < 32; ++j) {
+                    const int64_t kk = t * 64 + gh * 32 + j;
+                    dig[j] = (row < n && kk < k) ? canonical_code(TERNARY, c, row, kk, k) : 1;   // pad: q = 0
+                }
+                uint8_t e[3], o[3];
+                for (int b = 0; b < 3; ++b) {
+                    int de[5], dd[5];
+                    for (int u = 0; u < 5; ++u) {
+                        de[u] = dig[2 * (5 * b + u)];
+                        dd[u] = dig[2 * (5 * b + u) + 1];
+                    }
+                    e[b] = base3_fixed(de, 5);
+                    o[b] = base3_fixed(dd, 5);
+                }
+                chunk[l * 4 + 0] = e[0];
+                chunk[l * 4 + 1] = o[0];
+                chunk[l * 4 + 2] = e[1];
+                chunk[l * 4 + 3] = o[1];
+                chunk[256 + l * 2 + 0] = e[2];
+                chunk[256 + l * 2 + 1] = o[2];
+            }
+            for (int tl = 0; tl < 32; ++tl) {     // tail byte of lanes 2 tl and 2 tl + 1
+                int td[4];
+                for (int h = 0; h < 2; ++h) {
+                    const int l = 2 * tl + h, gh = l / 32, i = l % 32;
+                    const int64_t row = r * 32 + i;
+                    for (int u = 0; u < 2; ++u) {
+                        const int64_t kk = t * 64 + gh * 32 + 30 + u;
+                        td[2 * h + u] = (row < n && kk < k) ? canonical_code(TERNARY, c, row, kk, k) : 1;
+                    }
+                }
+                chunk[384 + tl] = base3_fixed(td, 4);
+            }
+        }
 }
 
 }  // namespace
@@ -91,6 +173,7 @@ const char *qg_status_str(qg_status s)
     case QG_ERR_MISMATCH: return "gate and up weights differ in codec, N or K";
     case QG_ERR_LAUNCH: return "kernel launch failed";
     case QG_ERR_SIZE: return "host buffer smaller than the format requires";
+    case QG_ERR_CODE: return "canonical code byte outside the codec's range";
     }
     return "unknown status";
 }
@@ -130,6 +213,8 @@ qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonica
         return QG_ERR_NULL;
     if (canonical_bytes < canonical_size(codec, n, k))
         return QG_ERR_SIZE;
+    if (codec == TERNARY && !ternary_codes_valid(static_cast<const uint8_t *>(canonical), n, k))
+        return QG_ERR_CODE;
 
     const uint8_t *c = static_cast<const uint8_t *>(canonical);
     uint8_t *q = static_cast<uint8_t *>(qs);
@@ -143,6 +228,15 @@ qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonica
 
     memset(q, 0, size_t(g.qs_bytes));
     memset(s, 0, size_t(g.scale_bytes));
+
+    if (codec == TERNARY) {
+        pack_ternary_codes(c, n, k, g, q);
+        const int64_t nb = k / 256;
+        for (int64_t row = 0; row < n; ++row)
+            for (int64_t blk = 0; blk < nb; ++blk)
+                wr16(s + (((row / 32) * nb + blk) * 32 + row % 32) * 2, rd16(c + (row * nb + blk) * 54));
+        return QG_OK;
+    }
 
     for (int64_t r = 0; r < g.groups; ++r) {
         for (int64_t t = 0; t < g.ksteps; ++t) {

@@ -44,6 +44,19 @@
 //              sub-block 2 u + g (the 6-bit fields unpacked to bytes); bytes
 //              512..639 are u32 [32 rows], fp16 d low and fp16 dmin high.
 //              4.625 bits per weight (canonical: 4.5).
+//  * Ternary:  fp16 [N/32][K/256][32]    -- d of block t/4
+//
+// Ternary codes keep the canonical density (1.625 bits per weight of digits):
+// a (row group, k-step) chunk is 416 bytes -- u32 A[64 lanes], u16 B[64 lanes],
+// u8 T[32].  Lane l's 32 weights form pairs p = (j = 2p, 2p + 1); for p < 15
+// the even weight is digit p % 5 of byte E[p / 5] and the odd one digit p % 5
+// of byte O[p / 5], with A = E0 | O0 << 8 | E1 << 16 | O1 << 24 and
+// B = E2 | O2 << 8; weights 30, 31 are digits 2 (l & 1) and 2 (l & 1) + 1 of
+// T[l / 2].  Digits are t = q + 1 in {0, 1, 2}.  Each byte stores its (up to
+// five) digits in fixed-point base 3: byte = ceil(256 v / 243) with
+// v = sum_i t_i 3^(4 - i), so that digit i = ((byte 3^i) mod 256) 3 >> 8 --
+// every digit comes out with the same four 16-bit operations, two bytes (one
+// per register half) at a time.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -59,7 +72,9 @@
 
 namespace qg {
 
-enum Codec : int32_t { Q4_0 = 1, MLX4_G64 = 2, Q2_0 = 3, Q8_0 = 4, MLX4_G32 = 5, Q4_K = 6 };
+enum Codec : int32_t { Q4_0 = 1, MLX4_G64 = 2, Q2_0 = 3, Q8_0 = 4, MLX4_G32 = 5, Q4_K = 6, TERNARY = 7 };
+
+constexpr int TERNARY_CHUNK = 416;   // bytes of ternary digits per (row group, k-step)
 
 QG_HD inline bool is_mlx(int codec) { return codec == MLX4_G64 || codec == MLX4_G32; }
 
@@ -68,7 +83,7 @@ QG_HD inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 QG_HD inline int block_size(int codec)
 {
     return codec == Q4_0 ? 32 : codec == MLX4_G64 ? 64 : codec == Q2_0 ? 128 : codec == Q8_0 ? 32 : codec == MLX4_G32 ? 32
-         : codec == Q4_K ? 256 : 0;
+         : codec == Q4_K ? 256 : codec == TERNARY ? 256 : 0;
 }
 
 // bytes of codes a lane holds per chunk
@@ -85,7 +100,7 @@ QG_HD inline Geometry geometry(int codec, int64_t n, int64_t k)
     Geometry g;
     g.groups = ceil_div(n, QG_ROWS_PER_GROUP);
     g.ksteps = ceil_div(k, QG_KSTEP);
-    g.qs_bytes = g.groups * g.ksteps * 64 * lane_code_bytes(codec);
+    g.qs_bytes = codec == TERNARY ? g.groups * g.ksteps * TERNARY_CHUNK : g.groups * g.ksteps * 64 * lane_code_bytes(codec);
     if (codec == Q4_0 || codec == Q8_0)
         g.scale_bytes = g.groups * g.ksteps * 64 * 2;
     else if (codec == MLX4_G32)
@@ -94,6 +109,8 @@ QG_HD inline Geometry geometry(int codec, int64_t n, int64_t k)
         g.scale_bytes = g.groups * g.ksteps * 32 * 4;
     else if (codec == Q4_K)
         g.scale_bytes = g.groups * (g.ksteps / 4) * 640;
+    else if (codec == TERNARY)
+        g.scale_bytes = g.groups * (g.ksteps / 4) * 64;
     else
         g.scale_bytes = g.groups * ceil_div(k, 128) * 32 * 2;
     return g;

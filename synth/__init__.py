@@ -35,6 +35,11 @@ Canonical byte formats (the input contract both sides read):
   at bits 6-7, byte ``8 + j`` = ``m[j]`` plus the top two bits of ``m[j + 4]``;
   byte ``12 + j`` = low nibbles of ``sc[j + 4]`` and ``m[j + 4]``.  Weight
   value ``d * sc[j] * q - dmin * m[j]`` in sub-block ``j`` (32 weights).
+* Ternary 1.58-bit (the pages name the BitNet ternary format without a
+  packing; reading): 256 weights in 54 bytes: fp16 ``d`` (bytes 0-1), then
+  byte ``2 + j`` holding weights ``5 j .. 5 j + 4`` as base-3 digits
+  ``t = q + 1`` (weight ``5 j + i`` contributes ``t * 3**i``); weight 255 is
+  digit 0 of byte 53.  Weight value ``q * d`` with ``q`` in {-1, 0, +1}.
 
 Distributions and shapes follow the five workloads of the method: fp16
 activations ~N(0,1); Q4_0 scales ~U(0.005, 0.02) with codes ~U{0..15}; MLX
@@ -43,7 +48,9 @@ scales ~U(0.002, 0.01), biases ~N(0, 0.02), codes ~U{0..15}; Q2_0 scales
 (a next-step codec, not one of the five) uses codes ~U{-127..127} and scales
 ~U(0.0005, 0.0015), which keeps its weights in the Q4_0 workload's range.
 The Q4_K workloads (next-step codec) draw codes ~U{0..15}, sub-block scales
-and mins ~U{0..63} and super-block d, dmin ~U(0.0001, 0.0004).
+and mins ~U{0..63} and super-block d, dmin ~U(0.0001, 0.0004).  The ternary
+workloads draw q = -1, 0, +1 with probabilities 0.345, 0.31, 0.345 (absmean
+rounding of Gaussian weights gives about 0.31 zeros) and d ~U(0.01, 0.03).
 
 Random streams: numpy PCG64 seeded from ``SeedSequence([seed, tensor_id])``
 so every tensor of every workload has its own reproducible stream.
@@ -60,11 +67,13 @@ CODEC_Q2_0 = 3
 CODEC_Q8_0 = 4
 CODEC_MLX4_G32 = 5
 CODEC_Q4_K = 6
+CODEC_TERNARY = 7
 
 CODEC_NAMES = {CODEC_Q4_0: "q4_0", CODEC_MLX4_G64: "mlx4_g64", CODEC_Q2_0: "q2_0", CODEC_Q8_0: "q8_0",
-               CODEC_MLX4_G32: "mlx4_g32", CODEC_Q4_K: "q4_k"}
+               CODEC_MLX4_G32: "mlx4_g32", CODEC_Q4_K: "q4_k",
+               CODEC_TERNARY: "ternary"}
 # weights per block (scale group) along K
-BLOCK = {CODEC_Q4_0: 32, CODEC_MLX4_G64: 64, CODEC_Q2_0: 128, CODEC_Q8_0: 32, CODEC_MLX4_G32: 32, CODEC_Q4_K: 256}
+BLOCK = {CODEC_Q4_0: 32, CODEC_MLX4_G64: 64, CODEC_Q2_0: 128, CODEC_Q8_0: 32, CODEC_MLX4_G32: 32, CODEC_Q4_K: 256, CODEC_TERNARY: 256}
 
 BASE_SEED = 0x51C0DEC0
 
@@ -93,6 +102,8 @@ def canonical_bytes(codec: int, n: int, k: int) -> int:
         return n * (k // 32) * 34
     if codec == CODEC_Q4_K:
         return n * (k // 256) * 144
+    if codec == CODEC_TERNARY:
+        return n * (k // 256) * 54
     raise ValueError(codec)
 
 
@@ -169,6 +180,37 @@ def encode_q4_k(codes: np.ndarray, sc: np.ndarray, mn: np.ndarray, d: np.ndarray
     return out.reshape(-1)
 
 
+def encode_ternary(q: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Lay out ternary values q [n, k] (-1, 0, +1) and fp16 scales [n, k/256] as
+    54-byte blocks of base-3 digits."""
+    n, k = q.shape
+    nb = k // 256
+    t = (q.astype(np.int64) + 1).reshape(n, nb, 256)
+    padded = np.zeros((n, nb, 260), dtype=np.int64)
+    padded[:, :, :256] = t
+    digits = padded.reshape(n, nb, 52, 5)
+    packed = np.zeros((n, nb, 52), dtype=np.int64)
+    for i in range(5):
+        packed += digits[:, :, :, i] * 3 ** i
+    out = np.empty((n, nb, 54), dtype=np.uint8)
+    out[:, :, 0:2] = d.astype("<f2").reshape(n, nb, 1).view(np.uint8).reshape(n, nb, 2)
+    out[:, :, 2:54] = packed.astype(np.uint8)
+    return out.reshape(-1)
+
+
+TERNARY_PROBS = (0.345, 0.31, 0.345)
+
+
+def gen_ternary(n: int, k: int, seed: int, tensor_id: int = T_W,
+                d_range=(0.01, 0.03), probs=TERNARY_PROBS) -> np.ndarray:
+    rng = _rng(seed, tensor_id)
+    u = rng.random((n, k))
+    edges = np.cumsum(np.asarray(probs, dtype=np.float64))[:-1]
+    q = np.searchsorted(edges, u, side="right").astype(np.int8) - 1
+    d = fp16_uniform(rng, d_range[0], d_range[1], (n, k // 256))
+    return encode_ternary(q, d)
+
+
 def gen_q4_0(n: int, k: int, seed: int, tensor_id: int = T_W,
              d_range=(0.005, 0.02)) -> np.ndarray:
     rng = _rng(seed, tensor_id)
@@ -228,7 +270,7 @@ def gen_q4_k(n: int, k: int, seed: int, tensor_id: int = T_W,
 
 
 GEN = {CODEC_Q4_0: gen_q4_0, CODEC_MLX4_G64: gen_mlx4, CODEC_Q2_0: gen_q2_0, CODEC_Q8_0: gen_q8_0,
-       CODEC_MLX4_G32: gen_mlx4_g32, CODEC_Q4_K: gen_q4_k}
+       CODEC_MLX4_G32: gen_mlx4_g32, CODEC_Q4_K: gen_q4_k, CODEC_TERNARY: gen_ternary}
 
 
 def gen_weight(codec: int, n: int, k: int, seed: int, tensor_id: int = T_W) -> np.ndarray:
@@ -289,4 +331,9 @@ WORKLOADS = {
     "q4_k_prefill_2048x2048x8192": Workload("q4_k_prefill_2048x2048x8192", "prefill", CODEC_Q4_K, 2048, 2048, 8192,
                                             BASE_SEED + 10),
     "q4_k_gemv_1x4096x14336": Workload("q4_k_gemv_1x4096x14336", "gemv", CODEC_Q4_K, 1, 4096, 14336, BASE_SEED + 11),
+    # next-step codec: BitNet ternary (base-3, 1.6875 bits per weight) on the same two shapes
+    "ternary_prefill_2048x2048x8192": Workload("ternary_prefill_2048x2048x8192", "prefill", CODEC_TERNARY, 2048, 2048,
+                                               8192, BASE_SEED + 12),
+    "ternary_gemv_1x4096x14336": Workload("ternary_gemv_1x4096x14336", "gemv", CODEC_TERNARY, 1, 4096, 14336,
+                                          BASE_SEED + 13),
 }

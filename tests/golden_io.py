@@ -4,7 +4,7 @@ import re
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
-_CODECS = {"q4_0": 1, "mlx4_g64": 2, "q2_0": 3, "q8_0": 4, "mlx4_g32": 5, "q4_k": 6}
+_CODECS = {"q4_0": 1, "mlx4_g64": 2, "q2_0": 3, "q8_0": 4, "mlx4_g32": 5, "q4_k": 6, "ternary": 7}
 
 
 def _expand(tokens, conv):

@@ -41,12 +41,15 @@ def test_library_exports_every_declared_symbol():
 
 @pytest.mark.parametrize("codec,n,k", [(1, 8192, 2048), (1, 40, 96), (2, 14336, 4096), (3, 4096, 4096), (3, 33, 128),
                                      (4, 8192, 2048), (4, 40, 96), (5, 14336, 4096), (5, 33, 96),
-                                     (6, 8192, 2048), (6, 40, 256)])
+                                     (6, 8192, 2048), (6, 40, 256), (7, 8192, 2048), (7, 40, 512)])
 def test_sizes(codec, n, k):
     qs, sc = qg.qg_packed_sizes(codec, n, k)
     groups, ksteps = -(-n // 32), -(-k // 64)
-    code_bytes = {1: 16, 2: 16, 3: 8, 4: 32, 5: 16, 6: 16}[codec]
-    assert qs == groups * ksteps * 64 * code_bytes
+    if codec == 7:
+        assert qs == groups * ksteps * 416                    # 1.625 bits per weight of digits
+    else:
+        code_bytes = {1: 16, 2: 16, 3: 8, 4: 32, 5: 16, 6: 16}[codec]
+        assert qs == groups * ksteps * 64 * code_bytes
     if codec in (1, 4):
         assert sc == groups * ksteps * 64 * 2
     elif codec == 2:
@@ -55,13 +58,49 @@ def test_sizes(codec, n, k):
         assert sc == groups * ksteps * 64 * 4
     elif codec == 6:
         assert sc == groups * (k // 256) * 640
+    elif codec == 7:
+        assert sc == groups * (k // 256) * 64
     else:
         assert sc == groups * (k // 128) * 32 * 2
     assert qg.qg_canonical_size(codec, n, k) == synth.canonical_bytes(codec, n, k)
 
 
+def _ternary_digits(byte):
+    """Digits (t0..t4, t0 most significant) of fixed-point base-3 bytes:
+    byte = ceil(256 v / 243) inverts as v = floor(243 byte / 256)."""
+    v = (np.asarray(byte, np.int64) * 243) // 256
+    return np.stack([(v // 3 ** (4 - i)) % 3 for i in range(5)], axis=-1)
+
+
+def _read_ternary_planar(n, k, qs, sc):
+    groups, ksteps = -(-n // 32), -(-k // 64)
+    ch = qs.reshape(groups, ksteps, 416)
+    a = ch[:, :, :256].reshape(groups, ksteps, 64, 4)
+    b = ch[:, :, 256:384].reshape(groups, ksteps, 64, 2)
+    tail = ch[:, :, 384:].repeat(2, axis=2)                     # [groups, ksteps, 64]: byte of lane l // 2
+    even = [_ternary_digits(x) for x in (a[..., 0], a[..., 2], b[..., 0])]
+    odd = [_ternary_digits(x) for x in (a[..., 1], a[..., 3], b[..., 1])]
+    td = _ternary_digits(tail)
+    lane = np.arange(64)
+    t = np.zeros((groups, ksteps, 64, 32), np.int64)
+    for p in range(15):
+        t[..., 2 * p] = even[p // 5][..., p % 5]
+        t[..., 2 * p + 1] = odd[p // 5][..., p % 5]
+    t[..., 30] = np.take_along_axis(td, (2 * (lane & 1))[None, None, :, None], axis=-1)[..., 0]
+    t[..., 31] = np.take_along_axis(td, (2 * (lane & 1) + 1)[None, None, :, None], axis=-1)[..., 0]
+    # lane 32 g + i: row 32 r + i, k = 64 t + 32 g + j
+    codes = t.reshape(groups, ksteps, 2, 32, 32).transpose(0, 3, 1, 2, 4).reshape(groups * 32, ksteps * 64)
+    codes = codes[:n, :k] - 1
+    d = sc.view(np.float16).reshape(groups, k // 256, 32).astype(np.float64)
+    rr, kk = np.arange(n), np.arange(k)
+    scale = d[rr[:, None] // 32, kk[None, :] // 256, rr[:, None] % 32]
+    return codes, scale, None
+
+
 def _read_planar(codec, n, k, qs, sc):
     """Independent reader of the planar layout -> (codes [n,k], scale, bias)."""
+    if codec == 7:
+        return _read_ternary_planar(n, k, qs, sc)
     groups, ksteps = -(-n // 32), -(-k // 64)
     cb = {1: 16, 2: 16, 3: 8, 4: 32, 5: 16, 6: 16}[codec]
     if codec == 4:
@@ -131,7 +170,7 @@ def _read_planar(codec, n, k, qs, sc):
 def _value(codec, codes, scale, bias):
     if codec == 1:
         return (codes - 8) * scale
-    if codec == 4:
+    if codec in (4, 7):
         return codes * scale
     if codec in (2, 5, 6):
         return codes * scale + bias
@@ -140,7 +179,7 @@ def _value(codec, codes, scale, bias):
 
 @pytest.mark.parametrize("codec,n,k", [(1, 40, 96), (1, 64, 64), (2, 33, 192), (3, 37, 256), (3, 32, 128),
                                      (4, 40, 96), (4, 64, 128), (5, 33, 96), (5, 64, 256), (6, 40, 512),
-                                     (6, 64, 256)])
+                                     (6, 64, 256), (7, 40, 512), (7, 64, 256), (7, 33, 768)])
 def test_pack_roundtrip_random(codec, n, k):
     canon = synth.gen_weight(codec, n, k, 77)
     qs, sc = qg.qg_pack_host(codec, n, k, canon)
@@ -167,6 +206,19 @@ def test_pack_padding_decodes_to_zero():
     d = sc.view(np.float16).reshape(2, 2, 2, 32)
     assert np.all(d[1, :, :, 8:] == 0)          # rows 40..63
     assert np.all(d[:, 1, 1, :] == 0)           # k 96..127 (block 3)
+
+
+def test_pack_rejects_invalid_ternary_bytes():
+    canon = synth.gen_weight(7, 4, 256, 3)
+    canon[54 + 2 + 17] = 243                                 # row 1, a five-digit byte
+    qs = np.full(qg.qg_packed_sizes(7, 4, 256)[0], 0xAB, np.uint8)
+    L = qg.lib()
+    sc = np.zeros(qg.qg_packed_sizes(7, 4, 256)[1], np.uint8)
+    assert L.qg_pack_host(7, 4, 256, canon.ctypes.data, canon.size, qs.ctypes.data, sc.ctypes.data) == -8
+    assert np.all(qs == 0xAB)                                # nothing written
+    canon[54 + 2 + 17] = 0
+    canon[53] = 3                                            # the one-digit byte
+    assert L.qg_pack_host(7, 4, 256, canon.ctypes.data, canon.size, qs.ctypes.data, sc.ctypes.data) == -8
 
 
 def test_pack_errors():

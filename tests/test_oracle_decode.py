@@ -8,6 +8,9 @@
   144-byte super-blocks with 6-bit sub-block fields (public GGUF layout, a
   reading).  They fix the offsets, signs, nibble / bit order, block strides and
   row strides.
+* Ternary 1.58-bit (base-3 digits, five per byte, a reading) is further
+  pinned by an exhaustive sweep of all 243 valid byte values in every byte
+  position against repeated division by 3, and by rejection of invalid bytes.
 * Q4_K is further pinned by a special case that reduces to the fixture-pinned
   Q4_0 decode, an exhaustive sweep of its 6-bit fields and exact rational
   arithmetic at extreme scale ratios.
@@ -117,6 +120,41 @@ def test_q4_k_decode_exact_at_extreme_ratios():
             assert Fraction(w[r, kk]) == exact
 
 
+def test_ternary_geometry():
+    weights, nbytes = oracle.block_geometry(oracle.TERNARY)
+    assert (weights, nbytes) == (256, 54)
+    assert nbytes * 8 / weights == 1.6875          # log2(3) = 1.585 for the digits alone
+
+
+def test_ternary_all_byte_values_exhaustive():
+    # byte values 0..242 spread over the 51 five-digit bytes of 5 rows; weight
+    # 255 (digit 0 of byte 53) cycles through 0..2
+    n, k = 5, 256
+    vals = np.arange(n * 51) % 243
+    canon = np.zeros((n, 54), np.uint8)
+    canon[:, 0:2] = np.array([0x3C00], np.uint16).view(np.uint8)   # d = 1
+    canon[:, 2:53] = vals.reshape(n, 51)
+    canon[:, 53] = np.arange(n) % 3
+    w = oracle.decode(oracle.TERNARY, canon.reshape(-1), n, k)
+    want = np.empty((n, k))
+    for r in range(n):
+        for j in range(51):
+            v = int(canon[r, 2 + j])
+            for i in range(5):
+                v, t = divmod(v, 3)
+                want[r, 5 * j + i] = t - 1
+        want[r, 255] = int(canon[r, 53]) - 1
+    assert np.array_equal(w, want)
+
+
+@pytest.mark.parametrize("pos,val", [(2, 243), (30, 255), (53, 3)])
+def test_ternary_rejects_invalid_bytes(pos, val):
+    canon = np.zeros(54, np.uint8)
+    canon[pos] = val
+    with pytest.raises(ValueError):
+        oracle.decode(oracle.TERNARY, canon, 1, 256)
+
+
 def test_decode_rejects_bad_shapes():
     with pytest.raises(ValueError):
         oracle.decode(oracle.Q4_0, np.zeros(18, np.uint8), 1, 48)
@@ -141,7 +179,7 @@ def _random_canon(codec, n, k, seed):
     return synth.gen_weight(codec, n, k, seed)
 
 
-@pytest.mark.parametrize("codec", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("codec", [1, 2, 3, 4, 5, 6, 7])
 def test_dequant_f16_matches_numpy_rounding(codec):
     n, k = 16, 512
     canon = _random_canon(codec, n, k, 99)
@@ -215,6 +253,23 @@ def test_generator_q4_k_encoding_matches_decode():
     mm = np.repeat(dmin.astype(np.float64), 256, axis=1)
     want = dd * np.repeat(sc, 32, axis=1) * codes - mm * np.repeat(mn, 32, axis=1)
     assert np.array_equal(w, want)
+
+
+def test_generator_ternary_encoding_matches_decode():
+    rng = np.random.default_rng(10)
+    n, k = 3, 768
+    q = rng.integers(-1, 2, (n, k)).astype(np.int8)
+    d = rng.uniform(0.01, 0.03, (n, k // 256)).astype(np.float16)
+    w = oracle.decode(7, synth.encode_ternary(q, d), n, k)
+    assert np.array_equal(w, q.astype(np.float64) * np.repeat(d.astype(np.float64), 256, axis=1))
+
+
+def test_generator_ternary_frequencies():
+    n, k = 64, 4096
+    w = oracle.decode(7, synth.gen_ternary(n, k, 12), n, k)
+    q = np.sign(w).astype(np.int64) + 1
+    freq = np.bincount(q.reshape(-1), minlength=3) / q.size
+    assert np.allclose(freq, synth.TERNARY_PROBS, atol=0.005)
 
 
 def test_generator_q2_0_code_frequencies():

@@ -31,7 +31,7 @@ def _exact_ref(x16, w):
     return out
 
 
-@pytest.mark.parametrize("codec,k", [(1, 64), (2, 128), (3, 128), (4, 64), (5, 64), (6, 256)])
+@pytest.mark.parametrize("codec,k", [(1, 64), (2, 128), (3, 128), (4, 64), (5, 64), (6, 256), (7, 256)])
 def test_matmul_exact_bruteforce(codec, k):
     m, n = 3, 5
     x = synth.gen_x(m, k, 17)
