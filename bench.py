@@ -43,7 +43,8 @@ HEADLINE = "q4_0_prefill_2048x2048x8192"
 SECONDARY = ["mlx4_swiglu_2048x4096x14336", "q2_0_prefill_2048x4096x4096",
              "q4_0_gemv_1x4096x14336", "q4_0_gemv_64x4096x14336", "q8_0_prefill_2048x2048x8192",
              "mlx4_geglu_2048x4096x14336", "q4_0_qproj_heads_2048x4096x4096", "mlx4_g32_prefill_2048x2048x8192",
-             "q4_k_prefill_2048x2048x8192", "q4_k_gemv_1x4096x14336"]
+             "q4_k_prefill_2048x2048x8192", "q4_k_gemv_1x4096x14336",
+             "ternary_prefill_2048x2048x8192", "ternary_gemv_1x4096x14336"]
 KERNEL_SOURCES = ["gemm.hip", "gemv.hip", "unpack.h", "planar.h", "lds_dma.h"]
 
 

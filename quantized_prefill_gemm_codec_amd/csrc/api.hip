@@ -10,7 +10,10 @@ namespace {
 constexpr int64_t LIMIT = int64_t(1) << 31;   // bytes per buffer, and M/N/K
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-bool valid_codec(int32_t c) { return c == Q4_0 || c == MLX4_G64 || c == Q2_0 || c == Q8_0 || c == MLX4_G32 || c == Q4_K; }
+bool valid_codec(int32_t c)
+{
+    return c == Q4_0 || c == MLX4_G64 || c == Q2_0 || c == Q8_0 || c == MLX4_G32 || c == Q4_K || c == TERNARY;
+}
 
 qg_status check_weight(const qg_weight *w)
 {

@@ -340,11 +340,15 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     constexpr int FM = TM / 32, FN = TN / 32;
     constexpr int NMAT = GLU ? 2 : 1;
     constexpr int RG = BN / 32;                            // row groups per matrix per tile
+    constexpr bool TERN = CODEC == TERNARY;
     constexpr int CB = CODEC == Q2_0 ? 8 : CODEC == Q8_0 ? 32 : 16;   // code bytes per lane per chunk
-    constexpr int WCH = 64 * CB;                           // bytes per (row group, k-step) chunk
+    // LDS bytes per (row group, k-step) chunk; ternary chunks (416 bytes in
+    // memory) arrive by two dword DMA instructions into a 512-byte slot
+    constexpr int WCH = TERN ? 512 : 64 * CB;
+    constexpr int WDMA = TERN ? 256 : 1024;                // chunk bytes per code DMA instruction
     // scale bytes staged per (row group, k-step); Q4_K: the k-step's u16 (sc, m)
     // lane records, then the super-block's (d, dmin) row records
-    constexpr int SB = CODEC == Q2_0 ? 64 : (CODEC == MLX4_G32 || CODEC == Q4_K) ? 256 : 128;
+    constexpr int SB = (CODEC == Q2_0 || TERN) ? 64 : (CODEC == MLX4_G32 || CODEC == Q4_K) ? 256 : 128;
     constexpr int X_OFF = 0, X_BYTES = BM * 128;
     constexpr int W_OFF = X_BYTES, W_BYTES = NMAT * RG * WCH;
     constexpr int S_OFF = W_OFF + W_BYTES, S_BYTES = NMAT * RG * SB;
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     constexpr int PPITCH = BN * 4 + 16;                    // fp32 partial tile row pitch (WK > 1)
     constexpr int EPI_BYTES = WK == 1 ? BM * BN * 2 : WK * BM * PPITCH;
     constexpr int LDS_BYTES = NSTAGE * STAGE > EPI_BYTES ? NSTAGE * STAGE : EPI_BYTES;
-    constexpr int NX = X_BYTES / 1024, NWI = W_BYTES / 1024, NSI = (S_BYTES + 255) / 256;   // DMA ops per slice
+    constexpr int NX = X_BYTES / 1024, NWI = W_BYTES / WDMA, NSI = (S_BYTES + 255) / 256;   // DMA ops per slice
     constexpr int XPW = NX / NWT, WPW = (NWI + NWT - 1) / NWT, SPW = (NSI + NWT - 1) / NWT;
     constexpr int VMIN = XPW + NWI / NWT + NSI / NWT;       // fewest DMA ops any wave issues per stage
     constexpr int VWAIT = (AHEAD - 1) * VMIN;               // DMA ops that may stay in flight
@@ -407,6 +411,16 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
 #pragma unroll
     for (int u = 0; u < WPW; ++u) {
         const int j = wr + NWT * u;
+        if constexpr (TERN) {
+            // instruction j: bytes [256 (j & 1), + 256) of chunk j / 2 (valid below 416)
+            const int c = j >> 1, rg = c % RG;
+            const uint32_t lo = uint32_t(j & 1) * 256u + uint32_t(lane) * 4u;
+            wmat[u] = c / RG;
+            wv[u] = (j < NWI && rg0 + rg < a.groups && lo < uint32_t(TERNARY_CHUNK))
+                        ? uint32_t(rg0 + rg) * uint32_t(a.ksteps) * uint32_t(TERNARY_CHUNK) + lo
+                        : OOB;
+            continue;
+        }
         const int c = CB == 16 ? j : CB == 32 ? (j >> 1) : 2 * j + (lane >> 5);
         const int rg = c % RG;
         const uint32_t lo = CB == 16 ? uint32_t(lane) * 16
@@ -427,6 +441,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
         const int rg = c % RG;
         smat[u] = (256 * j / SB) / RG;              // wave-uniform: chunks never straddle matrices
         const uint32_t pitch = CODEC == Q2_0   ? uint32_t(a.kb128) * 64u
+                             : TERN          ? uint32_t(a.ksteps >> 2) * 64u   // one record per 4 k-steps
                              : CODEC == Q4_K ? uint32_t(a.ksteps) * 160u      // 640 B per 4 k-steps
                                              : uint32_t(a.ksteps) * uint32_t(SB);
         // Q4_K: bytes [0, 128) of a chunk come from the k-step's lane records
@@ -450,13 +465,19 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
 #pragma unroll
         for (int u = 0; u < WPW; ++u) {
             const int j = wr + NWT * u;
-            if (j < NWI)
-                dma_b128(wmat[u] ? q1 : q0, in ? wv[u] : OOB, uint32_t(t) * WCH, base + W_OFF + uint32_t(j * 1024));
+            if (j < NWI) {
+                if constexpr (TERN)
+                    dma_b32(wmat[u] ? q1 : q0, in ? wv[u] : OOB, uint32_t(t) * uint32_t(TERNARY_CHUNK),
+                            base + W_OFF + uint32_t(j * 256));
+                else
+                    dma_b128(wmat[u] ? q1 : q0, in ? wv[u] : OOB, uint32_t(t) * WCH, base + W_OFF + uint32_t(j * 1024));
+            }
         }
 #pragma unroll
         for (int u = 0; u < SPW; ++u) {
             const int j = wr + NWT * u;
             const uint32_t so = CODEC == Q2_0   ? uint32_t(t >> 1) * 64u
+                              : TERN          ? uint32_t(t >> 2) * 64u
                               : CODEC == Q4_K ? uint32_t(t >> 2) * 640u
                                               : uint32_t(t) * uint32_t(SB);
             uint32_t v = in ? sv[u] : OOB;
@@ -489,7 +510,14 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
                 const int c = mt * RG + wn * FN + fn;
                 const char *wp = st + W_OFF + c * WCH + lane * (CB == 32 ? 16 : CB);
                 const char *sp = st + S_OFF + c * SB;
-                if constexpr (CODEC == Q4_K) {
+                if constexpr (TERN) {
+                    const char *cp = st + W_OFF + c * WCH;
+                    cw[mt][fn].a = *reinterpret_cast<const uint32_t *>(cp + lane * 4);
+                    cw[mt][fn].b = *reinterpret_cast<const unsigned short *>(cp + 256 + lane * 2);
+                    cw[mt][fn].tl = *reinterpret_cast<const unsigned char *>(cp + 384 + (lane >> 1));
+                    cw[mt][fn].d = *reinterpret_cast<const _Float16 *>(sp + i * 2);
+                    prepare_lane<CODEC>(cw[mt][fn]);
+                } else if constexpr (CODEC == Q4_K) {
                     cw[mt][fn].c = *reinterpret_cast<const u32x4 *>(wp);
                     cw[mt][fn].scm = *reinterpret_cast<const unsigned short *>(sp + lane * 2);
                     cw[mt][fn].dd = *reinterpret_cast<const uint32_t *>(sp + 128 + i * 4);
@@ -769,6 +797,7 @@ hipError_t launch_gemm(const GemmProblem &p, int glu, hipStream_t stream)
     case Q2_0: return launch_codec<Q2_0>(p, glu, stream);
     case Q8_0: return launch_codec<Q8_0>(p, glu, stream);
     case Q4_K: return launch_codec<Q4_K>(p, glu, stream);
+    case TERNARY: return launch_codec<TERNARY>(p, glu, stream);
     }
     return hipErrorInvalidValue;
 }

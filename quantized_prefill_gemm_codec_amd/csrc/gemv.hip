@@ -58,6 +58,8 @@ __device__ __forceinline__ void slice_correction(const u32x4 *chunks, float *out
     }
     if constexpr (CODEC == Q8_0) {
         out[0] = -1152.0f * ((sp[0] + sp[1]) + (sp[2] + sp[3]));
+    } else if constexpr (CODEC == TERNARY) {
+        out[0] = -1025.0f * ((sp[0] + sp[1]) + (sp[2] + sp[3]));
     } else if constexpr (CODEC == Q4_0) {
         out[0] = -1032.0f * (sp[0] + sp[2]) - 72.0f * (sp[1] + sp[3]);
     } else if constexpr (CODEC == MLX4_G64 || CODEC == MLX4_G32 || CODEC == Q4_K) {
@@ -78,13 +80,27 @@ __device__ __forceinline__ void slice_correction(const u32x4 *chunks, float *out
 //   Q4_0 / MLX4 / Q4_K: d[0] (fields at bits 0, 8 -> factor 1), d[1] (bits 4, 12 -> 16)
 //   Q2_0:         d[p] (fields at bits 2p, 8 + 2p -> factor 4^p), p = 0..3
 //   Q8_0:         d[0] (bytes at bits 0, 8 -> factor 1; stored q + 128)
+//   ternary:      d[0] (digits t = q + 1 extracted to the low bits first)
 // block_sum then removes the 1024 offsets (and the codec zero point) with the
 // precomputed X term: sum_k (q_k - z) x_k = sum_c d[c] / 2^f_c + corr.
 template <int CODEC, int MM>
 __device__ __forceinline__ void slice_dots(const LaneCodes<CODEC> &lc, const u32x4 *const (&xrow)[MM],
                                            uint32_t magic, float (&d)[4][MM])
 {
-    if constexpr (CODEC == Q8_0) {
+    if constexpr (CODEC == TERNARY) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int p = 4 * s + u;
+                const uint32_t r = p < 5 ? lc.r0 : p < 10 ? lc.r1 : p < 15 ? lc.r2 : lc.r3;
+                const uint32_t pw = p % 5 == 0 ? 1u : p % 5 == 1 ? 3u : p % 5 == 2 ? 9u : p % 5 == 3 ? 27u : 81u;
+                const uint32_t h = ternary_digits(r, p == 15 ? lc.m3 : pw | (pw << 16));
+#pragma unroll
+                for (int mr = 0; mr < MM; ++mr)
+                    d[0][mr] = __builtin_amdgcn_fdot2(as_f16x2(h), as_f16x2(xrow[mr][s][u]), d[0][mr], false);
+            }
+    } else if constexpr (CODEC == Q8_0) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const u32x4 h = (s < 2) ? lc.lo : lc.hi;
@@ -158,7 +174,7 @@ __device__ __forceinline__ float block_sum(const LaneCodes<CODEC> &lc, const flo
         const float nm = -(float(sb[1]) * float((lc.scm >> 8) & 0xFFu));
         const float v = __builtin_fmaf(d[1], 0.0625f, d[0]) + corr[0];
         return __builtin_fmaf(dsc, v, __builtin_fmaf(nm, corr[1], acc));
-    } else if constexpr (CODEC == Q8_0) {
+    } else if constexpr (CODEC == Q8_0 || CODEC == TERNARY) {
         return __builtin_fmaf(float(sb[0]), d[0] + corr[0], acc);
     } else if constexpr (CODEC == Q2_0) {
         const float v = __builtin_fmaf(d[3], 0.015625f, __builtin_fmaf(d[2], 0.0625f, __builtin_fmaf(d[1], 0.25f, d[0])));
@@ -235,6 +251,7 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
 #pragma unroll
                     for (int mr = 0; mr < MM; ++mr)
                         dots[c][mr] = 0.0f;
+                prepare_lane<CODEC>(lc[u]);
                 slice_dots<CODEC, MM>(lc[u], xrow, magic, dots);
 #pragma unroll
                 for (int mr = 0; mr < MM; ++mr) {
@@ -364,6 +381,7 @@ hipError_t launch_gemv(const GemmProblem &p, hipStream_t stream)
     case Q2_0: return launch_gemv_codec<Q2_0>(p, stream);
     case Q8_0: return launch_gemv_codec<Q8_0>(p, stream);
     case Q4_K: return launch_gemv_codec<Q4_K>(p, stream);
+    case TERNARY: return launch_gemv_codec<TERNARY>(p, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -385,6 +403,7 @@ hipError_t launch_dequant(const GemmProblem &p, _Float16 *out, int64_t ldw, hipS
     case Q2_0: fn = reinterpret_cast<const void *>(&dequant_kernel<Q2_0>); break;
     case Q8_0: fn = reinterpret_cast<const void *>(&dequant_kernel<Q8_0>); break;
     case Q4_K: fn = reinterpret_cast<const void *>(&dequant_kernel<Q4_K>); break;
+    case TERNARY: fn = reinterpret_cast<const void *>(&dequant_kernel<TERNARY>); break;
     default: return hipErrorInvalidValue;
     }
     return hipLaunchKernel(fn, grid, block, args, 0, stream);

@@ -18,6 +18,9 @@
 //   MLX4-G32  the same, one (s, b) per 32 weights
 //   Q2_0      w = (q - 1) * d, q=3 -> +2d  (v_pk_add_f16, v_pk_mul_f16)
 //   Q8_0      w = q * d, stored q + 128    (v_pk_add_f16, v_pk_mul_f16)
+//   ternary   w = (t - 1) * d, digit t of a fixed-point base-3 byte (two
+//             v_pk_mul_lo_u16, one and, one v_pk_lshrrev_b16 per two digits,
+//             then the or / v_pk_add_f16 / v_pk_mul_f16 of the others)
 //   Q4_K      w = d * (q sc) - dmin m      (v_pk_fma_f16 for the exact
 //             integer q sc, then v_fma_mix{lo,hi}_f16: fp16 d times fp16 q sc
 //             plus the fp32 value -dmin m, rounded once to fp16; see mix_pair)
@@ -36,6 +39,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
@@ -93,10 +97,27 @@ template <> struct LaneCodes<Q4_K> {
     float nm;                  // from prepare_lane: -dmin * m, exact in fp32
 };
 
-// Per-k-step values a lane derives once from its scale record before the
-// unpack (only Q4_K has any).
+template <> struct LaneCodes<TERNARY> {
+    uint32_t a;                // bytes E0 O0 E1 O1
+    uint32_t b;                // bytes E2 O2 (low 16 bits)
+    uint32_t tl;               // the tail byte shared with the neighbouring lane (low 8 bits)
+    _Float16 d;
+    uint32_t r0, r1, r2, r3;   // from prepare_lane: (E_b, O_b) one byte per 16-bit half; tail twice
+    uint32_t m3;               // from prepare_lane: 16-bit digit multipliers of the lane's two tail digits
+};
+
+// Per-k-step values a lane derives once from its codes and scale record
+// before the unpack (Q4_K and ternary).
 template <int CODEC> __device__ __forceinline__ void prepare_lane(LaneCodes<CODEC> &lc)
 {
+    if constexpr (CODEC == TERNARY) {
+        // v_perm_b32: selector byte k picks the destination byte k (0x0C: zero)
+        lc.r0 = __builtin_amdgcn_perm(lc.a, lc.a, 0x0C010C00u);
+        lc.r1 = __builtin_amdgcn_perm(lc.a, lc.a, 0x0C030C02u);
+        lc.r2 = __builtin_amdgcn_perm(lc.b, lc.b, 0x0C010C00u);
+        lc.r3 = __builtin_amdgcn_perm(lc.tl, lc.tl, 0x0C000C00u);
+        lc.m3 = (__lane_id() & 1) ? (9u | (27u << 16)) : (1u | (3u << 16));   // digits 2, 3 or 0, 1
+    }
     if constexpr (CODEC == Q4_K) {
         const _Float16 sc = _Float16(float(lc.scm & 0xFFu));    // 0..63, exact
         const f16x2 s2 = {sc, sc};
@@ -132,6 +153,19 @@ template <> struct CodeZero<MLX4_G32> { static constexpr int v = 0; };
 template <> struct CodeZero<Q2_0> { static constexpr int v = 1; };
 template <> struct CodeZero<Q8_0> { static constexpr int v = 128; };   // codes are stored as q + 128
 template <> struct CodeZero<Q4_K> { static constexpr int v = 0; };
+template <> struct CodeZero<TERNARY> { static constexpr int v = 1; };    // digit t = q + 1
+
+// Base-3 digits of fixed-point bytes, one byte per 16-bit half of r: digit i
+// of byte B is ((B 3^i) mod 256) 3 >> 8 (mul = 3^i in both halves, or the
+// lane's tail multipliers).  Returns (1024 + t_lo, 1024 + t_hi) as fp16 bits.
+__device__ __forceinline__ uint32_t ternary_digits(uint32_t r, uint32_t mul)
+{
+    const u16x2 x = __builtin_bit_cast(u16x2, r) * __builtin_bit_cast(u16x2, mul);
+    const u16x2 y = __builtin_bit_cast(u16x2, __builtin_bit_cast(uint32_t, x) & 0x00FF00FFu);
+    const u16x2 three = {3, 3};
+    const u16x2 t = (y * three) >> (u16x2){8, 8};
+    return __builtin_bit_cast(uint32_t, t) | 0x64006400u;
+}
 
 // (2^E + q_even, 2^E + q_odd) -> exact fp16 (q_even - z, q_odd - z)
 template <int CODEC, int E>
@@ -148,7 +182,17 @@ template <int CODEC>
 __device__ __forceinline__ f16x8 unpack_substep(const LaneCodes<CODEC> &lc, int s, const Magics &mg)
 {
     f16x2 q[4];
-    if constexpr (CODEC == Q4_K) {
+    if constexpr (CODEC == TERNARY) {
+        // pairs p = 4 s .. 4 s + 3: digit p % 5 of (E, O)[p / 5]; p = 15: the tail
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int p = 4 * s + u;
+            const uint32_t r = p < 5 ? lc.r0 : p < 10 ? lc.r1 : p < 15 ? lc.r2 : lc.r3;
+            const uint32_t pw = p % 5 == 0 ? 1u : p % 5 == 1 ? 3u : p % 5 == 2 ? 9u : p % 5 == 3 ? 27u : 81u;
+            const uint32_t mul = p == 15 ? lc.m3 : pw | (pw << 16);
+            q[u] = factor<CODEC, 10>(ternary_digits(r, mul));
+        }
+    } else if constexpr (CODEC == Q4_K) {
         // (2^E + q) sc - 2^E sc = q sc exactly (at most 15 * 63 = 945), then
         // one rounding: d (q sc) - dmin m
         const uint32_t w = lc.c[s], w8 = w >> 8;
@@ -245,6 +289,7 @@ __device__ __forceinline__ _Float16 load_f16(__amdgpu_buffer_rsrc_t r, uint32_t 
 // must itself stay inside the plane (callers keep 0 <= t < ksteps).
 struct LaneOffsets {
     uint32_t q, s, s2;    // s2: Q4_K's super-block record
+    uint32_t q2, q3;      // ternary: the B and T parts of the chunk
 };
 
 template <int CODEC>
@@ -253,9 +298,16 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int rg, int groups, int lane
     LaneOffsets o;
     const uint32_t i = uint32_t(lane & 31);
     o.s2 = OOB;
+    o.q2 = OOB;
+    o.q3 = OOB;
     if (rg >= groups) {
         o.q = OOB;
         o.s = OOB;
+    } else if constexpr (CODEC == TERNARY) {
+        o.q = uint32_t(lane) * 4;
+        o.q2 = 256u + uint32_t(lane) * 2;
+        o.q3 = 384u + uint32_t(lane >> 1);
+        o.s = i * 2;
     } else if constexpr (CODEC == Q4_K) {
         o.q = uint32_t(lane) * 16;
         o.s = uint32_t(lane) * 2;
@@ -286,7 +338,13 @@ __device__ __forceinline__ LaneCodes<CODEC> load_lane(const PlaneRsrc &w, LaneOf
 {
     LaneCodes<CODEC> lc;
     const uint32_t chunk = uint32_t(rg) * uint32_t(ksteps) + uint32_t(t);
-    if constexpr (CODEC == Q8_0) {
+    if constexpr (CODEC == TERNARY) {
+        const uint32_t base = chunk * uint32_t(TERNARY_CHUNK);
+        lc.a = __builtin_amdgcn_raw_buffer_load_b32(w.qs, o.q, base, 0);
+        lc.b = __builtin_amdgcn_raw_buffer_load_b16(w.qs, o.q2, base, 0);
+        lc.tl = __builtin_amdgcn_raw_buffer_load_b8(w.qs, o.q3, base, 0);
+        lc.d = load_f16(w.sc, o.s, (uint32_t(rg) * uint32_t(ksteps >> 2) + uint32_t(t >> 2)) * 64u);
+    } else if constexpr (CODEC == Q8_0) {
         lc.lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 2048, 0));
         lc.hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 2048 + 1024, 0));
         lc.d = load_f16(w.sc, o.s, chunk * 128);

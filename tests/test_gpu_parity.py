@@ -68,7 +68,8 @@ def _same_value_bits(a16, b16):
 
 DEQ_SHAPES = [(1, 256, 256), (1, 40, 96), (1, 1000, 544), (2, 33, 192), (2, 300, 1024),
               (3, 37, 256), (3, 520, 1152), (4, 256, 256), (4, 40, 96), (4, 300, 544),
-              (5, 256, 256), (5, 33, 96), (5, 300, 544), (6, 256, 256), (6, 40, 512), (6, 300, 768)]
+              (5, 256, 256), (5, 33, 96), (5, 300, 544), (6, 256, 256), (6, 40, 512), (6, 300, 768),
+              (7, 256, 256), (7, 40, 512), (7, 300, 768)]
 
 
 @pytest.mark.parametrize("codec,n,k", DEQ_SHAPES)
@@ -135,7 +136,7 @@ def test_q4_k_single_rounding_through_kernels(torch):
         assert _same_value_bits(y, want.T[:m])
 
 
-@pytest.mark.parametrize("codec", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("codec", [1, 2, 3, 4, 5, 6, 7])
 def test_identity_probe_through_gemm(torch, codec):
     """X = I: every output is one product with 1.0, so Y = W^T exactly."""
     n = k = 256
@@ -163,6 +164,9 @@ GEMM_SHAPES = [
     # Q4_K likewise (K a multiple of the 256-weight super-block), and a split-k shape
     (6, 16, 256, 256), (6, 33, 200, 512), (6, 129, 136, 256), (6, 300, 264, 768), (6, 257, 1024, 256),
     (6, 48, 320, 2304),
+    # ternary likewise, plus the register-staged class (64 < M <= 128)
+    (7, 16, 256, 256), (7, 33, 200, 512), (7, 100, 136, 256), (7, 129, 136, 256), (7, 300, 264, 768),
+    (7, 257, 1024, 256), (7, 48, 320, 2304), (6, 100, 264, 512),
 ]
 
 
@@ -227,7 +231,8 @@ def test_prefill_row_permutation_and_determinism(torch):
 
 
 HEADS_SHAPES = [(1, 2, 256, 128, 64), (2, 37, 192, 256, 64), (1, 300, 512, 256, 128), (3, 64, 384, 256, 96),
-                (4, 129, 256, 160, 32), (6, 37, 192, 256, 64), (1, 2048, 8192, 128, 128)]
+                (4, 129, 256, 160, 32), (6, 37, 192, 256, 64), (7, 300, 256, 512, 128),
+                (1, 2048, 8192, 128, 128)]
 
 
 @pytest.mark.parametrize("codec,m,n,k,d", HEADS_SHAPES)
@@ -251,7 +256,8 @@ def test_prefill_heads_layout(torch, codec, m, n, k, d):
 
 SWIGLU_SHAPES = [(2, 33, 200, 192), (2, 130, 256, 128), (2, 300, 264, 256), (1, 70, 136, 96), (3, 200, 128, 256),
                  (4, 200, 128, 256), (4, 70, 136, 96), (5, 200, 128, 256), (5, 70, 136, 96),
-                 (6, 300, 264, 256), (6, 70, 136, 512)]
+                 (6, 300, 264, 256), (6, 70, 136, 512), (7, 300, 264, 256), (7, 70, 136, 512),
+                 (7, 40, 64, 256)]
 
 
 @pytest.mark.parametrize("codec,m,n,k", SWIGLU_SHAPES)
@@ -283,7 +289,7 @@ def test_swiglu_one_hot_probe(torch):
 # -------------------------------------------------------------------- GeGLU --
 
 GEGLU_SHAPES = [(2, 300, 264, 256), (2, 70, 136, 128), (1, 33, 200, 192), (4, 200, 128, 256), (3, 129, 256, 256),
-                (6, 129, 256, 256)]
+                (6, 129, 256, 256), (7, 129, 256, 256)]
 
 
 @pytest.mark.parametrize("codec,m,n,k", GEGLU_SHAPES)
@@ -319,7 +325,8 @@ GEMV_SHAPES = [(1, 1, 1000, 512), (1, 2, 256, 96), (1, 3, 520, 256), (1, 4, 200,
                (3, 1, 264, 512), (3, 3, 256, 256), (3, 64, 200, 384),
                (4, 1, 1000, 512), (4, 3, 264, 256), (4, 64, 200, 384),
                (5, 1, 1000, 512), (5, 2, 264, 96), (5, 64, 200, 384),
-               (6, 1, 1000, 512), (6, 2, 256, 1024), (6, 3, 264, 256), (6, 64, 200, 512)]
+               (6, 1, 1000, 512), (6, 2, 256, 1024), (6, 3, 264, 256), (6, 64, 200, 512),
+               (7, 1, 1000, 512), (7, 2, 256, 1024), (7, 4, 264, 256), (7, 64, 200, 512)]
 
 
 @pytest.mark.parametrize("codec,m,n,k", GEMV_SHAPES)

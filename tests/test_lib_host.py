@@ -243,7 +243,7 @@ FAKE = 0x100000    # aligned, non-null; never dereferenced: every call below is 
 
 
 @pytest.mark.parametrize("args,status", [
-    (dict(w=_w(codec=7)), -2),
+    (dict(w=_w(codec=9)), -2),
     (dict(w=_w(k=48)), -3),
     (dict(w=_w(flags=1)), -3),
     (dict(w=_w(qs=0)), -1),

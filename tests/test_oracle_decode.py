@@ -159,7 +159,7 @@ def test_decode_rejects_bad_shapes():
     with pytest.raises(ValueError):
         oracle.decode(oracle.Q4_0, np.zeros(18, np.uint8), 1, 48)
     with pytest.raises(ValueError):
-        oracle.decode(7, np.zeros(18, np.uint8), 1, 32)
+        oracle.decode(9, np.zeros(18, np.uint8), 1, 32)
 
 
 def test_mlx_zero_code_returns_bias_bits():
