@@ -28,6 +28,11 @@ namespace {
 constexpr int GEMV_NW = 8;               // waves per workgroup (split of the k-steps)
 constexpr int GEMV_NT = 64 * GEMV_NW;
 constexpr int GEMV_PF = 4;               // k-steps of codes in flight per lane
+#ifndef QG_PF_SMALL
+#define QG_PF_SMALL 4
+#endif
+// codecs with few code bytes per lane and k-step keep more k-steps in flight
+template <int CODEC> constexpr int gemv_pf() { return (CODEC == TERNARY || CODEC == Q2_0) ? QG_PF_SMALL : GEMV_PF; }
 constexpr int GEMV_X_LDS_MAX = 64 * 1024; // largest staged X (M x K fp16) the GEMV takes
 
 struct GemvArgs {
@@ -59,7 +64,7 @@ __device__ __forceinline__ void slice_correction(const u32x4 *chunks, float *out
     if constexpr (CODEC == Q8_0) {
         out[0] = -1152.0f * ((sp[0] + sp[1]) + (sp[2] + sp[3]));
     } else if constexpr (CODEC == TERNARY) {
-        out[0] = -1025.0f * ((sp[0] + sp[1]) + (sp[2] + sp[3]));
+        out[0] = -((sp[0] + sp[1]) + (sp[2] + sp[3]));
     } else if constexpr (CODEC == Q4_0) {
         out[0] = -1032.0f * (sp[0] + sp[2]) - 72.0f * (sp[1] + sp[3]);
     } else if constexpr (CODEC == MLX4_G64 || CODEC == MLX4_G32 || CODEC == Q4_K) {
@@ -80,7 +85,8 @@ __device__ __forceinline__ void slice_correction(const u32x4 *chunks, float *out
 //   Q4_0 / MLX4 / Q4_K: d[0] (fields at bits 0, 8 -> factor 1), d[1] (bits 4, 12 -> 16)
 //   Q2_0:         d[p] (fields at bits 2p, 8 + 2p -> factor 4^p), p = 0..3
 //   Q8_0:         d[0] (bytes at bits 0, 8 -> factor 1; stored q + 128)
-//   ternary:      d[0] (digits t = q + 1 extracted to the low bits first)
+//   ternary:      d[0..3] (digits t = q + 1 as subnormal fp16 t 2^-24, one
+//                 accumulator per pair position)
 // block_sum then removes the 1024 offsets (and the codec zero point) with the
 // precomputed X term: sum_k (q_k - z) x_k = sum_c d[c] / 2^f_c + corr.
 template <int CODEC, int MM>
@@ -88,18 +94,27 @@ __device__ __forceinline__ void slice_dots(const LaneCodes<CODEC> &lc, const u32
                                            uint32_t magic, float (&d)[4][MM])
 {
     if constexpr (CODEC == TERNARY) {
+        // The digits t (0..2) are dotted as they come out of the extraction:
+        // read as binary16 bit patterns they are the subnormals t 2^-24, so
+        // each product is t x 2^-24 exactly and block_sum scales by 2^24.
+        // Four independent pair chains and accumulators per sub-step keep the
+        // multiply-to-use latencies of the packed integer ops covered.
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s) {
+            uint32_t h[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int p = 4 * s + u;
                 const uint32_t r = p < 5 ? lc.r0 : p < 10 ? lc.r1 : p < 15 ? lc.r2 : lc.r3;
                 const uint32_t pw = p % 5 == 0 ? 1u : p % 5 == 1 ? 3u : p % 5 == 2 ? 9u : p % 5 == 3 ? 27u : 81u;
-                const uint32_t h = ternary_digits(r, p == 15 ? lc.m3 : pw | (pw << 16));
+                h[u] = ternary_digits(r, p == 15 ? lc.m3 : pw | (pw << 16)) & 0x00030003u;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
 #pragma unroll
                 for (int mr = 0; mr < MM; ++mr)
-                    d[0][mr] = __builtin_amdgcn_fdot2(as_f16x2(h), as_f16x2(xrow[mr][s][u]), d[0][mr], false);
-            }
+                    d[u][mr] = __builtin_amdgcn_fdot2(as_f16x2(h[u]), as_f16x2(xrow[mr][s][u]), d[u][mr], false);
+        }
     } else if constexpr (CODEC == Q8_0) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -174,7 +189,11 @@ __device__ __forceinline__ float block_sum(const LaneCodes<CODEC> &lc, const flo
         const float nm = -(float(sb[1]) * float((lc.scm >> 8) & 0xFFu));
         const float v = __builtin_fmaf(d[1], 0.0625f, d[0]) + corr[0];
         return __builtin_fmaf(dsc, v, __builtin_fmaf(nm, corr[1], acc));
-    } else if constexpr (CODEC == Q8_0 || CODEC == TERNARY) {
+    } else if constexpr (CODEC == TERNARY) {
+        // sum (t - 1) x = 2^24 (sum of the subnormal-digit dots) - sum x
+        const float v = __builtin_fmaf((d[0] + d[1]) + (d[2] + d[3]), 16777216.0f, corr[0]);
+        return __builtin_fmaf(float(sb[0]), v, acc);
+    } else if constexpr (CODEC == Q8_0) {
         return __builtin_fmaf(float(sb[0]), d[0] + corr[0], acc);
     } else if constexpr (CODEC == Q2_0) {
         const float v = __builtin_fmaf(d[3], 0.015625f, __builtin_fmaf(d[2], 0.0625f, __builtin_fmaf(d[1], 0.25f, d[0])));
@@ -191,6 +210,7 @@ template <int CODEC, int MM>
 __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
 {
     constexpr int NC = corr_floats<CODEC>();
+    constexpr int PF = gemv_pf<CODEC>();
 
     extern __shared__ u32x4 smem[];
     char *lds = reinterpret_cast<char *>(smem);
@@ -211,9 +231,9 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
     // the first GEMV_PF k-steps of codes and scales
     const PlaneRsrc w = plane_rsrc(a.w);
     const LaneOffsets lo = lane_offsets<CODEC>(rg, a.groups, lane);
-    LaneCodes<CODEC> lc[GEMV_PF];
+    LaneCodes<CODEC> lc[PF];
 #pragma unroll
-    for (int u = 0; u < GEMV_PF; ++u)
+    for (int u = 0; u < PF; ++u)
         if (t0 + u < t1)
             lc[u] = load_lane<CODEC>(w, lo, rg, t0 + u, a.ksteps, a.kb128);
 
@@ -236,9 +256,9 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
     for (int mr = 0; mr < MM; ++mr)
         acc[mr] = 0.0f;
 
-    for (int tb = t0; tb < t1; tb += GEMV_PF) {
+    for (int tb = t0; tb < t1; tb += PF) {
 #pragma unroll
-        for (int u = 0; u < GEMV_PF; ++u) {
+        for (int u = 0; u < PF; ++u) {
             const int t = tb + u;
             if (t < t1) {
                 const u32x4 *xrow[MM];
@@ -260,7 +280,7 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
                 }
             }
             // refill this slot with the k-step one batch ahead
-            const int tn = tb + GEMV_PF + u;
+            const int tn = tb + PF + u;
             if (tn < t1)
                 lc[u] = load_lane<CODEC>(w, lo, rg, tn, a.ksteps, a.kb128);
         }

@@ -157,7 +157,9 @@ template <> struct CodeZero<TERNARY> { static constexpr int v = 1; };    // digi
 
 // Base-3 digits of fixed-point bytes, one byte per 16-bit half of r: digit i
 // of byte B is ((B 3^i) mod 256) 3 >> 8 (mul = 3^i in both halves, or the
-// lane's tail multipliers).  Returns (1024 + t_lo, 1024 + t_hi) as fp16 bits.
+// lane's tail multipliers).  Returns (1024 + t_lo, 1024 + t_hi) as fp16 bits;
+// the bits above bit 1 of each half are the magic, so `& 0x00030003` gives
+// the bare digits.
 __device__ __forceinline__ uint32_t ternary_digits(uint32_t r, uint32_t mul)
 {
     const u16x2 x = __builtin_bit_cast(u16x2, r) * __builtin_bit_cast(u16x2, mul);
