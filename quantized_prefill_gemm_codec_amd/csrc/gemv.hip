@@ -28,11 +28,7 @@ namespace {
 constexpr int GEMV_NW = 8;               // waves per workgroup (split of the k-steps)
 constexpr int GEMV_NT = 64 * GEMV_NW;
 constexpr int GEMV_PF = 4;               // k-steps of codes in flight per lane
-#ifndef QG_PF_SMALL
-#define QG_PF_SMALL 4
-#endif
-// codecs with few code bytes per lane and k-step keep more k-steps in flight
-template <int CODEC> constexpr int gemv_pf() { return (CODEC == TERNARY || CODEC == Q2_0) ? QG_PF_SMALL : GEMV_PF; }
+// (8 and 12 measured no faster for the small-code codecs, Q2_0 and ternary)
 constexpr int GEMV_X_LDS_MAX = 64 * 1024; // largest staged X (M x K fp16) the GEMV takes
 
 struct GemvArgs {
@@ -210,7 +206,7 @@ template <int CODEC, int MM>
 __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
 {
     constexpr int NC = corr_floats<CODEC>();
-    constexpr int PF = gemv_pf<CODEC>();
+    constexpr int PF = GEMV_PF;
 
     extern __shared__ u32x4 smem[];
     char *lds = reinterpret_cast<char *>(smem);
