@@ -185,6 +185,40 @@ qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonica
  * binary16 value nearest its exact codec value.  For verification. */
 qg_status qg_dequant(const qg_weight *w, void *w_fp16, int64_t ldw, void *stream);
 
+/* Attention over a Q8_0-compressed KV cache, prefill (comparison page section
+ * 2.3 and project index Brick 4: a FlashAttention core with online softmax
+ * whose K and V are dequantized from the Q8_0 cache as they are read; releases
+ * page v0.2.3: D in {64, 128}; releases page v0.3.0: grouped-query attention
+ * and causal masking).  For each query head h with KV head g = h / (heads /
+ * kv_heads):
+ *     O[h, i] = sum_t softmax_t(scale * Q[h, i] . K[g, t]) V[g, t]
+ * over the keys t < s, and with causal != 0 only t <= (s - m) + i (the m
+ * queries are the last m of the s positions).  K and V elements are the
+ * binary16 values nearest q * d (the Q8_0 rule of QG_CODEC_Q8_0); scores,
+ * softmax and sums are fp32, P is rounded to fp16 for the second product.
+ *  q         device fp16 [heads, m, head_dim] (the direct-head layout of
+ *            qgemm_prefill_heads), 16-byte aligned
+ *  o         device fp16 [heads, m, head_dim], written; 16-byte aligned
+ *  k_codes   device int8 [kv_heads * s, head_dim] (two's complement q)
+ *  k_scales  device fp16 [kv_heads * s, head_dim / 32] (d of each 32 codes)
+ *  v_codes, v_scales  the same for V; all four 16-byte aligned
+ *  head_dim  64 or 128;  1 <= heads <= 65535, heads % kv_heads == 0;
+ *  1 <= m <= s;  causal 0 or 1;  scale > 0 and finite (usually 1/sqrt(D))
+ * Buffers must stay below 2 GiB.  Errors: QG_ERR_NULL, QG_ERR_SHAPE,
+ * QG_ERR_ALIGN, QG_ERR_LAUNCH; nothing is launched on an argument error. */
+qg_status qattn_prefill_q8kv(const void *q, void *o, int64_t heads, int64_t m, int64_t head_dim,
+                             const void *k_codes, const void *k_scales, const void *v_codes,
+                             const void *v_scales, int64_t kv_heads, int64_t s, int32_t causal,
+                             float scale, void *stream);
+
+/* Host-side split of canonical Q8_0 rows (GGUF block_q8_0: fp16 d then 32
+ * int8 codes, per 32 elements of a row) into the planar KV cache format of
+ * qattn_prefill_q8kv: codes [rows, head_dim] int8 and scales [rows,
+ * head_dim / 32] fp16.  Byte moves only.  head_dim a multiple of 32 (<= 4096);
+ * canonical_bytes >= rows * head_dim / 32 * 34 (else QG_ERR_SIZE). */
+qg_status qg_pack_kv_host(const void *canonical, size_t canonical_bytes, int64_t rows, int64_t head_dim,
+                          void *codes, void *scales);
+
 /* Static text for a status code. */
 const char *qg_status_str(qg_status s);
 

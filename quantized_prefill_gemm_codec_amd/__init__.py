@@ -10,6 +10,7 @@ fallback: if the library is not built, every entry point raises.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import numpy as np
@@ -35,7 +36,7 @@ STATUS = {0: "QG_OK", -1: "QG_ERR_NULL", -2: "QG_ERR_CODEC", -3: "QG_ERR_SHAPE",
           -8: "QG_ERR_CODE"}
 
 EXPORTS = ("qgemm_prefill", "qgemm_prefill_heads", "qgemm_swiglu", "qgemm_geglu", "qgemv_decode", "qg_packed_sizes", "qg_canonical_size",
-           "qg_pack_host", "qg_dequant", "qg_status_str", "qg_version")
+           "qg_pack_host", "qg_dequant", "qg_status_str", "qg_version", "qattn_prefill_q8kv", "qg_pack_kv_host")
 
 
 class QGError(RuntimeError):
@@ -71,11 +72,13 @@ def lib():
         L.qg_canonical_size.argtypes = [i32, i64, i64, ctypes.POINTER(sz)]
         L.qg_pack_host.argtypes = [i32, i64, i64, p, sz, p, p]
         L.qg_dequant.argtypes = [W, p, i64, p]
+        L.qattn_prefill_q8kv.argtypes = [p, p, i64, i64, i64, p, p, p, p, i64, i64, i32, ctypes.c_float, p]
+        L.qg_pack_kv_host.argtypes = [p, sz, i64, i64, p, p]
         L.qg_status_str.argtypes = [ctypes.c_int]
         L.qg_status_str.restype = ctypes.c_char_p
         L.qg_version.restype = i32
         for f in ("qgemm_prefill", "qgemm_prefill_heads", "qgemm_swiglu", "qgemm_geglu", "qgemv_decode", "qg_packed_sizes", "qg_canonical_size",
-                  "qg_pack_host", "qg_dequant"):
+                  "qg_pack_host", "qg_dequant", "qattn_prefill_q8kv", "qg_pack_kv_host"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -245,6 +248,51 @@ def qg_dequant(w: QWeight, stream=None):
     buf = torch.empty((w.n, ldw), dtype=torch.float16, device=w.qs.device)
     _check(lib().qg_dequant(w.desc, buf.data_ptr(), ldw, _stream(stream)), "qg_dequant")
     return buf[:, :w.k]
+
+
+class Q8KVCache:
+    """Planar Q8_0 KV cache on the device: int8 codes [rows, D] and fp16 scales
+    [rows, D / 32] for K and for V (rows = kv_heads * s)."""
+
+    def __init__(self, kv_heads: int, s: int, head_dim: int, k_codes, k_scales, v_codes, v_scales):
+        self.kv_heads, self.s, self.head_dim = kv_heads, s, head_dim
+        self.k_codes, self.k_scales, self.v_codes, self.v_scales = k_codes, k_scales, v_codes, v_scales
+
+    @classmethod
+    def from_canonical(cls, kv_heads: int, s: int, head_dim: int, k_canonical: np.ndarray,
+                       v_canonical: np.ndarray, device="cuda"):
+        """Split canonical Q8_0 rows (qg_pack_kv_host) and upload."""
+        torch = _torch()
+        parts = []
+        for canon in (k_canonical, v_canonical):
+            canon = np.ascontiguousarray(canon, dtype=np.uint8)
+            rows = kv_heads * s
+            codes = np.empty(rows * head_dim, np.uint8)
+            scales = np.empty(rows * (head_dim // 32) * 2, np.uint8)
+            _check(lib().qg_pack_kv_host(canon.ctypes.data, canon.size, rows, head_dim, codes.ctypes.data,
+                                         scales.ctypes.data), "qg_pack_kv_host")
+            parts += [torch.from_numpy(codes).to(device), torch.from_numpy(scales).to(device)]
+        return cls(kv_heads, s, head_dim, *parts)
+
+
+def qattn_prefill_q8kv(q, cache: Q8KVCache, causal: bool = True, scale: float | None = None, out=None,
+                       stream=None):
+    """Attention of fp16 queries q [H, M, D] over a Q8_0 KV cache; returns fp16 [H, M, D]."""
+    torch = _torch()
+    if q.dtype != torch.float16 or not q.is_cuda or q.dim() != 3 or q.shape[2] != cache.head_dim:
+        raise ValueError("q must be a float16 [H, M, D] tensor on a HIP device with D matching the cache")
+    q = q.contiguous()
+    heads, m, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != torch.float16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float16 tensor shaped like q")
+    sc = float(scale) if scale is not None else 1.0 / math.sqrt(d)
+    _check(lib().qattn_prefill_q8kv(q.data_ptr(), out.data_ptr(), heads, m, d, cache.k_codes.data_ptr(),
+                                    cache.k_scales.data_ptr(), cache.v_codes.data_ptr(), cache.v_scales.data_ptr(),
+                                    cache.kv_heads, cache.s, 1 if causal else 0, sc, _stream(stream)),
+           "qattn_prefill_q8kv")
+    return out
 
 
 def qg_version() -> int:

@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libqgemm.so")
 BUILD = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["gemm.hip", "gemv.hip", "api.hip"]
+HIP_SOURCES = ["gemm.hip", "gemv.hip", "attention.hip", "api.hip"]
 CXX_SOURCES = ["pack.cpp"]
 HEADERS = ["planar.h", "unpack.h", "launch.h", "lds_dma.h"]
 

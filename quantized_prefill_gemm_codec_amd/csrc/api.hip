@@ -78,6 +78,8 @@ GemmProblem problem(const qg_weight *w, const void *x, int64_t m, int64_t ldx, v
 
 qg_status launched(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH; }
 
+bool finite_positive(float v) { return v > 0.0f && v <= 3.4e38f; }
+
 qg_status check_gemm(const qg_weight *w, const void *x, int64_t m, int64_t ldx, void *y, int64_t ldy)
 {
     qg_status st = check_weight(w);
@@ -169,6 +171,37 @@ qg_status qg_dequant(const qg_weight *w, void *w_fp16, int64_t ldw, void *stream
         return st;
     const GemmProblem p = problem(w, nullptr, 1, w->k, nullptr, w->n);
     return launched(launch_dequant(p, static_cast<_Float16 *>(w_fp16), ldw, static_cast<hipStream_t>(stream)));
+}
+
+qg_status qattn_prefill_q8kv(const void *q, void *o, int64_t heads, int64_t m, int64_t head_dim,
+                             const void *k_codes, const void *k_scales, const void *v_codes, const void *v_scales,
+                             int64_t kv_heads, int64_t s, int32_t causal, float scale, void *stream)
+{
+    if (!q || !o || !k_codes || !k_scales || !v_codes || !v_scales)
+        return QG_ERR_NULL;
+    if ((head_dim != 64 && head_dim != 128) || heads < 1 || heads > 65535 || kv_heads < 1 || heads % kv_heads != 0 ||
+        m < 1 || s < m || (causal != 0 && causal != 1) || !finite_positive(scale))
+        return QG_ERR_SHAPE;
+    if (heads * m * head_dim * 2 >= LIMIT || kv_heads * s * head_dim >= LIMIT)
+        return QG_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(o) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_scales) ||
+        !aligned16(v_scales))
+        return QG_ERR_ALIGN;
+    AttnProblem p;
+    p.q = static_cast<const _Float16 *>(q);
+    p.o = static_cast<_Float16 *>(o);
+    p.k_codes = static_cast<const uint8_t *>(k_codes);
+    p.v_codes = static_cast<const uint8_t *>(v_codes);
+    p.k_scales = static_cast<const _Float16 *>(k_scales);
+    p.v_scales = static_cast<const _Float16 *>(v_scales);
+    p.heads = heads;
+    p.m = m;
+    p.head_dim = head_dim;
+    p.kv_heads = kv_heads;
+    p.s = s;
+    p.causal = causal != 0;
+    p.scale = scale;
+    return launched(launch_attention(p, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -1,0 +1,290 @@
+// Attention over a Q8_0 KV cache (prefill), fused with the on-the-fly
+// dequantization of K and V.
+//
+// Pages: comparison page section 2.3 and project index Brick 4 -- a
+// FlashAttention core (online softmax, no round trip of the score matrix
+// through memory) whose K and V come from a Q8_0-compressed cache and are
+// dequantized as they are read; releases page v0.2.3, the attention core is
+// templated on the head dimension D in {64, 128}; releases page v0.3.0,
+// grouped-query attention and causal masking in the transformer block.
+//
+// One workgroup of four wave64 handles 128 queries of one head; each wave owns
+// 32 of them for the whole key range.  Per tile of 64 keys:
+//  * the 256 threads turn the tile's int8 codes and fp16 block scales into
+//    fp16 K [64][D] (row-major) and V^T [D][64] in LDS -- each element is the
+//    correctly rounded q * d, the weights' Q8_0 rule; the raw codes of the next
+//    tile are already in registers (loaded one tile ahead);
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_f16 (A = K rows, B = the wave's Q
+//    fragments, loaded once).  K rows are read in the order pi below, which
+//    makes each lane's 32 scores exactly the B fragments P^T needs for the
+//    next product: no lane exchange between the two products;
+//  * online softmax in fp32 on the log2 scale: the row maximum and sum are
+//    lane-local over 32 scores plus one exchange with lane l ^ 32 (the other
+//    half of the same query's keys); the O accumulators are rescaled by
+//    2^(m_old - m_new);
+//  * O^T += V^T P^T (A = V^T rows from LDS, B = P as fp16).
+// The epilogue divides by the row sum and writes O [H, M, D] fp16.
+#include "launch.h"
+
+namespace qg {
+namespace {
+
+constexpr int AT_BQ = 128;   // queries per workgroup
+constexpr int AT_BK = 64;    // keys per tile
+constexpr int AT_NT = 256;   // threads per workgroup
+
+struct AttnArgs {
+    const _Float16 *q;
+    _Float16 *o;
+    const uint8_t *kq, *vq;     // int8 codes [kv_heads * s][D]
+    const _Float16 *ks, *vs;    // fp16 scales [kv_heads * s][D / 32]
+    int heads, m, kv_heads, s, causal, tiles_q;
+    float scale_log2;           // softmax scale times log2(e)
+};
+
+// 16 int8 codes (two's complement) of one 32-element block half -> the fp16
+// values q * d, in order.  XOR 0x80 turns q into q + 128 in 0..255; two
+// bytes moved into the low bytes of the halves of a word and OR-ed into
+// binary16 1024 read 1024 + q + 128; subtracting 1152 is exact, the multiply
+// by d rounds once.
+__device__ __forceinline__ void dequant16(u32x4 c, _Float16 d, u32x4 &lo, u32x4 &hi)
+{
+    const f16x2 dd = {d, d};
+    const f16x2 off = {_Float16(1152.0f), _Float16(1152.0f)};
+    uint32_t r[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t x = c[w] ^ 0x80808080u;
+        const uint32_t p01 = __builtin_amdgcn_perm(x, x, 0x0C010C00u) | 0x64006400u;
+        const uint32_t p23 = __builtin_amdgcn_perm(x, x, 0x0C030C02u) | 0x64006400u;
+        r[2 * w] = as_u32((as_f16x2(p01) - off) * dd);
+        r[2 * w + 1] = as_u32((as_f16x2(p23) - off) * dd);
+    }
+    lo = u32x4{r[0], r[1], r[2], r[3]};
+    hi = u32x4{r[4], r[5], r[6], r[7]};
+}
+
+// A-operand row r (0..31) of a 32-key block reads key pi(r): the MFMA puts
+// row 8 q + 4 g + e of the product in register 4 q + e of lane half g, and
+// pi(8 q + 4 g + e) = 16 (q >> 1) + 8 g + 4 (q & 1) + e hands lane half g the
+// keys 16 k + 8 g + 0..7 in registers 8 (k & 1) .. 8 (k & 1) + 7 -- the
+// B-operand layout of the 16-deep sub-step k of the P V product.
+__device__ __forceinline__ int pi_row(int r)
+{
+    const int q = r >> 3, g = (r >> 2) & 1, e = r & 3;
+    return 16 * (q >> 1) + 8 * g + 4 * (q & 1) + e;
+}
+
+template <int D>
+__global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
+{
+    constexpr int KP = D + 8;              // K tile row pitch (halves); the pad staggers LDS banks
+    constexpr int VP = AT_BK + 8;          // V^T tile row pitch (halves)
+    constexpr int NDB = D / 32;            // 32-row blocks of O^T
+    constexpr int NDD = D / 16;            // 16-deep steps over d
+    constexpr int CPR = D / 16;            // 16-code chunks per key
+    constexpr int IPT = AT_BK * CPR / AT_NT;   // chunks per thread per matrix
+    static_assert(D == 64 || D == 128, "head dimension");
+    static_assert(IPT >= 1 && AT_BK * CPR % AT_NT == 0, "tile");
+
+    __shared__ __attribute__((aligned(16))) _Float16 ks[AT_BK * KP];
+    __shared__ __attribute__((aligned(16))) _Float16 vt[D * VP];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int i = lane & 31, g = lane >> 5;
+    const int h = blockIdx.y;
+    const int qt = a.tiles_q - 1 - int(blockIdx.x);   // longest (causal) tiles first
+    const int q0 = qt * AT_BQ;
+    const int kvh = h / (a.heads / a.kv_heads);
+    const int off = a.s - a.m;                        // the queries are the last m positions
+    const int qrow = q0 + 32 * wave + i;
+
+    // Q fragments (B operand): lane (i, g) holds Q[qrow][16 dd + 8 g .. + 7]
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + int64_t(h) * a.m * D, uint32_t(a.m) * D * 2u);
+    f16x8 qf[NDD];
+#pragma unroll
+    for (int dd = 0; dd < NDD; ++dd) {
+        const uint32_t v = qrow < a.m ? (uint32_t(qrow) * D + uint32_t(16 * dd + 8 * g)) * 2u : OOB;
+        qf[dd] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, v, 0, 0));
+    }
+
+    int t_end = (a.s + AT_BK - 1) / AT_BK;
+    if (a.causal)
+        t_end = min(t_end, (off + q0 + AT_BQ - 1) / AT_BK + 1);
+
+    // raw codes and scales of one tile, AT_BK * CPR chunks per matrix:
+    // chunk j = key j / CPR, 16 codes from d = 16 (j % CPR)
+    const uint32_t cache_rows = uint32_t(a.kv_heads) * uint32_t(a.s);
+    const __amdgpu_buffer_rsrc_t kqr = make_rsrc(a.kq, cache_rows * D);
+    const __amdgpu_buffer_rsrc_t vqr = make_rsrc(a.vq, cache_rows * D);
+    const __amdgpu_buffer_rsrc_t ksr = make_rsrc(a.ks, cache_rows * (D / 32) * 2u);
+    const __amdgpu_buffer_rsrc_t vsr = make_rsrc(a.vs, cache_rows * (D / 32) * 2u);
+    u32x4 kc[IPT], vc[IPT];
+    _Float16 kd[IPT], vd[IPT];
+    auto fetch = [&](int t) {
+#pragma unroll
+        for (int u = 0; u < IPT; ++u) {
+            const int j = tid + AT_NT * u, kk = j / CPR, c = j % CPR;
+            const int key = t * AT_BK + kk;
+            const uint32_t row = uint32_t(kvh) * uint32_t(a.s) + uint32_t(key);
+            const uint32_t cv = key < a.s ? row * D + uint32_t(16 * c) : OOB;
+            const uint32_t sv = key < a.s ? (row * (D / 32) + uint32_t(c >> 1)) * 2u : OOB;
+            kc[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kqr, cv, 0, 0));
+            vc[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vqr, cv, 0, 0));
+            kd[u] = load_f16(ksr, sv, 0);
+            vd[u] = load_f16(vsr, sv, 0);
+        }
+    };
+    fetch(0);
+
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            oacc[db][e] = 0.0f;
+    float mrow = -__builtin_inff(), lrow = 0.0f;
+    const int qpos = off + qrow;
+
+    // K rows this lane reads for the A operand, and the LDS offsets
+    const int krow0 = pi_row(i), krow1 = 32 + pi_row(i);
+
+    for (int t = 0; t < t_end; ++t) {
+        __syncthreads();   // every wave is done reading the previous tile
+#pragma unroll
+        for (int u = 0; u < IPT; ++u) {
+            const int j = tid + AT_NT * u, kk = j / CPR, c = j % CPR;
+            u32x4 lo, hi;
+            dequant16(kc[u], kd[u], lo, hi);
+            *reinterpret_cast<u32x4 *>(ks + kk * KP + 16 * c) = lo;
+            *reinterpret_cast<u32x4 *>(ks + kk * KP + 16 * c + 8) = hi;
+            dequant16(vc[u], vd[u], lo, hi);
+            const f16x8 vl = __builtin_bit_cast(f16x8, lo), vh = __builtin_bit_cast(f16x8, hi);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                vt[(16 * c + e) * VP + kk] = vl[e];
+                vt[(16 * c + 8 + e) * VP + kk] = vh[e];
+            }
+        }
+        if (t + 1 < t_end)
+            fetch(t + 1);
+        __syncthreads();
+
+        // S^T for keys 32 kb .. 32 kb + 31 of the tile
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                sacc[kb][e] = 0.0f;
+            const _Float16 *kp = ks + (kb ? krow1 : krow0) * KP + 8 * g;
+#pragma unroll
+            for (int dd = 0; dd < NDD; ++dd) {
+                const f16x8 ka = *reinterpret_cast<const f16x8 *>(kp + 16 * dd);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[dd], sacc[kb], 0, 0, 0);
+            }
+        }
+
+        // scores on the log2 scale; keys past the sequence or (causal) past
+        // the query's own position are -inf.  Register 4 q + e of block kb
+        // holds key 32 kb + 16 (q >> 1) + 8 g + 4 (q & 1) + e of the tile.
+        const int kbase = t * AT_BK;
+        const bool edge = kbase + AT_BK > a.s || (a.causal && kbase + AT_BK - 1 > off + q0 + 32 * wave);
+        float tmax = -__builtin_inff();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float v = sacc[kb][r] * a.scale_log2;
+                if (edge) {
+                    const int q = r >> 2, e = r & 3;
+                    const int key = kbase + 32 * kb + 16 * (q >> 1) + 8 * g + 4 * (q & 1) + e;
+                    if (key >= a.s || (a.causal && key > qpos))
+                        v = -__builtin_inff();
+                }
+                sacc[kb][r] = v;
+                tmax = __builtin_fmaxf(tmax, v);
+            }
+        tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float mnew = __builtin_fmaxf(mrow, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
+        float lsum = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(sacc[kb][r] - mnew);
+                sacc[kb][r] = p;
+                lsum += p;
+            }
+        lsum += __shfl_xor(lsum, 32);
+        lrow = lrow * alpha + lsum;
+        mrow = mnew;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                oacc[db][e] *= alpha;
+
+        // P as fp16 B fragments: sub-step k takes registers 8 (k & 1) .. + 7 of block k >> 1
+        f16x8 pf[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                pf[k][e] = _Float16(sacc[k >> 1][8 * (k & 1) + e]);
+
+        // O^T += V^T P^T
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const _Float16 *vp = vt + (32 * db + i) * VP + 8 * g;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const f16x8 va = *reinterpret_cast<const f16x8 *>(vp + 16 * k);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[k], oacc[db], 0, 0, 0);
+            }
+        }
+    }
+
+    // O[h][qrow][32 db + 8 q + 4 g + e] = O^T acc / row sum
+    if (qrow < a.m) {
+        const float inv = 1.0f / lrow;
+        _Float16 *orow = a.o + (int64_t(h) * a.m + qrow) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f16x2 lo2 = {_Float16(oacc[db][4 * q] * inv), _Float16(oacc[db][4 * q + 1] * inv)};
+                const f16x2 hi2 = {_Float16(oacc[db][4 * q + 2] * inv), _Float16(oacc[db][4 * q + 3] * inv)};
+                *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * q + 4 * g) = u32x2{as_u32(lo2), as_u32(hi2)};
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnProblem &p, hipStream_t stream)
+{
+    AttnArgs a;
+    a.q = p.q;
+    a.o = p.o;
+    a.kq = p.k_codes;
+    a.vq = p.v_codes;
+    a.ks = p.k_scales;
+    a.vs = p.v_scales;
+    a.heads = int(p.heads);
+    a.m = int(p.m);
+    a.kv_heads = int(p.kv_heads);
+    a.s = int(p.s);
+    a.causal = p.causal ? 1 : 0;
+    a.tiles_q = int(ceil_div(p.m, AT_BQ));
+    a.scale_log2 = p.scale * 1.4426950408889634f;
+    void *args[] = {&a};
+    const dim3 grid(unsigned(a.tiles_q), unsigned(a.heads)), block(AT_NT);
+    const void *fn = p.head_dim == 64 ? reinterpret_cast<const void *>(&attn_q8kv_kernel<64>)
+                                      : reinterpret_cast<const void *>(&attn_q8kv_kernel<128>);
+    return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
+}  // namespace qg

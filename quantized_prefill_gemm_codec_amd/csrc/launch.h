@@ -36,4 +36,17 @@ hipError_t launch_gemv(const GemmProblem &p, hipStream_t stream);
 // fp16 image of the weights, [n, ldw].
 hipError_t launch_dequant(const GemmProblem &p, _Float16 *out, int64_t ldw, hipStream_t stream);
 
+// Attention over a Q8_0 KV cache: Q, O [heads, m, head_dim] fp16; K, V as int8
+// codes [kv_heads * s, head_dim] and fp16 scales [kv_heads * s, head_dim / 32].
+struct AttnProblem {
+    const _Float16 *q;
+    _Float16 *o;
+    const uint8_t *k_codes, *v_codes;
+    const _Float16 *k_scales, *v_scales;
+    int64_t heads, m, head_dim, kv_heads, s;
+    bool causal;
+    float scale;
+};
+hipError_t launch_attention(const AttnProblem &p, hipStream_t stream);
+
 }  // namespace qg

@@ -329,4 +329,26 @@ qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonica
     return QG_OK;
 }
 
+qg_status qg_pack_kv_host(const void *canonical, size_t canonical_bytes, int64_t rows, int64_t head_dim,
+                          void *codes, void *scales)
+{
+    if (!canonical || !codes || !scales)
+        return QG_ERR_NULL;
+    if (rows < 1 || head_dim < 32 || head_dim % 32 != 0 || rows > (int64_t(1) << 31) || head_dim > 4096)
+        return QG_ERR_SHAPE;
+    const int64_t nb = head_dim / 32;
+    if (canonical_bytes < size_t(rows) * size_t(nb) * 34)
+        return QG_ERR_SIZE;
+    const uint8_t *c = static_cast<const uint8_t *>(canonical);
+    uint8_t *q = static_cast<uint8_t *>(codes);
+    uint8_t *sc = static_cast<uint8_t *>(scales);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = c + (r * nb + b) * 34;
+            memcpy(sc + (r * nb + b) * 2, blk, 2);
+            memcpy(q + r * head_dim + b * 32, blk + 2, 32);
+        }
+    return QG_OK;
+}
+
 }  // extern "C"

@@ -337,3 +337,56 @@ WORKLOADS = {
     "ternary_gemv_1x4096x14336": Workload("ternary_gemv_1x4096x14336", "gemv", CODEC_TERNARY, 1, 4096, 14336,
                                           BASE_SEED + 13),
 }
+
+
+T_Q, T_K, T_V = 5, 6, 7
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    """Attention over a Q8_0 KV cache: H query heads of M queries attend to
+    the S positions of KV heads shared by H / H_kv query heads each."""
+    name: str
+    heads: int
+    kv_heads: int
+    m: int
+    s: int
+    head_dim: int
+    causal: bool
+    seed: int
+
+    def q(self) -> np.ndarray:
+        """fp16 queries [H, M, D] ~N(0, 1)."""
+        return gen_x(self.heads * self.m, self.head_dim, self.seed, T_Q).reshape(self.heads, self.m, self.head_dim)
+
+    def kv(self):
+        """Canonical Q8_0 rows [H_kv * S, D] of K and of V: codes ~U{-127..127},
+        block scales ~U(0.01, 0.03), so elements spread over about +-3.8."""
+        rows = self.kv_heads * self.s
+        return (gen_q8_0(rows, self.head_dim, self.seed, T_K, d_range=(0.01, 0.03)),
+                gen_q8_0(rows, self.head_dim, self.seed, T_V, d_range=(0.01, 0.03)))
+
+    def visible_pairs(self) -> int:
+        if not self.causal:
+            return self.m * self.s
+        off = self.s - self.m
+        return sum(off + i + 1 for i in range(self.m))
+
+    def flops(self) -> int:
+        """2 D for the score and 2 D for the weighted sum of every visible (query, key) pair."""
+        return 4 * self.head_dim * self.heads * self.visible_pairs()
+
+    def algorithmic_bytes(self) -> int:
+        """Q and O in fp16 once, K and V as canonical Q8_0 once."""
+        cache = 2 * self.kv_heads * self.s * (self.head_dim // 32) * 34
+        return 2 * 2 * self.heads * self.m * self.head_dim + cache
+
+
+ATTN_WORKLOADS = {
+    # 8B-shape prefill attention: 32 query heads over 8 KV heads (grouped 4:1), D = 128, 2048 tokens, causal
+    "q8kv_attention_2048x2048_h32kv8_d128": AttnWorkload("q8kv_attention_2048x2048_h32kv8_d128", 32, 8, 2048, 2048, 128,
+                                                         True, BASE_SEED + 20),
+    # 1B-shape prefill attention: 32 heads, D = 64
+    "q8kv_attention_2048x2048_h32kv8_d64": AttnWorkload("q8kv_attention_2048x2048_h32kv8_d64", 32, 8, 2048, 2048, 64,
+                                                        True, BASE_SEED + 21),
+}

@@ -296,3 +296,38 @@ def test_prefill_heads_argument_errors():
 def test_status_strings():
     for st in qg.STATUS:
         assert qg.lib().qg_status_str(st)
+
+
+def test_pack_kv_host_splits_blocks():
+    rows, d = 5, 128
+    canon = synth.gen_q8_0(rows, d, 31)
+    L = qg.lib()
+    codes = np.empty(rows * d, np.uint8)
+    scales = np.empty(rows * (d // 32) * 2, np.uint8)
+    assert L.qg_pack_kv_host(canon.ctypes.data, canon.size, rows, d, codes.ctypes.data, scales.ctypes.data) == 0
+    blk = canon.reshape(rows, d // 32, 34)
+    assert np.array_equal(scales.reshape(rows, d // 32, 2), blk[:, :, :2])
+    assert np.array_equal(codes.reshape(rows, d // 32, 32), blk[:, :, 2:])
+    # decoded from the planar split, the values are the oracle's Q8_0 decode
+    w = codes.view(np.int8).reshape(rows, d).astype(np.float64) * np.repeat(
+        scales.view(np.float16).reshape(rows, d // 32).astype(np.float64), 32, axis=1)
+    assert np.array_equal(w, oracle.decode(oracle.Q8_0, canon, rows, d))
+    assert L.qg_pack_kv_host(canon.ctypes.data, canon.size - 1, rows, d, codes.ctypes.data, scales.ctypes.data) == -7
+    assert L.qg_pack_kv_host(canon.ctypes.data, canon.size, rows, 48, codes.ctypes.data, scales.ctypes.data) == -3
+    assert L.qg_pack_kv_host(0, canon.size, rows, d, codes.ctypes.data, scales.ctypes.data) == -1
+
+
+def _attn(L, **kw):
+    a = dict(q=FAKE, o=FAKE, heads=4, m=8, d=64, kq=FAKE, ks=FAKE, vq=FAKE, vs=FAKE, kvh=2, s=8, causal=1, scale=0.125)
+    a.update(kw)
+    return L.qattn_prefill_q8kv(a["q"], a["o"], a["heads"], a["m"], a["d"], a["kq"], a["ks"], a["vq"], a["vs"],
+                                a["kvh"], a["s"], a["causal"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(vs=0), -1), (dict(d=96), -3), (dict(d=32), -3), (dict(kvh=3), -3), (dict(heads=0), -3),
+    (dict(m=0), -3), (dict(s=7), -3), (dict(causal=2), -3), (dict(scale=0.0), -3), (dict(scale=float("nan")), -3),
+    (dict(scale=float("inf")), -3), (dict(heads=70000, kvh=1), -3), (dict(q=FAKE + 2), -4), (dict(ks=FAKE + 8), -4),
+])
+def test_attention_argument_errors(kw, status):
+    assert _attn(qg.lib(), **kw) == status
