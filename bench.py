@@ -4,8 +4,10 @@ One step = one launch of the hot path over the measured workload, with inputs
 already resident in HBM.  The headline workload is the 1B-shape MLP
 up-projection prefill (Q4_0 weights [8192, 2048], X fp16 [2048, 2048]); the
 line reports TFLOP/s (2*M*N*K per second) with its fraction of the fp16 dense
-MFMA peak.  The other workloads (MLX4 fused SwiGLU, Q2_0 GEMM, M=1 / M=64
-GEMV) are timed the same way under "secondary", each with its own roofline.
+MFMA peak.  The other workloads (MLX4 fused SwiGLU and GeGLU, the Q2_0, Q8_0,
+Q4_K, MLX4-G32 and ternary GEMMs, the direct-head projection, the M=1 / M=64
+GEMVs and the Q8_0-KV attention) are timed the same way under "secondary",
+each with its own roofline.
 
 Cold caches: every timed launch uses one of R rotated copies of weights, X and
 Y (R copies together exceed the 256 MB Infinity Cache), in the spirit of the
@@ -46,11 +48,12 @@ SECONDARY = ["mlx4_swiglu_2048x4096x14336", "q2_0_prefill_2048x4096x4096",
              "q4_k_prefill_2048x2048x8192", "q4_k_gemv_1x4096x14336",
              "ternary_prefill_2048x2048x8192", "ternary_gemv_1x4096x14336"]
 KERNEL_SOURCES = ["gemm.hip", "gemv.hip", "unpack.h", "planar.h", "lds_dma.h"]
+ATTN_SOURCES = ["attention.hip", "unpack.h"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "quantized_prefill_gemm_codec_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -134,6 +137,39 @@ def settle(torch, prep, settle_ms=SETTLE_MS):
     return n
 
 
+class AttnPrepared:
+    """R rotated device copies of an attention workload's queries, Q8_0 KV
+    cache and output; launch(i) calls the C-ABI entry point on copy i mod R."""
+
+    def __init__(self, torch, qg, wl, rotate=None):
+        self.wl = wl
+        q = wl.q()
+        kc, vc = wl.kv()
+        per_set = 2 * q.nbytes + kc.size + vc.size
+        if rotate is None:
+            rotate = max(2, min(16, -(-(MALL_BYTES + (32 << 20)) // per_set) + 1))
+        self.rotate = rotate
+        self.sets = []
+        for _ in range(rotate):
+            cache = qg.Q8KVCache.from_canonical(wl.kv_heads, wl.s, wl.head_dim, kc, vc)
+            qd = torch.from_numpy(q).cuda()
+            self.sets.append((qd, cache, torch.empty_like(qd)))
+        L = qg.lib()
+        stream = qg._stream(None)
+        scale = 1.0 / float(np.sqrt(wl.head_dim))
+        self.calls = [(L.qattn_prefill_q8kv, (qd.data_ptr(), o.data_ptr(), wl.heads, wl.m, wl.head_dim,
+                                              c.k_codes.data_ptr(), c.k_scales.data_ptr(), c.v_codes.data_ptr(),
+                                              c.v_scales.data_ptr(), wl.kv_heads, wl.s, 1 if wl.causal else 0,
+                                              scale, stream))
+                      for qd, c, o in self.sets]
+
+    def launch(self, i):
+        fn, args = self.calls[i % self.rotate]
+        st = fn(*args)
+        if st != 0:
+            raise RuntimeError(f"{fn.__name__} returned status {st}")
+
+
 def time_launches(torch, prep, steps, warmup, settle_ms=SETTLE_MS):
     settled = settle(torch, prep, settle_ms) if settle_ms > 0 else 0
     for i in range(warmup):
@@ -166,7 +202,7 @@ def load_traffic(name):
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     if not os.path.exists(path):
         return None
-    sha = kernel_source_hash()
+    sha = kernel_source_hash(ATTN_SOURCES if name in synth.ATTN_WORKLOADS else KERNEL_SOURCES)
     with open(path) as f:
         for line in f:
             if line.startswith("#") or "workload=" not in line:
@@ -289,6 +325,19 @@ def main():
             r2 = roofline(w2, ms2, load_traffic(name))
             sec[name] = {"us_per_launch": round(ms2 * 1e3, 2), "tflops": round(w2.flops() / (ms2 * 1e-3) / 1e12, 2),
                          "gbs": round(w2.algorithmic_bytes() / (ms2 * 1e-3) / 1e9, 1), "roofline": r2,
+                         "rotate": p2.rotate, "settle_launches": settled2}
+            print(f"# timed {name}: {ms2 * 1e3:.1f} us/launch", file=sys.stderr, flush=True)
+            del p2
+            torch.cuda.empty_cache()
+        for name, aw in synth.ATTN_WORKLOADS.items():
+            p2 = AttnPrepared(torch, qg, aw)
+            ms2, settled2 = time_launches(torch, p2, max(10, args.steps), args.warmup, args.settle_ms)
+            achieved = aw.flops() / (ms2 * 1e-3) / 1e12
+            sec[name] = {"us_per_launch": round(ms2 * 1e3, 2), "tflops": round(achieved, 2),
+                         "gbs": round(aw.algorithmic_bytes() / (ms2 * 1e-3) / 1e9, 1),
+                         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+                                      "traffic": load_traffic(name)},
                          "rotate": p2.rotate, "settle_launches": settled2}
             print(f"# timed {name}: {ms2 * 1e3:.1f} us/launch", file=sys.stderr, flush=True)
             del p2

@@ -10,10 +10,12 @@
 //
 // One workgroup of four wave64 handles 128 queries of one head; each wave owns
 // 32 of them for the whole key range.  Per tile of 64 keys:
-//  * the 256 threads turn the tile's int8 codes and fp16 block scales into
-//    fp16 K [64][D] (row-major) and V^T [D][64] in LDS -- each element is the
-//    correctly rounded q * d, the weights' Q8_0 rule; the raw codes of the next
-//    tile are already in registers (loaded one tile ahead);
+//  * the 256 threads turn the next tile's int8 codes and fp16 block scales
+//    into fp16 K [64][D] (row-major) and V^T [D][64] in the other half of a
+//    double-buffered LDS area -- each element is the correctly rounded q * d,
+//    the weights' Q8_0 rule; V is transposed in registers (8 keys x 4 d per
+//    thread) so that it is stored with 16-byte writes.  The raw codes are
+//    loaded one tile ahead of that, so one barrier per tile suffices;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_f16 (A = K rows, B = the wave's Q
 //    fragments, loaded once).  K rows are read in the order pi below, which
 //    makes each lane's 32 scores exactly the B fragments P^T needs for the
@@ -24,6 +26,8 @@
 //    2^(m_old - m_new);
 //  * O^T += V^T P^T (A = V^T rows from LDS, B = P as fp16).
 // The epilogue divides by the row sum and writes O [H, M, D] fp16.
+// Causal work per query tile grows linearly; workgroups are ordered so that
+// each heavy query tile is launched next to a light one (see tile_of).
 #include "launch.h"
 
 namespace qg {
@@ -64,6 +68,35 @@ __device__ __forceinline__ void dequant16(u32x4 c, _Float16 d, u32x4 &lo, u32x4 
     hi = u32x4{r[4], r[5], r[6], r[7]};
 }
 
+// Four codes (d .. d + 3 of one key, two's complement) -> two fp16 pairs
+// (d, d + 1), (d + 2, d + 3) of q * scale, in the rounding of dequant16.
+__device__ __forceinline__ void dequant4(uint32_t c, _Float16 d, uint32_t &p01, uint32_t &p23)
+{
+    const f16x2 dd = {d, d};
+    const f16x2 off = {_Float16(1152.0f), _Float16(1152.0f)};
+    const uint32_t x = c ^ 0x80808080u;
+    p01 = as_u32((as_f16x2(__builtin_amdgcn_perm(x, x, 0x0C010C00u) | 0x64006400u) - off) * dd);
+    p23 = as_u32((as_f16x2(__builtin_amdgcn_perm(x, x, 0x0C030C02u) | 0x64006400u) - off) * dd);
+}
+
+// Query tile and head of workgroup `lin` (0 .. tiles_q * heads - 1).  The
+// query heads [0, H/2) take their tiles longest (causal) first, the heads
+// [H/2, H) shortest first, so that workgroups lin and lin + half -- dispatched
+// to the same compute unit when all of them are resident -- carry
+// tiles_q - 1 key-tile rows of work between them.  A bijection for any H.
+__device__ __forceinline__ void tile_of(int lin, int tiles_q, int heads, int &qt, int &h)
+{
+    const int hh = heads / 2, half = hh * tiles_q;
+    if (lin < half) {
+        qt = tiles_q - 1 - lin % tiles_q;
+        h = lin / tiles_q;
+    } else {
+        const int l2 = lin - half;
+        qt = l2 % tiles_q;
+        h = hh + l2 / tiles_q;
+    }
+}
+
 // A-operand row r (0..31) of a 32-key block reads key pi(r): the MFMA puts
 // row 8 q + 4 g + e of the product in register 4 q + e of lane half g, and
 // pi(8 q + 4 g + e) = 16 (q >> 1) + 8 g + 4 (q & 1) + e hands lane half g the
@@ -82,19 +115,22 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
     constexpr int VP = AT_BK + 8;          // V^T tile row pitch (halves)
     constexpr int NDB = D / 32;            // 32-row blocks of O^T
     constexpr int NDD = D / 16;            // 16-deep steps over d
-    constexpr int CPR = D / 16;            // 16-code chunks per key
-    constexpr int IPT = AT_BK * CPR / AT_NT;   // chunks per thread per matrix
+    constexpr int CPR = D / 16;            // 16-code chunks per key (K)
+    constexpr int IPT = AT_BK * CPR / AT_NT;   // K chunks per thread
+    constexpr int VITEMS = AT_BK * D / 32;           // V items of 8 keys x 4 d per tile
+    constexpr int VIT = (VITEMS + AT_NT - 1) / AT_NT;   // per thread (D = 64: half the threads)
+    constexpr int VDG = D / 4;             // 4-wide d groups per key
     static_assert(D == 64 || D == 128, "head dimension");
-    static_assert(IPT >= 1 && AT_BK * CPR % AT_NT == 0, "tile");
+    static_assert(IPT >= 1 && AT_BK * CPR % AT_NT == 0 && VITEMS % 64 == 0, "tile");
 
-    __shared__ __attribute__((aligned(16))) _Float16 ks[AT_BK * KP];
-    __shared__ __attribute__((aligned(16))) _Float16 vt[D * VP];
+    __shared__ __attribute__((aligned(16))) _Float16 ks[2][AT_BK * KP];
+    __shared__ __attribute__((aligned(16))) _Float16 vt[2][D * VP];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int i = lane & 31, g = lane >> 5;
-    const int h = blockIdx.y;
-    const int qt = a.tiles_q - 1 - int(blockIdx.x);   // longest (causal) tiles first
+    int qt, h;
+    tile_of(int(blockIdx.x), a.tiles_q, a.heads, qt, h);
     const int q0 = qt * AT_BQ;
     const int kvh = h / (a.heads / a.kv_heads);
     const int off = a.s - a.m;                        // the queries are the last m positions
@@ -120,8 +156,12 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
     const __amdgpu_buffer_rsrc_t vqr = make_rsrc(a.vq, cache_rows * D);
     const __amdgpu_buffer_rsrc_t ksr = make_rsrc(a.ks, cache_rows * (D / 32) * 2u);
     const __amdgpu_buffer_rsrc_t vsr = make_rsrc(a.vs, cache_rows * (D / 32) * 2u);
-    u32x4 kc[IPT], vc[IPT];
-    _Float16 kd[IPT], vd[IPT];
+    // K item j: key j / CPR, codes 16 (j % CPR) .. + 15.  V item j: keys
+    // 8 (j / VDG) .. + 7, codes 4 (j % VDG) .. + 3 of each.
+    u32x4 kc[IPT];
+    _Float16 kd[IPT];
+    uint32_t vc[VIT][8];
+    _Float16 vd[VIT][8];
     auto fetch = [&](int t) {
 #pragma unroll
         for (int u = 0; u < IPT; ++u) {
@@ -131,12 +171,63 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
             const uint32_t cv = key < a.s ? row * D + uint32_t(16 * c) : OOB;
             const uint32_t sv = key < a.s ? (row * (D / 32) + uint32_t(c >> 1)) * 2u : OOB;
             kc[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kqr, cv, 0, 0));
-            vc[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vqr, cv, 0, 0));
             kd[u] = load_f16(ksr, sv, 0);
-            vd[u] = load_f16(vsr, sv, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < VIT; ++u) {
+            const int j = tid + AT_NT * u, k8 = j / VDG, c4 = j % VDG;
+            if (j >= VITEMS)
+                break;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int key = t * AT_BK + 8 * k8 + e;
+                const uint32_t row = uint32_t(kvh) * uint32_t(a.s) + uint32_t(key);
+                const uint32_t cv = key < a.s ? row * D + uint32_t(4 * c4) : OOB;
+                const uint32_t sv = key < a.s ? (row * (D / 32) + uint32_t(c4 >> 3)) * 2u : OOB;
+                vc[u][e] = __builtin_amdgcn_raw_buffer_load_b32(vqr, cv, 0, 0);
+                vd[u][e] = load_f16(vsr, sv, 0);
+            }
+        }
+    };
+    // dequantize the fetched tile into LDS buffer b
+    auto stage = [&](int b) {
+#pragma unroll
+        for (int u = 0; u < IPT; ++u) {
+            const int j = tid + AT_NT * u, kk = j / CPR, c = j % CPR;
+            u32x4 lo, hi;
+            dequant16(kc[u], kd[u], lo, hi);
+            *reinterpret_cast<u32x4 *>(&ks[b][kk * KP + 16 * c]) = lo;
+            *reinterpret_cast<u32x4 *>(&ks[b][kk * KP + 16 * c + 8]) = hi;
+        }
+#pragma unroll
+        for (int u = 0; u < VIT; ++u) {
+            const int j = tid + AT_NT * u, k8 = j / VDG, c4 = j % VDG;
+            if (j >= VITEMS)
+                break;
+            uint32_t p01[8], p23[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                dequant4(vc[u][e], vd[u][e], p01[e], p23[e]);
+            // row d = 4 c4 + r of V^T gets keys 8 k8 .. + 7: the low (r even)
+            // or high (r odd) halves of keys e, e + 1 paired by v_perm_b32
+            u32x4 rows[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                rows[0][e] = __builtin_amdgcn_perm(p01[2 * e + 1], p01[2 * e], 0x05040100u);
+                rows[1][e] = __builtin_amdgcn_perm(p01[2 * e + 1], p01[2 * e], 0x07060302u);
+                rows[2][e] = __builtin_amdgcn_perm(p23[2 * e + 1], p23[2 * e], 0x05040100u);
+                rows[3][e] = __builtin_amdgcn_perm(p23[2 * e + 1], p23[2 * e], 0x07060302u);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<u32x4 *>(&vt[b][(4 * c4 + r) * VP + 8 * k8]) = rows[r];
         }
     };
     fetch(0);
+    stage(0);
+    if (t_end > 1)
+        fetch(1);
+    __syncthreads();
 
     f32x16 oacc[NDB];
 #pragma unroll
@@ -144,32 +235,21 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
             oacc[db][e] = 0.0f;
-    float mrow = -__builtin_inff(), lrow = 0.0f;
+    float mrow = -__builtin_inff(), lrow = 0.0f;   // running maximum (log2 scale) and sum
     const int qpos = off + qrow;
 
     // K rows this lane reads for the A operand, and the LDS offsets
     const int krow0 = pi_row(i), krow1 = 32 + pi_row(i);
 
     for (int t = 0; t < t_end; ++t) {
-        __syncthreads();   // every wave is done reading the previous tile
-#pragma unroll
-        for (int u = 0; u < IPT; ++u) {
-            const int j = tid + AT_NT * u, kk = j / CPR, c = j % CPR;
-            u32x4 lo, hi;
-            dequant16(kc[u], kd[u], lo, hi);
-            *reinterpret_cast<u32x4 *>(ks + kk * KP + 16 * c) = lo;
-            *reinterpret_cast<u32x4 *>(ks + kk * KP + 16 * c + 8) = hi;
-            dequant16(vc[u], vd[u], lo, hi);
-            const f16x8 vl = __builtin_bit_cast(f16x8, lo), vh = __builtin_bit_cast(f16x8, hi);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                vt[(16 * c + e) * VP + kk] = vl[e];
-                vt[(16 * c + 8 + e) * VP + kk] = vh[e];
-            }
+        const int b = t & 1;
+        // the tile after this one goes into the other buffer: its last
+        // readers finished before the barrier that ended the previous step
+        if (t + 1 < t_end) {
+            stage(b ^ 1);
+            if (t + 2 < t_end)
+                fetch(t + 2);
         }
-        if (t + 1 < t_end)
-            fetch(t + 1);
-        __syncthreads();
 
         // S^T for keys 32 kb .. 32 kb + 31 of the tile
         f32x16 sacc[2];
@@ -178,7 +258,7 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 sacc[kb][e] = 0.0f;
-            const _Float16 *kp = ks + (kb ? krow1 : krow0) * KP + 8 * g;
+            const _Float16 *kp = &ks[b][(kb ? krow1 : krow0) * KP + 8 * g];
 #pragma unroll
             for (int dd = 0; dd < NDD; ++dd) {
                 const f16x8 ka = *reinterpret_cast<const f16x8 *>(kp + 16 * dd);
@@ -191,41 +271,47 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
         // holds key 32 kb + 16 (q >> 1) + 8 g + 4 (q & 1) + e of the tile.
         const int kbase = t * AT_BK;
         const bool edge = kbase + AT_BK > a.s || (a.causal && kbase + AT_BK - 1 > off + q0 + 32 * wave);
+        // (the maximum is taken on the raw scores: the scale is positive)
         float tmax = -__builtin_inff();
+        if (edge) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float v = sacc[kb][r] * a.scale_log2;
-                if (edge) {
+                for (int r = 0; r < 16; ++r) {
                     const int q = r >> 2, e = r & 3;
                     const int key = kbase + 32 * kb + 16 * (q >> 1) + 8 * g + 4 * (q & 1) + e;
                     if (key >= a.s || (a.causal && key > qpos))
-                        v = -__builtin_inff();
+                        sacc[kb][r] = -__builtin_inff();
                 }
-                sacc[kb][r] = v;
-                tmax = __builtin_fmaxf(tmax, v);
-            }
-        tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                tmax = __builtin_fmaxf(tmax, sacc[kb][r]);
+        tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32)) * a.scale_log2;
         const float mnew = __builtin_fmaxf(mrow, tmax);
-        const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
         float lsum = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(sacc[kb][r] - mnew);
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], a.scale_log2, -mnew));
                 sacc[kb][r] = p;
                 lsum += p;
             }
         lsum += __shfl_xor(lsum, 32);
-        lrow = lrow * alpha + lsum;
+        if (__builtin_amdgcn_ballot_w64(mnew != mrow) != 0) {   // some row's maximum moved: rescale
+            const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
+            lrow *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    oacc[db][e] *= alpha;
+        }
+        lrow += lsum;
         mrow = mnew;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                oacc[db][e] *= alpha;
 
         // P as fp16 B fragments: sub-step k takes registers 8 (k & 1) .. + 7 of block k >> 1
         f16x8 pf[4];
@@ -238,13 +324,14 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
         // O^T += V^T P^T
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-            const _Float16 *vp = vt + (32 * db + i) * VP + 8 * g;
+            const _Float16 *vp = &vt[b][(32 * db + i) * VP + 8 * g];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const f16x8 va = *reinterpret_cast<const f16x8 *>(vp + 16 * k);
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[k], oacc[db], 0, 0, 0);
             }
         }
+        __syncthreads();   // tile t's buffer is free; tile t + 1's is written
     }
 
     // O[h][qrow][32 db + 8 q + 4 g + e] = O^T acc / row sum
@@ -281,7 +368,7 @@ hipError_t launch_attention(const AttnProblem &p, hipStream_t stream)
     a.tiles_q = int(ceil_div(p.m, AT_BQ));
     a.scale_log2 = p.scale * 1.4426950408889634f;
     void *args[] = {&a};
-    const dim3 grid(unsigned(a.tiles_q), unsigned(a.heads)), block(AT_NT);
+    const dim3 grid(unsigned(a.tiles_q * a.heads)), block(AT_NT);
     const void *fn = p.head_dim == 64 ? reinterpret_cast<const void *>(&attn_q8kv_kernel<64>)
                                       : reinterpret_cast<const void *>(&attn_q8kv_kernel<128>);
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
