@@ -361,9 +361,10 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     constexpr int NX = X_BYTES / 1024, NWI = W_BYTES / WDMA, NSI = (S_BYTES + 255) / 256;   // DMA ops per slice
     constexpr int XPW = NX / NWT, WPW = (NWI + NWT - 1) / NWT, SPW = (NSI + NWT - 1) / NWT;
     constexpr int VMIN = XPW + NWI / NWT + NSI / NWT;       // fewest DMA ops any wave issues per stage
-    constexpr int VWAIT = (AHEAD - 1) * VMIN;               // DMA ops that may stay in flight
+    constexpr int VMAX = XPW + WPW + SPW;                   // most
+    constexpr int VWAIT = (AHEAD - 1) * VMAX;               // DMA ops that may stay in flight, at most
     static_assert(NX % NWT == 0 && W_BYTES % 1024 == 0 && SLICE % 256 == 0, "dma tiling");
-    static_assert((FM == 1 || FM % 2 == 0) && VMIN >= 1 && NSTAGE >= 3 && VWAIT < 64, "tile");
+    static_assert((FM == 1 || FM % 2 == 0) && VMIN >= 1 && NSTAGE >= 3 && VWAIT < 64 && VMAX - VMIN <= 2, "tile");
     static_assert(!(GLU && WK > 1), "the split-K epilogue sums plain GEMM partials");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
@@ -449,6 +450,28 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
         const uint32_t src = CODEC == Q4_K && o >= 128 ? uint32_t(o) - 128u + 512u : uint32_t(o);
         sv[u] = (j < NSI && b < S_BYTES && rg0 + rg < a.groups) ? uint32_t(rg0 + rg) * pitch + src : OOB;
     }
+
+    // Waves issue different numbers of DMA ops per stage (the code and scale
+    // instructions are spread over the slice's waves), so each waits for its
+    // own count: stage t+1 has landed once at most this wave's ops of the
+    // AHEAD-1 newer stages remain.  Waiting for fewer (a shared, smaller
+    // count) would also wait for loads just issued for the newest stage.
+    int nops = XPW;
+#pragma unroll
+    for (int u = 0; u < WPW; ++u)
+        nops += (wr + NWT * u < NWI) ? 1 : 0;
+#pragma unroll
+    for (int u = 0; u < SPW; ++u)
+        nops += (wr + NWT * u < NSI) ? 1 : 0;
+    nops = __builtin_amdgcn_readfirstlane(nops);
+    auto wait_stage = [&]() {
+        if (nops >= VMIN + 2)
+            wait_vmcnt<(AHEAD - 1) * (VMIN + 2 <= VMAX ? VMIN + 2 : VMIN)>();
+        else if (nops == VMIN + 1)
+            wait_vmcnt<(AHEAD - 1) * (VMIN + 1 <= VMAX ? VMIN + 1 : VMIN)>();
+        else
+            wait_vmcnt<(AHEAD - 1) * VMIN>();
+    };
 
     // iteration i of this wave's slice = k-step kbase + i; past the end of K
     // (last slice of a ragged split) every vector offset is out of range, so
@@ -562,7 +585,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i)
         issue_stage(min(i, kq - 1), i);
-    wait_vmcnt<VWAIT>();
+    wait_stage();
     __syncthreads();
     LaneCodes<CODEC> cw[NMAT][FN];
     const int slice = wk * SLICE;
@@ -585,11 +608,12 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
                 read_x(sp, s + 1, xf[cur ^ 1]);
                 unpack(cw, s + 1, wf[cur ^ 1]);
             } else {
-                // stage t+1 has landed once at most the newest AHEAD-1 stages'
-                // DMAs remain; after the barrier nobody reads stage t again.
+                // stage t+1 has landed once at most this wave's DMAs of the
+                // newest AHEAD-1 stages remain (wait_stage); after the
+                // barrier nobody reads stage t again.
                 // sched_barrier: sub-step 3's operands stay ahead of the wait.
                 __builtin_amdgcn_sched_barrier(0);
-                wait_vmcnt<VWAIT>();
+                wait_stage();
                 __syncthreads();
                 const char *np = lds + ((t + 1) % NSTAGE) * STAGE + slice;
                 read_w(np, cw);
