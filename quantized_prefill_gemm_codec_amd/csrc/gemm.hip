@@ -27,6 +27,8 @@
 // gemm_dma_kernel (M > 128, and M <= 64 with a split k-loop): X tiles, code
 // chunks and scale records all reach LDS by hardware DMA a few k-steps ahead
 // of use; see the comment above the kernel.
+#include <type_traits>
+
 #include "launch.h"
 #include "lds_dma.h"
 
@@ -75,6 +77,15 @@ template <int GLU> __device__ __forceinline__ float glu_mul(float g, float u)
         return sigmoid_mul(g, g, u);
     else
         return sigmoid_mul(g, 1.5957691216057308f * __builtin_fmaf(0.044715f * g, g * g, g), u);
+}
+
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), unrolled.
+template <int N, int I = 0, class F> __device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
 }
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
@@ -597,10 +608,12 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     f16x8 wf[2][NMAT][FN];
     read_x(lds + slice, 0, xf[0]);
     unpack(cw, 0, wf[0]);
-    for (int t = 0; t < kq; ++t) {
-        const int st = t % NSTAGE;
-        issue_stage(min(t + AHEAD, kq - 1), (t + AHEAD) % NSTAGE);
-        const char *sp = lds + st * STAGE + slice;
+    // one k-step; ST = t % NSTAGE is a compile-time constant (the loop below
+    // is unrolled by NSTAGE), so every LDS stage address folds to a constant
+    auto kstep = [&](int t, auto stc) {
+        constexpr int ST = decltype(stc)::value;
+        issue_stage(min(t + AHEAD, kq - 1), (ST + AHEAD) % NSTAGE);
+        const char *sp = lds + ST * STAGE + slice;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int cur = s & 1;
@@ -615,7 +628,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
                 __builtin_amdgcn_sched_barrier(0);
                 wait_stage();
                 __syncthreads();
-                const char *np = lds + ((t + 1) % NSTAGE) * STAGE + slice;
+                const char *np = lds + ((ST + 1) % NSTAGE) * STAGE + slice;
                 read_w(np, cw);
                 read_x(np, 0, xf[cur ^ 1]);
                 unpack(cw, 0, wf[cur ^ 1]);
@@ -638,7 +651,12 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
                     __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
             }
         }
-    }
+    };
+    for (int t0 = 0; t0 < kq; t0 += NSTAGE)
+        static_for<NSTAGE>([&](auto u) {
+            if (t0 + int(decltype(u)::value) < kq)
+                kstep(t0 + int(decltype(u)::value), u);
+        });
 
     // ---- epilogue: fp16 tile staged in LDS, then whole-row 16-byte stores ----
     wait_vmcnt<0>();
