@@ -151,11 +151,13 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
 
     // raw codes and scales of one tile, AT_BK * CPR chunks per matrix:
     // chunk j = key j / CPR, 16 codes from d = 16 (j % CPR)
-    const uint32_t cache_rows = uint32_t(a.kv_heads) * uint32_t(a.s);
-    const __amdgpu_buffer_rsrc_t kqr = make_rsrc(a.kq, cache_rows * D);
-    const __amdgpu_buffer_rsrc_t vqr = make_rsrc(a.vq, cache_rows * D);
-    const __amdgpu_buffer_rsrc_t ksr = make_rsrc(a.ks, cache_rows * (D / 32) * 2u);
-    const __amdgpu_buffer_rsrc_t vsr = make_rsrc(a.vs, cache_rows * (D / 32) * 2u);
+    // descriptors over this KV head's s rows: a vector offset at or past s
+    // rows reads as zero
+    const int64_t head_row = int64_t(kvh) * a.s;
+    const __amdgpu_buffer_rsrc_t kqr = make_rsrc(a.kq + head_row * D, uint32_t(a.s) * D);
+    const __amdgpu_buffer_rsrc_t vqr = make_rsrc(a.vq + head_row * D, uint32_t(a.s) * D);
+    const __amdgpu_buffer_rsrc_t ksr = make_rsrc(a.ks + head_row * (D / 32), uint32_t(a.s) * (D / 32) * 2u);
+    const __amdgpu_buffer_rsrc_t vsr = make_rsrc(a.vs + head_row * (D / 32), uint32_t(a.s) * (D / 32) * 2u);
     // K item j: key j / CPR, codes 16 (j % CPR) .. + 15.  V item j: keys
     // 8 (j / VDG) .. + 7, codes 4 (j % VDG) .. + 3 of each.
     u32x4 kc[IPT];
@@ -166,26 +168,37 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
 #pragma unroll
         for (int u = 0; u < IPT; ++u) {
             const int j = tid + AT_NT * u, kk = j / CPR, c = j % CPR;
-            const int key = t * AT_BK + kk;
-            const uint32_t row = uint32_t(kvh) * uint32_t(a.s) + uint32_t(key);
-            const uint32_t cv = key < a.s ? row * D + uint32_t(16 * c) : OOB;
-            const uint32_t sv = key < a.s ? (row * (D / 32) + uint32_t(c >> 1)) * 2u : OOB;
-            kc[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kqr, cv, 0, 0));
-            kd[u] = load_f16(ksr, sv, 0);
+            const uint32_t key = uint32_t(t * AT_BK + kk);
+            const bool in = key < uint32_t(a.s);
+            kc[u] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(kqr, in ? key * D + uint32_t(16 * c) : OOB, 0, 0));
+            kd[u] = load_f16(ksr, in ? (key * (D / 32) + uint32_t(c >> 1)) * 2u : OOB, 0);
         }
 #pragma unroll
         for (int u = 0; u < VIT; ++u) {
             const int j = tid + AT_NT * u, k8 = j / VDG, c4 = j % VDG;
             if (j >= VITEMS)
                 break;
+            // keys 8 k8 .. + 7 are D (codes) and D / 16 (scale bytes) apart:
+            // inside the sequence one vector offset serves all eight (the key
+            // goes into the instruction offset); the tile that crosses s puts
+            // each key past it out of range by its vector offset
+            const uint32_t key0 = uint32_t(t * AT_BK + 8 * k8);
+            const uint32_t cv = key0 * D + uint32_t(4 * c4);
+            const uint32_t sv = (key0 * (D / 32) + uint32_t(c4 >> 3)) * 2u;
+            if (t * AT_BK + AT_BK <= a.s) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int key = t * AT_BK + 8 * k8 + e;
-                const uint32_t row = uint32_t(kvh) * uint32_t(a.s) + uint32_t(key);
-                const uint32_t cv = key < a.s ? row * D + uint32_t(4 * c4) : OOB;
-                const uint32_t sv = key < a.s ? (row * (D / 32) + uint32_t(c4 >> 3)) * 2u : OOB;
-                vc[u][e] = __builtin_amdgcn_raw_buffer_load_b32(vqr, cv, 0, 0);
-                vd[u][e] = load_f16(vsr, sv, 0);
+                for (int e = 0; e < 8; ++e) {
+                    vc[u][e] = __builtin_amdgcn_raw_buffer_load_b32(vqr, cv + uint32_t(e * D), 0, 0);
+                    vd[u][e] = load_f16(vsr, sv + uint32_t(e * (D / 16)), 0);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const bool in = key0 + uint32_t(e) < uint32_t(a.s);
+                    vc[u][e] = __builtin_amdgcn_raw_buffer_load_b32(vqr, in ? cv + uint32_t(e * D) : OOB, 0, 0);
+                    vd[u][e] = load_f16(vsr, in ? sv + uint32_t(e * (D / 16)) : OOB, 0);
+                }
             }
         }
     };
