@@ -97,6 +97,11 @@ __device__ __forceinline__ void tile_of(int lin, int tiles_q, int heads, int &qt
     }
 }
 
+// V^T row d keeps its chunk c (keys 8 c .. 8 c + 7) at chunk position
+// c ^ vswz(d): the MFMA reads (16 rows, one chunk each) hit distinct banks and
+// the 16-byte stores of consecutive threads (rows 4 apart) at most two-way.
+__device__ __forceinline__ int vswz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
+
 // A-operand row r (0..31) of a 32-key block reads key pi(r): the MFMA puts
 // row 8 q + 4 g + e of the product in register 4 q + e of lane half g, and
 // pi(8 q + 4 g + e) = 16 (q >> 1) + 8 g + 4 (q & 1) + e hands lane half g the
@@ -112,7 +117,7 @@ template <int D>
 __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
 {
     constexpr int KP = D + 8;              // K tile row pitch (halves); the pad staggers LDS banks
-    constexpr int VP = AT_BK + 8;          // V^T tile row pitch (halves)
+    constexpr int VP = AT_BK;              // V^T tile row pitch (halves): 8 chunks of 8 keys, swizzled
     constexpr int NDB = D / 32;            // 32-row blocks of O^T
     constexpr int NDD = D / 16;            // 16-deep steps over d
     constexpr int CPR = D / 16;            // 16-code chunks per key (K)
@@ -232,8 +237,10 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
                 rows[3][e] = __builtin_amdgcn_perm(p23[2 * e + 1], p23[2 * e], 0x07060302u);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                *reinterpret_cast<u32x4 *>(&vt[b][(4 * c4 + r) * VP + 8 * k8]) = rows[r];
+            for (int r = 0; r < 4; ++r) {
+                const int d = 4 * c4 + r;
+                *reinterpret_cast<u32x4 *>(&vt[b][d * VP + 8 * (k8 ^ vswz(d))]) = rows[r];
+            }
         }
     };
     fetch(0);
@@ -337,10 +344,11 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
         // O^T += V^T P^T
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-            const _Float16 *vp = &vt[b][(32 * db + i) * VP + 8 * g];
+            const int d = 32 * db + i;
+            const _Float16 *vp = &vt[b][d * VP];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const f16x8 va = *reinterpret_cast<const f16x8 *>(vp + 16 * k);
+                const f16x8 va = *reinterpret_cast<const f16x8 *>(vp + 8 * ((2 * k + g) ^ vswz(d)));
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[k], oacc[db], 0, 0, 0);
             }
         }
