@@ -7,13 +7,19 @@
 // first cycles and as little VALU per byte as the codec allows.
 //
 // GEMV kernel (1 <= M <= 4): one workgroup of GEMV_NW waves per 32-row group.
-//  * Wave w owns k-steps [w * per, (w + 1) * per) of the row group and keeps
+//  * Wave w owns k-steps w, w + NW, w + 2 NW, ... of the row group and keeps
 //    GEMV_PF of them in flight: per k-step one 128-bit (64-bit for Q2_0) code
-//    load and one scale load per lane, contiguous across the wave.  The first
-//    batch is issued before X [M, K] is staged in LDS, so the X latency hides
-//    behind it; every consumed slot is refilled with the k-step one batch on.
-//    (Eight waves with four slots each measured fastest on the 14336 x 4096
-//    Q4_0 decode shape: more loads in flight per wave did not help.)
+//    load and one scale load per lane, contiguous across the wave, so the
+//    eight waves together stream one contiguous run of the row group's codes
+//    at a time.  Code loads carry the non-temporal hint (each byte is read
+//    once), except ternary's three partial loads of one chunk, which share
+//    cache lines.
+//  * X [M, K] reaches LDS by DMA issued before the first batch of codes; the
+//    wait for it leaves those codes in flight.  Every consumed slot is
+//    refilled with the k-step one batch on, after its last use, so the load
+//    reuses the slot's registers.  (Eight waves with four slots each measured
+//    fastest on the 14336 x 4096 Q4_0 decode shape: eight slots, or sixteen
+//    or four waves, were slower.)
 //  * The 1024 offset of the mantissa trick is not subtracted per weight:
 //    slice_dots dots the raw (1024 + 2^f q) halves with X and block_sum removes
 //    the offsets and the codec zero point once per 32-weight slice with a term
@@ -21,6 +27,7 @@
 //  * Lane halves, then waves, are reduced in a fixed order: results are
 //    bit-identical from run to run.
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace qg {
 namespace {
@@ -39,9 +46,11 @@ struct GemvArgs {
     int m, n, k, ldx, ldy;
     int groups, ksteps, kb128;
     int head_dim;            // 0: row-major Y; > 0: direct-head layout
-    int per;                 // k-steps per wave
     int x_lds;               // bytes of the X region
 };
+
+// memory instructions one load_lane issues
+template <int CODEC> constexpr int lane_loads() { return CODEC == TERNARY ? 4 : (CODEC == Q8_0 || CODEC == Q4_K) ? 3 : 2; }
 
 template <int CODEC> constexpr int corr_floats() { return CODEC == MLX4_G64 || CODEC == MLX4_G32 || CODEC == Q4_K ? 2 : 1; }
 
@@ -221,25 +230,35 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
     const int rg = blockIdx.x;
     const uint32_t magic = magic1024();
 
-    const int t0 = min(wave * a.per, a.ksteps);
-    const int t1 = min(a.ksteps, t0 + a.per);
-
-    // the first GEMV_PF k-steps of codes and scales
+    const int t1 = a.ksteps;
     const PlaneRsrc w = plane_rsrc(a.w);
     const LaneOffsets lo = lane_offsets<CODEC>(rg, a.groups, lane);
+    LaneOffsets none = lo;
+    none.q = none.s = none.s2 = none.q2 = none.q3 = OOB;
+    // codes and scales of k-step t; past the end the vector offsets are out
+    // of range (zeros), so every call issues exactly lane_loads<CODEC>()
+    // memory instructions
+    auto fetch = [&](int t) {
+        return load_lane<CODEC, CODEC != TERNARY>(w, t < t1 ? lo : none, rg, min(t, t1 - 1), a.ksteps, a.kb128);
+    };
+    {
+        const u32x4 xw = rsrc_words(a.x, a.x_bytes);
+        const uint32_t lbase = lds_u32(lds);
+        const int xch = MM * kchunks, nxi = (xch + 63) >> 6;
+        for (int j = wave; j < nxi; j += GEMV_NW) {
+            const int q = j * 64 + lane;
+            const int mr = q / kchunks, ch = q - mr * kchunks;
+            const uint32_t off = (q < xch && mr < a.m && ch * 8 < a.k)
+                                     ? (uint32_t(mr) * uint32_t(a.ldx) + uint32_t(ch) * 8u) * 2u : OOB;
+            dma_b128(xw, off, 0, lbase + uint32_t(j) * 1024u);
+        }
+    }
     LaneCodes<CODEC> lc[PF];
 #pragma unroll
     for (int u = 0; u < PF; ++u)
-        if (t0 + u < t1)
-            lc[u] = load_lane<CODEC>(w, lo, rg, t0 + u, a.ksteps, a.kb128);
-
-    // X rows into LDS
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
-    for (int q = tid; q < MM * kchunks; q += GEMV_NT) {
-        const int mr = q / kchunks, ch = q - mr * kchunks;
-        const uint32_t off = (mr < a.m && ch * 8 < a.k) ? (uint32_t(mr) * uint32_t(a.ldx) + uint32_t(ch) * 8u) * 2u : OOB;
-        smem[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-    }
+        lc[u] = fetch(wave + u * GEMV_NW);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<PF * lane_loads<CODEC>()>();   // this wave's X DMAs (issued first) have landed
     __syncthreads();
     for (int q = tid; q < MM * a.ksteps * 2; q += GEMV_NT) {
         const int mr = q / (2 * a.ksteps), h = q - mr * 2 * a.ksteps;   // h = 2 t + g
@@ -252,10 +271,10 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
     for (int mr = 0; mr < MM; ++mr)
         acc[mr] = 0.0f;
 
-    for (int tb = t0; tb < t1; tb += PF) {
+    for (int tb = wave; tb < t1; tb += PF * GEMV_NW) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
-            const int t = tb + u;
+            const int t = tb + u * GEMV_NW;
             if (t < t1) {
                 const u32x4 *xrow[MM];
 #pragma unroll
@@ -275,10 +294,9 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
                     acc[mr] = block_sum<CODEC>(lc[u], d4, corr + ((mr * a.ksteps + t) * 2 + g) * NC, acc[mr]);
                 }
             }
-            // refill this slot with the k-step one batch ahead
-            const int tn = tb + PF + u;
-            if (tn < t1)
-                lc[u] = load_lane<CODEC>(w, lo, rg, tn, a.ksteps, a.kb128);
+            // refill this slot with the k-step one batch on, after its last use
+            __builtin_amdgcn_sched_barrier(0);
+            lc[u] = fetch(tb + (PF + u) * GEMV_NW);
         }
     }
 
@@ -332,15 +350,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(Planes wp, int n, int k, i
 
 // LDS layout of one GEMV workgroup: X, the X corrections, the wave partial sums.
 struct GemvLds {
-    int per, x_lds;
+    int x_lds;
     size_t bytes;
 };
 
 inline GemvLds gemv_lds(int codec, int64_t mm, int64_t ksteps)
 {
     GemvLds l;
-    l.per = int((ksteps + GEMV_NW - 1) / GEMV_NW);
-    const int64_t x = mm * ksteps * 128;
+    const int64_t x = (mm * ksteps * 128 + 1023) / 1024 * 1024;   // whole 1 KB DMA rows
     l.x_lds = int(x);
     const int64_t nc = is_mlx(codec) || codec == Q4_K ? 2 : 1;
     l.bytes = size_t(l.x_lds + mm * ksteps * 2 * nc * 4 + GEMV_NW * mm * 32 * 4);
@@ -365,7 +382,6 @@ hipError_t launch_gemv_mm(const GemmProblem &p, hipStream_t stream)
     a.ksteps = int(p.ksteps);
     a.kb128 = int(p.kb128);
     const GemvLds l = gemv_lds(CODEC, MM, p.ksteps);
-    a.per = l.per;
     a.x_lds = l.x_lds;
     void *args[] = {&a};
     return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_kernel<CODEC, MM>), dim3(unsigned(a.groups)),

@@ -333,40 +333,42 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int rg, int groups, int lane
 // Load the chunk (row group rg, k-step t) codes and scales a lane owns.
 // `ksteps` = padded K / 64, `kb128` = K / 128 (Q2_0 scale plane pitch).
 // rg and t are wave-uniform: the chunk part of each address is a scalar
-// offset, the lane part a fixed vector offset.
-template <int CODEC>
+// offset, the lane part a fixed vector offset.  STREAM marks the loads
+// non-temporal, for data read exactly once.
+template <int CODEC, bool STREAM = false>
 __device__ __forceinline__ LaneCodes<CODEC> load_lane(const PlaneRsrc &w, LaneOffsets o, int rg, int t, int ksteps,
                                                       int kb128)
 {
+    constexpr int AUX = STREAM ? 2 : 0;   // cache policy bits: 2 = nt
     LaneCodes<CODEC> lc;
     const uint32_t chunk = uint32_t(rg) * uint32_t(ksteps) + uint32_t(t);
     if constexpr (CODEC == TERNARY) {
         const uint32_t base = chunk * uint32_t(TERNARY_CHUNK);
-        lc.a = __builtin_amdgcn_raw_buffer_load_b32(w.qs, o.q, base, 0);
-        lc.b = __builtin_amdgcn_raw_buffer_load_b16(w.qs, o.q2, base, 0);
-        lc.tl = __builtin_amdgcn_raw_buffer_load_b8(w.qs, o.q3, base, 0);
+        lc.a = __builtin_amdgcn_raw_buffer_load_b32(w.qs, o.q, base, AUX);
+        lc.b = __builtin_amdgcn_raw_buffer_load_b16(w.qs, o.q2, base, AUX);
+        lc.tl = __builtin_amdgcn_raw_buffer_load_b8(w.qs, o.q3, base, AUX);
         lc.d = load_f16(w.sc, o.s, (uint32_t(rg) * uint32_t(ksteps >> 2) + uint32_t(t >> 2)) * 64u);
     } else if constexpr (CODEC == Q8_0) {
-        lc.lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 2048, 0));
-        lc.hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 2048 + 1024, 0));
+        lc.lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 2048, AUX));
+        lc.hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 2048 + 1024, AUX));
         lc.d = load_f16(w.sc, o.s, chunk * 128);
     } else if constexpr (CODEC == Q4_K) {
         // record of (row group, super-block): u16 [4 k-steps][64 lanes], then u32 [32 rows]
-        lc.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 1024, 0));
+        lc.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 1024, AUX));
         const uint32_t rec = (uint32_t(rg) * uint32_t(ksteps >> 2) + uint32_t(t >> 2)) * 640u;
-        lc.scm = __builtin_amdgcn_raw_buffer_load_b16(w.sc, o.s, rec + uint32_t(t & 3) * 128u, 0);
-        lc.dd = __builtin_amdgcn_raw_buffer_load_b32(w.sc, o.s2, rec, 0);
+        lc.scm = __builtin_amdgcn_raw_buffer_load_b16(w.sc, o.s, rec + uint32_t(t & 3) * 128u, AUX);
+        lc.dd = __builtin_amdgcn_raw_buffer_load_b32(w.sc, o.s2, rec, AUX);
     } else if constexpr (CODEC == Q2_0) {
-        lc.c = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(w.qs, o.q, chunk * 512, 0));
+        lc.c = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(w.qs, o.q, chunk * 512, AUX));
         lc.d = load_f16(w.sc, o.s, (uint32_t(rg) * kb128 + uint32_t(t >> 1)) * 64);
     } else {
-        lc.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 1024, 0));
+        lc.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 1024, AUX));
         if constexpr (CODEC == Q4_0)
             lc.d = load_f16(w.sc, o.s, chunk * 128);
         else if constexpr (CODEC == MLX4_G32)
-            lc.sb = __builtin_amdgcn_raw_buffer_load_b32(w.sc, o.s, chunk * 256, 0);
+            lc.sb = __builtin_amdgcn_raw_buffer_load_b32(w.sc, o.s, chunk * 256, AUX);
         else
-            lc.sb = __builtin_amdgcn_raw_buffer_load_b32(w.sc, o.s, chunk * 128, 0);
+            lc.sb = __builtin_amdgcn_raw_buffer_load_b32(w.sc, o.s, chunk * 128, AUX);
     }
     return lc;
 }
