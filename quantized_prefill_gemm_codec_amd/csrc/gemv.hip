@@ -15,11 +15,14 @@
 //    once), except ternary's three partial loads of one chunk, which share
 //    cache lines.
 //  * X [M, K] reaches LDS by DMA issued before the first batch of codes; the
-//    wait for it leaves those codes in flight.  Every consumed slot is
-//    refilled with the k-step one batch on, after its last use, so the load
-//    reuses the slot's registers.  (Eight waves with four slots each measured
-//    fastest on the 14336 x 4096 Q4_0 decode shape: eight slots, or sixteen
-//    or four waves, were slower.)
+//    wait for it leaves those codes in flight.
+//  * The codes sit in a ring of GEMV_PF + 1 register slots, walked with the
+//    loop unrolled by the ring size: before a wave waits for k-step j it
+//    issues the load of k-step j + GEMV_PF into the slot k-step j - 1 has
+//    just left, so a refill never waits for the dot products of the step
+//    before it.  (On the 14336 x 4096 decode shape three slots in flight
+//    measured fastest -- 7.45 us against 7.72 us for four slots refilled after
+//    use; more requests in flight per lane, or sixteen waves, were slower.)
 //  * The 1024 offset of the mantissa trick is not subtracted per weight:
 //    slice_dots dots the raw (1024 + 2^f q) halves with X and block_sum removes
 //    the offsets and the codec zero point once per 32-weight slice with a term
@@ -34,8 +37,7 @@ namespace {
 
 constexpr int GEMV_NW = 8;               // waves per workgroup (split of the k-steps)
 constexpr int GEMV_NT = 64 * GEMV_NW;
-constexpr int GEMV_PF = 4;               // k-steps of codes in flight per lane
-// (8 and 12 measured no faster for the small-code codecs, Q2_0 and ternary)
+constexpr int GEMV_PF = 3;               // k-steps of codes in flight per lane
 constexpr int GEMV_X_LDS_MAX = 64 * 1024; // largest staged X (M x K fp16) the GEMV takes
 
 struct GemvArgs {
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
             dma_b128(xw, off, 0, lbase + uint32_t(j) * 1024u);
         }
     }
-    LaneCodes<CODEC> lc[PF];
+    LaneCodes<CODEC> lc[PF + 1];
 #pragma unroll
     for (int u = 0; u < PF; ++u)
         lc[u] = fetch(wave + u * GEMV_NW);
@@ -271,11 +273,16 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
     for (int mr = 0; mr < MM; ++mr)
         acc[mr] = 0.0f;
 
-    for (int tb = wave; tb < t1; tb += PF * GEMV_NW) {
+    const int nper = (t1 - wave + GEMV_NW - 1) / GEMV_NW;   // k-steps of this wave
+    for (int j0 = 0; j0 < nper; j0 += PF + 1) {
 #pragma unroll
-        for (int u = 0; u < PF; ++u) {
-            const int t = tb + u * GEMV_NW;
-            if (t < t1) {
+        for (int v = 0; v < PF + 1; ++v) {
+            const int j = j0 + v;
+            // slot (v + PF) % (PF + 1) held k-step j - 1, already consumed
+            lc[(v + PF) % (PF + 1)] = fetch(wave + (j + PF) * GEMV_NW);
+            __builtin_amdgcn_sched_barrier(0);
+            const int t = wave + j * GEMV_NW;
+            if (j < nper) {
                 const u32x4 *xrow[MM];
 #pragma unroll
                 for (int mr = 0; mr < MM; ++mr)
@@ -286,17 +293,15 @@ __global__ __launch_bounds__(GEMV_NT) void gemv_kernel(GemvArgs a)
 #pragma unroll
                     for (int mr = 0; mr < MM; ++mr)
                         dots[c][mr] = 0.0f;
-                prepare_lane<CODEC>(lc[u]);
-                slice_dots<CODEC, MM>(lc[u], xrow, magic, dots);
+                prepare_lane<CODEC>(lc[v]);
+                slice_dots<CODEC, MM>(lc[v], xrow, magic, dots);
 #pragma unroll
                 for (int mr = 0; mr < MM; ++mr) {
                     const float d4[4] = {dots[0][mr], dots[1][mr], dots[2][mr], dots[3][mr]};
-                    acc[mr] = block_sum<CODEC>(lc[u], d4, corr + ((mr * a.ksteps + t) * 2 + g) * NC, acc[mr]);
+                    acc[mr] = block_sum<CODEC>(lc[v], d4, corr + ((mr * a.ksteps + t) * 2 + g) * NC, acc[mr]);
                 }
             }
-            // refill this slot with the k-step one batch on, after its last use
             __builtin_amdgcn_sched_barrier(0);
-            lc[u] = fetch(tb + (PF + u) * GEMV_NW);
         }
     }
 
