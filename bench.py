@@ -15,6 +15,10 @@ pages' cache flush before every measured run.  Timing: torch.cuda.Event on the
 stream the kernels are launched on, bracketing all K launches, after W warmup
 launches; ms_per_step is the mean launch duration.
 
+read_ceiling (decode lines): the library's plain streaming-read kernel timed the
+same way over the same number of bytes -- what one read-only kernel sustains
+at that size on this device, beside the GEMV's fraction of 8 TB/s.
+
 cpu_baseline: the fp64 oracle (tests' reference implementation) timed on a
 bounded sample of the same workload -- the first rows of X against all of W --
 on the host's cores; the GPU output is checked against it on the same sample.
@@ -109,6 +113,42 @@ class Prepared:
         if st != 0:
             raise RuntimeError(f"{fn.__name__} returned status {st}")
         return self.sets[i % self.rotate][2][:, :self.wl.n]
+
+
+class ReadPrepared:
+    """R rotated device buffers of `nbytes` (rounded up to 16) for the library's
+    streaming-read calibration kernel: the best a single plain read of the
+    same byte count achieves on this device, measured like the GEMV beside it."""
+
+    def __init__(self, torch, qg, nbytes, rotate):
+        nbytes = -(-nbytes // 16) * 16
+        self.nbytes = nbytes
+        self.rotate = rotate
+        self.bufs = [torch.full((nbytes // 4,), r + 1, dtype=torch.int32, device="cuda") for r in range(rotate)]
+        self.acc = torch.zeros(qg.QG_STREAM_READ_SLOTS, dtype=torch.int32, device="cuda")
+        L = qg.lib()
+        stream = qg._stream(None)
+        self.calls = [(L.qg_stream_read, (b.data_ptr(), nbytes, self.acc.data_ptr(), stream)) for b in self.bufs]
+
+    def launch(self, i):
+        fn, args = self.calls[i % self.rotate]
+        st = fn(*args)
+        if st != 0:
+            raise RuntimeError(f"qg_stream_read returned status {st}")
+
+
+def read_ceiling(torch, qg, wl, rotate, steps, warmup, settle_ms, gemv_ms):
+    """Streaming-read rate for the GEMV's algorithmic bytes, and the GEMV's
+    share of it (context for the HBM roofline fraction: at a few tens of MB a
+    single kernel's launch ramp and drain keep any read well below 8 TB/s)."""
+    rp = ReadPrepared(torch, qg, wl.algorithmic_bytes(), rotate)
+    ms, _ = time_launches(torch, rp, steps, warmup, settle_ms)
+    gbs = rp.nbytes / (ms * 1e-3) / 1e9
+    del rp
+    torch.cuda.empty_cache()
+    return {"kernel": "qg_stream_read", "bytes": -(-wl.algorithmic_bytes() // 16) * 16,
+            "us_per_launch": round(ms * 1e3, 2), "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "gemv_frac_of_ceiling": round(ms / gemv_ms, 4)}
 
 
 SETTLE_MS = 40.0
@@ -314,6 +354,8 @@ def main():
         "roofline": roofline(wl, ms, load_traffic(wl.name)),
         "settle": {"ms": args.settle_ms, "launches": settled},
     }
+    if wl.op == "gemv":
+        rec["read_ceiling"] = read_ceiling(torch, qg, wl, prep.rotate, args.steps, args.warmup, args.settle_ms, ms)
     if not args.no_secondary:
         sec = {}
         for name in SECONDARY:
@@ -326,6 +368,9 @@ def main():
             sec[name] = {"us_per_launch": round(ms2 * 1e3, 2), "tflops": round(w2.flops() / (ms2 * 1e-3) / 1e12, 2),
                          "gbs": round(w2.algorithmic_bytes() / (ms2 * 1e-3) / 1e9, 1), "roofline": r2,
                          "rotate": p2.rotate, "settle_launches": settled2}
+            if w2.op == "gemv":
+                sec[name]["read_ceiling"] = read_ceiling(torch, qg, w2, p2.rotate, max(10, args.steps), args.warmup,
+                                                         args.settle_ms, ms2)
             print(f"# timed {name}: {ms2 * 1e3:.1f} us/launch", file=sys.stderr, flush=True)
             del p2
             torch.cuda.empty_cache()

@@ -185,6 +185,20 @@ qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonica
  * binary16 value nearest its exact codec value.  For verification. */
 qg_status qg_dequant(const qg_weight *w, void *w_fp16, int64_t ldw, void *stream);
 
+/* Streaming-read calibration (not part of the GEMM path): reads every byte of
+ * src once, with the same 128-bit non-temporal loads the GEMV uses.  It
+ * measures the sustained HBM read rate one kernel achieves for a given byte
+ * count on the device at hand -- the practical ceiling against which the
+ * weight-streaming GEMV is compared (project index Pillar 4: decode time is
+ * bytes streamed over bandwidth).  Each of QG_STREAM_READ_SLOTS waves XORs the
+ * XOR of the 32-bit words it read into its own slot of out, so with out
+ * zeroed beforehand the XOR over all slots is the XOR of all words of src.
+ *  src    device, 16-byte aligned, bytes a positive multiple of 16, < 2 GiB
+ *  out    device uint32 [QG_STREAM_READ_SLOTS], 16-byte aligned, read and written
+ * Errors: QG_ERR_NULL, QG_ERR_SHAPE, QG_ERR_ALIGN, QG_ERR_LAUNCH. */
+#define QG_STREAM_READ_SLOTS 4096
+qg_status qg_stream_read(const void *src, size_t bytes, uint32_t *out, void *stream);
+
 /* Attention over a Q8_0-compressed KV cache, prefill (comparison page section
  * 2.3 and project index Brick 4: a FlashAttention core with online softmax
  * whose K and V are dequantized from the Q8_0 cache as they are read; releases

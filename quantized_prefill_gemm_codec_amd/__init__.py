@@ -36,7 +36,8 @@ STATUS = {0: "QG_OK", -1: "QG_ERR_NULL", -2: "QG_ERR_CODEC", -3: "QG_ERR_SHAPE",
           -8: "QG_ERR_CODE"}
 
 EXPORTS = ("qgemm_prefill", "qgemm_prefill_heads", "qgemm_swiglu", "qgemm_geglu", "qgemv_decode", "qg_packed_sizes", "qg_canonical_size",
-           "qg_pack_host", "qg_dequant", "qg_status_str", "qg_version", "qattn_prefill_q8kv", "qg_pack_kv_host")
+           "qg_pack_host", "qg_dequant", "qg_stream_read", "qg_status_str", "qg_version", "qattn_prefill_q8kv",
+           "qg_pack_kv_host")
 
 
 class QGError(RuntimeError):
@@ -72,13 +73,14 @@ def lib():
         L.qg_canonical_size.argtypes = [i32, i64, i64, ctypes.POINTER(sz)]
         L.qg_pack_host.argtypes = [i32, i64, i64, p, sz, p, p]
         L.qg_dequant.argtypes = [W, p, i64, p]
+        L.qg_stream_read.argtypes = [p, sz, p, p]
         L.qattn_prefill_q8kv.argtypes = [p, p, i64, i64, i64, p, p, p, p, i64, i64, i32, ctypes.c_float, p]
         L.qg_pack_kv_host.argtypes = [p, sz, i64, i64, p, p]
         L.qg_status_str.argtypes = [ctypes.c_int]
         L.qg_status_str.restype = ctypes.c_char_p
         L.qg_version.restype = i32
         for f in ("qgemm_prefill", "qgemm_prefill_heads", "qgemm_swiglu", "qgemm_geglu", "qgemv_decode", "qg_packed_sizes", "qg_canonical_size",
-                  "qg_pack_host", "qg_dequant", "qattn_prefill_q8kv", "qg_pack_kv_host"):
+                  "qg_pack_host", "qg_dequant", "qg_stream_read", "qattn_prefill_q8kv", "qg_pack_kv_host"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -248,6 +250,28 @@ def qg_dequant(w: QWeight, stream=None):
     buf = torch.empty((w.n, ldw), dtype=torch.float16, device=w.qs.device)
     _check(lib().qg_dequant(w.desc, buf.data_ptr(), ldw, _stream(stream)), "qg_dequant")
     return buf[:, :w.k]
+
+
+QG_STREAM_READ_SLOTS = 4096
+
+
+def qg_stream_read(src, out=None, stream=None):
+    """XOR of the 32-bit words of the contiguous device tensor src (its byte
+    size a multiple of 16), read once by the streaming-read calibration kernel.
+    With `out` (a device int32 tensor of QG_STREAM_READ_SLOTS elements) the
+    per-wave partial XORs accumulate into it on the stream and nothing is
+    synchronized; otherwise the XOR over fresh slots is returned."""
+    torch = _torch()
+    if not src.is_contiguous():
+        raise ValueError("qg_stream_read needs a contiguous tensor")
+    slots = out if out is not None else torch.zeros(QG_STREAM_READ_SLOTS, dtype=torch.int32, device=src.device)
+    if slots.numel() < QG_STREAM_READ_SLOTS or slots.dtype != torch.int32:
+        raise ValueError(f"qg_stream_read needs an int32 tensor of {QG_STREAM_READ_SLOTS} slots")
+    nbytes = src.numel() * src.element_size()
+    _check(lib().qg_stream_read(src.data_ptr(), nbytes, slots.data_ptr(), _stream(stream)), "qg_stream_read")
+    if out is not None:
+        return None
+    return int(np.bitwise_xor.reduce(slots.cpu().numpy().view(np.uint32)))
 
 
 class Q8KVCache:

@@ -173,6 +173,17 @@ qg_status qg_dequant(const qg_weight *w, void *w_fp16, int64_t ldw, void *stream
     return launched(launch_dequant(p, static_cast<_Float16 *>(w_fp16), ldw, static_cast<hipStream_t>(stream)));
 }
 
+qg_status qg_stream_read(const void *src, size_t bytes, uint32_t *out, void *stream)
+{
+    if (!src || !out)
+        return QG_ERR_NULL;
+    if (bytes == 0 || bytes % 16 != 0 || bytes >= size_t(LIMIT))
+        return QG_ERR_SHAPE;
+    if (!aligned16(src) || !aligned16(out))
+        return QG_ERR_ALIGN;
+    return launched(launch_stream_read(src, bytes, out, static_cast<hipStream_t>(stream)));
+}
+
 qg_status qattn_prefill_q8kv(const void *q, void *o, int64_t heads, int64_t m, int64_t head_dim,
                              const void *k_codes, const void *k_scales, const void *v_codes, const void *v_scales,
                              int64_t kv_heads, int64_t s, int32_t causal, float scale, void *stream)

@@ -29,6 +29,7 @@
 //    that depends on X only (slice_correction, computed once per workgroup).
 //  * Lane halves, then waves, are reduced in a fixed order: results are
 //    bit-identical from run to run.
+#include "../../include/qgemm.h"
 #include "launch.h"
 #include "lds_dma.h"
 
@@ -421,6 +422,53 @@ hipError_t launch_gemv(const GemmProblem &p, hipStream_t stream)
     case TERNARY: return launch_gemv_codec<TERNARY>(p, stream);
     }
     return hipErrorInvalidValue;
+}
+
+namespace {
+
+// Streaming read: 512 workgroups (two per compute unit) of 512 threads, each
+// reading one contiguous share with four 128-bit non-temporal loads in flight
+// per lane -- the shape that measured fastest among contiguous and
+// grid-stride variants at the 33 MB decode size.
+constexpr int SR_NT = 512, SR_PF = 4, SR_GRID = 512;
+static_assert(SR_GRID * SR_NT / 64 == QG_STREAM_READ_SLOTS, "one output slot per wave");
+
+__global__ __launch_bounds__(SR_NT) void stream_read_kernel(const u32x4 *__restrict__ src, uint32_t n16,
+                                                            uint32_t per_wg, uint32_t *out)
+{
+    const uint32_t base = blockIdx.x * per_wg;
+    const uint32_t end = min(base + per_wg, n16);
+    uint32_t acc = 0;
+    for (uint32_t o = base + threadIdx.x; o < end; o += SR_NT * SR_PF) {
+        u32x4 v[SR_PF];
+#pragma unroll
+        for (int u = 0; u < SR_PF; ++u) {
+            const uint32_t idx = o + uint32_t(u) * SR_NT;
+            v[u] = idx < end ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < SR_PF; ++u)
+            acc ^= (v[u][0] ^ v[u][1]) ^ (v[u][2] ^ v[u][3]);
+    }
+    // wave XOR into the wave's own slot (no two waves share one)
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+        acc ^= __shfl_xor(acc, d);
+    if ((threadIdx.x & 63) == 0)
+        out[blockIdx.x * (SR_NT / 64) + (threadIdx.x >> 6)] ^= acc;
+}
+
+}  // namespace
+
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *out, hipStream_t stream)
+{
+    const uint32_t n16 = uint32_t(bytes / 16);
+    const uint32_t per_wg = (n16 + SR_GRID - 1) / SR_GRID;
+    const u32x4 *s = static_cast<const u32x4 *>(src);
+    uint32_t n = n16, per = per_wg;
+    void *args[] = {&s, &n, &per, &out};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&stream_read_kernel), dim3(SR_GRID), dim3(SR_NT), args, 0,
+                           stream);
 }
 
 hipError_t launch_dequant(const GemmProblem &p, _Float16 *out, int64_t ldw, hipStream_t stream)

@@ -35,6 +35,8 @@ hipError_t launch_gemm(const GemmProblem &p, int glu, hipStream_t stream);   // 
 hipError_t launch_gemv(const GemmProblem &p, hipStream_t stream);
 // fp16 image of the weights, [n, ldw].
 hipError_t launch_dequant(const GemmProblem &p, _Float16 *out, int64_t ldw, hipStream_t stream);
+// Plain streaming read of `bytes` (a multiple of 16) bytes; XOR checksum into *out.
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *out, hipStream_t stream);
 
 // Attention over a Q8_0 KV cache: Q, O [heads, m, head_dim] fp16; K, V as int8
 // codes [kv_heads * s, head_dim] and fp16 scales [kv_heads * s, head_dim / 32].

@@ -109,3 +109,20 @@ def test_attention_long_context(torch):
     rows = _sample(np.random.default_rng(9104), m, 10)
     ref = q8kv_attention_ref(q, kc, vc, kv_heads, s, True, np.float32(1.0 / np.sqrt(d)).item(), rows=rows)
     assert _err(got[:, rows], ref) <= TOL
+
+
+@pytest.mark.parametrize("nbytes", [16, 1008, 1 << 20, 33030144 + 16 * 37])
+def test_stream_read_checksum(torch, nbytes):
+    """The calibration read touches every byte once: its XOR checksum equals
+    numpy's over the same words, ragged shares and tails included."""
+    rng = np.random.default_rng(nbytes)
+    words = rng.integers(0, 1 << 32, size=nbytes // 4, dtype=np.uint32)
+    want = int(np.bitwise_xor.reduce(words))
+    src = torch.from_numpy(words.view(np.int32)).cuda()
+    assert qg.qg_stream_read(src) == want
+    slots = torch.zeros(qg.QG_STREAM_READ_SLOTS, dtype=torch.int32, device="cuda")
+    qg.qg_stream_read(src, out=slots)
+    assert int(np.bitwise_xor.reduce(slots.cpu().numpy().view(np.uint32))) == want
+    qg.qg_stream_read(src, out=slots)
+    assert not slots.cpu().numpy().any()      # every slot XORed with the same partial twice
+

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(qg.EXPORTS)
-    assert qg.qg_version() == 100
+    assert qg.qg_version() == 101
 
 
 @pytest.mark.parametrize("codec,n,k", [(1, 8192, 2048), (1, 40, 96), (2, 14336, 4096), (3, 4096, 4096), (3, 33, 128),
@@ -291,6 +291,16 @@ def test_prefill_heads_argument_errors():
     assert L.qgemm_prefill_heads(ctypes.byref(w), 0, 4, 64, FAKE, 64, None) == -1
     assert L.qgemm_prefill_heads(ctypes.byref(_w(codec=9)), FAKE, 4, 64, FAKE, 64, None) == -2
     assert L.qgemm_prefill_heads(ctypes.byref(w), FAKE + 8, 4, 64, FAKE, 64, None) == -4
+
+
+def test_stream_read_argument_errors():
+    L = qg.lib()
+    assert L.qg_stream_read(0, 1024, FAKE, None) == -1
+    assert L.qg_stream_read(FAKE, 1024, 0, None) == -1
+    for nbytes in (0, 8, 1000, 1 << 31):
+        assert L.qg_stream_read(FAKE, nbytes, FAKE, None) == -3
+    assert L.qg_stream_read(FAKE + 8, 1024, FAKE, None) == -4
+    assert L.qg_stream_read(FAKE, 1024, FAKE + 4, None) == -4
 
 
 def test_status_strings():
