@@ -798,12 +798,17 @@ hipError_t launch_tile(const GemmProblem &p, hipStream_t stream)
 
 int64_t tiles(const GemmProblem &p, int bm, int bn) { return ceil_div(p.m, bm) * ceil_div(p.n, bn); }
 
-// gate/up projections with a gated epilogue (GLU 1 = SwiGLU, 2 = GeGLU)
+// gate/up projections with a gated epilogue (GLU 1 = SwiGLU, 2 = GeGLU).
+// M > 128: 128 x 256 tiles with the eight waves side by side along N (each
+// 128 x 32 of both matrices), so every weight is unpacked by one wave and a
+// k-step moves 25 KB by DMA; 256 x 128 tiles with 2 x 4 waves unpacked each
+// weight twice and moved 36.5 KB (424 against 399 us on the 2048 x 4096 x
+// 14336 SwiGLU).
 template <int CODEC, int GLU>
 hipError_t launch_glu(const GemmProblem &p, hipStream_t stream)
 {
     if (p.m > 128)
-        return launch_dma<CODEC, 256, 128, 2, 4, 1, GLU, 3>(p, stream);
+        return launch_dma<CODEC, 128, 256, 1, 8, 1, GLU, 3>(p, stream);
     return p.m > 64 ? launch_tile<CODEC, 128, 128, 2, 2, GLU>(p, stream)
                     : launch_tile<CODEC, 64, 64, 2, 2, GLU>(p, stream);
 }
@@ -817,9 +822,13 @@ hipError_t launch_codec(const GemmProblem &p, int glu, hipStream_t stream)
         return launch_glu<CODEC, 2>(p, stream);
     constexpr int64_t FILL = 256;   // compute units on MI355X
     if (p.m > 128) {
+        // 256 x 256 (2 x 4 waves of 128 x 64) while that fills the chip;
+        // otherwise 128 x 256 with 1 x 8 waves of 128 x 32, which unpacks each
+        // weight once (74.0 -> 67.5 us for the 2048 x 4096 x 4096 Q2_0 prefill
+        // against 256 x 128 with 2 x 4 waves)
         if (tiles(p, 256, 256) >= FILL)
             return launch_dma<CODEC, 256, 256, 2, 4, 1, 0, 3>(p, stream);
-        return launch_dma<CODEC, 256, 128, 2, 4, 1, 0, 3>(p, stream);
+        return launch_dma<CODEC, 128, 256, 1, 8, 1, 0, 3>(p, stream);
     }
     // small M: 64 x 64 tiles with the k-steps split four ways inside the
     // workgroup (eight waves), so that N / 64 tiles keep the SIMDs busy
