@@ -822,12 +822,16 @@ hipError_t launch_codec(const GemmProblem &p, int glu, hipStream_t stream)
         return launch_glu<CODEC, 2>(p, stream);
     constexpr int64_t FILL = 256;   // compute units on MI355X
     if (p.m > 128) {
-        // 256 x 256 (2 x 4 waves of 128 x 64) while that fills the chip;
-        // otherwise 128 x 256 with 1 x 8 waves of 128 x 32, which unpacks each
-        // weight once (74.0 -> 67.5 us for the 2048 x 4096 x 4096 Q2_0 prefill
-        // against 256 x 128 with 2 x 4 waves)
-        if (tiles(p, 256, 256) >= FILL)
-            return launch_dma<CODEC, 256, 256, 2, 4, 1, 0, 3>(p, stream);
+        // The eight waves sit side by side along N, so every weight is
+        // unpacked by one wave: 128 x 512 tiles (waves of 128 x 64) while they
+        // fill the chip, else 128 x 256 (waves of 128 x 32).  Per k-step a
+        // 128 x 512 tile moves 34 KB by DMA where a 256 x 256 tile with 2 x 4
+        // waves of the same 128 x 64 moved 41 KB (64.1 -> 62.1 us for the
+        // 2048 x 2048 x 8192 Q4_0 prefill); 128 x 256 against 256 x 128 with
+        // 2 x 4 waves took the 2048 x 4096 x 4096 Q2_0 prefill from 74.0 to
+        // 67.5 us.
+        if (tiles(p, 128, 512) >= FILL)
+            return launch_dma<CODEC, 128, 512, 1, 8, 1, 0, 3>(p, stream);
         return launch_dma<CODEC, 128, 256, 1, 8, 1, 0, 3>(p, stream);
     }
     // small M: 64 x 64 tiles with the k-steps split four ways inside the
