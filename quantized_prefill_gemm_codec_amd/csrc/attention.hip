@@ -47,11 +47,11 @@ struct AttnArgs {
 };
 
 // 16 int8 codes (two's complement) of one 32-element block half -> the fp16
-// values q * d, in order.  XOR 0x80 turns q into q + 128 in 0..255; two
-// bytes moved into the low bytes of the halves of a word and OR-ed into
-// binary16 1024 read 1024 + q + 128; subtracting 1152 is exact, the multiply
-// by d rounds once.
-__device__ __forceinline__ void dequant16(u32x4 c, _Float16 d, u32x4 &lo, u32x4 &hi)
+// values q * d, in order.  XOR 0x80 turns q into q + 128 in 0..255; one
+// v_perm_b32 puts two such bytes under the binary16 exponent byte 0x64 (taken
+// from the constant word e64 = 0x64646464), which reads 1024 + q + 128;
+// subtracting 1152 is exact, the multiply by d rounds once.
+__device__ __forceinline__ void dequant16(u32x4 c, _Float16 d, uint32_t e64, u32x4 &lo, u32x4 &hi)
 {
     const f16x2 dd = {d, d};
     const f16x2 off = {_Float16(1152.0f), _Float16(1152.0f)};
@@ -59,8 +59,9 @@ __device__ __forceinline__ void dequant16(u32x4 c, _Float16 d, u32x4 &lo, u32x4 
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         const uint32_t x = c[w] ^ 0x80808080u;
-        const uint32_t p01 = __builtin_amdgcn_perm(x, x, 0x0C010C00u) | 0x64006400u;
-        const uint32_t p23 = __builtin_amdgcn_perm(x, x, 0x0C030C02u) | 0x64006400u;
+        // selector bytes 0-3 pick bytes of x, 4-7 bytes of e64
+        const uint32_t p01 = __builtin_amdgcn_perm(e64, x, 0x04010400u);
+        const uint32_t p23 = __builtin_amdgcn_perm(e64, x, 0x04030402u);
         r[2 * w] = as_u32((as_f16x2(p01) - off) * dd);
         r[2 * w + 1] = as_u32((as_f16x2(p23) - off) * dd);
     }
@@ -70,13 +71,13 @@ __device__ __forceinline__ void dequant16(u32x4 c, _Float16 d, u32x4 &lo, u32x4 
 
 // Four codes (d .. d + 3 of one key, two's complement) -> two fp16 pairs
 // (d, d + 1), (d + 2, d + 3) of q * scale, in the rounding of dequant16.
-__device__ __forceinline__ void dequant4(uint32_t c, _Float16 d, uint32_t &p01, uint32_t &p23)
+__device__ __forceinline__ void dequant4(uint32_t c, _Float16 d, uint32_t e64, uint32_t &p01, uint32_t &p23)
 {
     const f16x2 dd = {d, d};
     const f16x2 off = {_Float16(1152.0f), _Float16(1152.0f)};
     const uint32_t x = c ^ 0x80808080u;
-    p01 = as_u32((as_f16x2(__builtin_amdgcn_perm(x, x, 0x0C010C00u) | 0x64006400u) - off) * dd);
-    p23 = as_u32((as_f16x2(__builtin_amdgcn_perm(x, x, 0x0C030C02u) | 0x64006400u) - off) * dd);
+    p01 = as_u32((as_f16x2(__builtin_amdgcn_perm(e64, x, 0x04010400u)) - off) * dd);
+    p23 = as_u32((as_f16x2(__builtin_amdgcn_perm(e64, x, 0x04030402u)) - off) * dd);
 }
 
 // Query tile and head of workgroup `lin` (0 .. tiles_q * heads - 1).  The
@@ -207,13 +208,14 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
             }
         }
     };
+    const uint32_t e64 = 0x64646464u;
     // dequantize the fetched tile into LDS buffer b
     auto stage = [&](int b) {
 #pragma unroll
         for (int u = 0; u < IPT; ++u) {
             const int j = tid + AT_NT * u, kk = j / CPR, c = j % CPR;
             u32x4 lo, hi;
-            dequant16(kc[u], kd[u], lo, hi);
+            dequant16(kc[u], kd[u], e64, lo, hi);
             *reinterpret_cast<u32x4 *>(&ks[b][kk * KP + 16 * c]) = lo;
             *reinterpret_cast<u32x4 *>(&ks[b][kk * KP + 16 * c + 8]) = hi;
         }
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
             uint32_t p01[8], p23[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                dequant4(vc[u][e], vd[u][e], p01[e], p23[e]);
+                dequant4(vc[u][e], vd[u][e], e64, p01[e], p23[e]);
             // row d = 4 c4 + r of V^T gets keys 8 k8 .. + 7: the low (r even)
             // or high (r odd) halves of keys e, e + 1 paired by v_perm_b32
             u32x4 rows[4];
