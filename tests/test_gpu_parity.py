@@ -360,6 +360,26 @@ def _sample(rng, size, count):
     return np.sort(np.concatenate([[0, size - 1], s]))
 
 
+@pytest.mark.parametrize("codec", [1, 2, 3, 4, 5, 6, 7])
+def test_prefill_wide_tile_ragged(torch, codec):
+    """M = 1921, N = 7681 is 16 x 16 tiles of 128 x 512 (the tile the prefill
+    takes when those fill the chip), with a one-row m tail and a one-column n
+    tail inside a partly filled row group; sampled rows and columns include
+    both tails."""
+    m, n, k = 1921, 7681, 256
+    canon = synth.gen_weight(codec, n, k, 4100 + codec)
+    x = synth.gen_x(m, k, 4200 + codec)
+    w = _weight(torch, codec, n, k, canon)
+    y = qg.qgemm_prefill(w, _dev(torch, x))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    rng = np.random.default_rng(codec)
+    rows_m = np.unique(np.concatenate([_sample(rng, m, 12), [1919, 1920]]))
+    rows_n = np.unique(np.concatenate([_sample(rng, n, 384), np.arange(7664, 7681)]))
+    ref = oracle.gemm_ref(codec, canon, n, k, x[rows_m], rows_n=rows_n)
+    assert _err(y.cpu().numpy()[np.ix_(rows_m, rows_n)], ref) <= TOL
+
+
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_full_workload_sampled(torch, name):
     wl = synth.WORKLOADS[name]
