@@ -115,7 +115,7 @@ __device__ __forceinline__ void slice_dots(const LaneCodes<CODEC> &lc, const u32
                 const int p = 4 * s + u;
                 const uint32_t r = p < 5 ? lc.r0 : p < 10 ? lc.r1 : p < 15 ? lc.r2 : lc.r3;
                 const uint32_t pw = p % 5 == 0 ? 1u : p % 5 == 1 ? 3u : p % 5 == 2 ? 9u : p % 5 == 3 ? 27u : 81u;
-                h[u] = ternary_digits(r, p == 15 ? lc.m3 : pw | (pw << 16)) & 0x00030003u;
+                h[u] = ternary_digits(r, p == 15 ? lc.m3 : pw | (pw << 16), p != 15 && p % 5 == 0);
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u)

@@ -18,9 +18,10 @@
 //   MLX4-G32  the same, one (s, b) per 32 weights
 //   Q2_0      w = (q - 1) * d, q=3 -> +2d  (v_pk_add_f16, v_pk_mul_f16)
 //   Q8_0      w = q * d, stored q + 128    (v_pk_add_f16, v_pk_mul_f16)
-//   ternary   w = (t - 1) * d, digit t of a fixed-point base-3 byte (two
-//             v_pk_mul_lo_u16, one and, one v_pk_lshrrev_b16 per two digits,
-//             then the or / v_pk_add_f16 / v_pk_mul_f16 of the others)
+//   ternary   w = (t - 1) * d, digit t of a fixed-point base-3 byte (one
+//             v_pk_mul_lo_u16, one v_pk_lshrrev_b16 and one v_pk_mad_u16 per
+//             two digits, then the or / v_pk_add_f16 / v_pk_mul_f16 of the
+//             others)
 //   Q4_K      w = d * (q sc) - dmin m      (v_pk_fma_f16 for the exact
 //             integer q sc, then v_fma_mix{lo,hi}_f16: fp16 d times fp16 q sc
 //             plus the fp32 value -dmin m, rounded once to fp16; see mix_pair)
@@ -155,18 +156,23 @@ template <> struct CodeZero<Q8_0> { static constexpr int v = 128; };   // codes 
 template <> struct CodeZero<Q4_K> { static constexpr int v = 0; };
 template <> struct CodeZero<TERNARY> { static constexpr int v = 1; };    // digit t = q + 1
 
-// Base-3 digits of fixed-point bytes, one byte per 16-bit half of r: digit i
-// of byte B is ((B 3^i) mod 256) 3 >> 8 (mul = 3^i in both halves, or the
-// lane's tail multipliers).  Returns (1024 + t_lo, 1024 + t_hi) as fp16 bits;
-// the bits above bit 1 of each half are the magic, so `& 0x00030003` gives
-// the bare digits.
-__device__ __forceinline__ uint32_t ternary_digits(uint32_t r, uint32_t mul)
+// Base-3 digits of fixed-point bytes, one byte per 16-bit half of r, returned
+// bare (t in 0..2 per half).  Digit i of byte B is ((B 3^i) mod 256) 3 >> 8,
+// the carry out of the fractional byte of B 3^i times 3; with
+// X_j = floor(B 3^j / 256) that is X_(i+1) - 3 X_i, because B 3^(i+1) =
+// 3 (256 X_i + (B 3^i mod 256)).  So a digit costs one multiply and one shift
+// for X_(i+1) and one multiply-add, and the next digit of the same byte reuses
+// X_(i+1).  B <= 242 keeps B 3^5 below 2^16.  mul = 3^i in both halves (or the
+// lane's tail multipliers); digit 0 (mul = 1) has X_0 = 0.
+__device__ __forceinline__ uint32_t ternary_digits(uint32_t r, uint32_t mul, bool first)
 {
-    const u16x2 x = __builtin_bit_cast(u16x2, r) * __builtin_bit_cast(u16x2, mul);
-    const u16x2 y = __builtin_bit_cast(u16x2, __builtin_bit_cast(uint32_t, x) & 0x00FF00FFu);
-    const u16x2 three = {3, 3};
-    const u16x2 t = (y * three) >> (u16x2){8, 8};
-    return __builtin_bit_cast(uint32_t, t) | 0x64006400u;
+    const u16x2 b = __builtin_bit_cast(u16x2, r), m = __builtin_bit_cast(u16x2, mul);
+    const u16x2 three = {3, 3}, eight = {8, 8};
+    const u16x2 x1 = (b * (m * three)) >> eight;
+    if (first)
+        return __builtin_bit_cast(uint32_t, x1);
+    const u16x2 x0 = (b * m) >> eight;
+    return __builtin_bit_cast(uint32_t, x1 - x0 * three);
 }
 
 // (2^E + q_even, 2^E + q_odd) -> exact fp16 (q_even - z, q_odd - z)
@@ -192,7 +198,7 @@ __device__ __forceinline__ f16x8 unpack_substep(const LaneCodes<CODEC> &lc, int 
             const uint32_t r = p < 5 ? lc.r0 : p < 10 ? lc.r1 : p < 15 ? lc.r2 : lc.r3;
             const uint32_t pw = p % 5 == 0 ? 1u : p % 5 == 1 ? 3u : p % 5 == 2 ? 9u : p % 5 == 3 ? 27u : 81u;
             const uint32_t mul = p == 15 ? lc.m3 : pw | (pw << 16);
-            q[u] = factor<CODEC, 10>(ternary_digits(r, mul));
+            q[u] = factor<CODEC, 10>(ternary_digits(r, mul, p != 15 && p % 5 == 0) | 0x64006400u);
         }
     } else if constexpr (CODEC == Q4_K) {
         // (2^E + q) sc - 2^E sc = q sc exactly (at most 15 * 63 = 945), then
