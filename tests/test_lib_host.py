@@ -293,6 +293,20 @@ def test_prefill_heads_argument_errors():
     assert L.qgemm_prefill_heads(ctypes.byref(w), FAKE + 8, 4, 64, FAKE, 64, None) == -4
 
 
+def test_ternary_digit_identity_in_16_bit_arithmetic():
+    """The kernels take digit i of a fixed-point base-3 byte B as
+    X_(i+1) - 3 X_i with X_j = floor(B 3^j / 256), in 16-bit lanes; that equals
+    ((B 3^i) mod 256) * 3 >> 8 for every valid byte, no product overflows 16
+    bits, and the digits reproduce the byte's base-3 value."""
+    for v in range(243):
+        b = -(-256 * v // 243)                  # byte = ceil(256 v / 243)
+        x = [((b * 3 ** j) & 0xFFFF) >> 8 for j in range(6)]
+        assert all(b * 3 ** j < 1 << 16 for j in range(6))
+        digits = [(x[i + 1] - 3 * x[i]) & 0xFFFF for i in range(5)]
+        assert digits == [((b * 3 ** i) & 0xFF) * 3 >> 8 for i in range(5)]
+        assert sum(t * 3 ** (4 - i) for i, t in enumerate(digits)) == v
+
+
 def test_stream_read_argument_errors():
     L = qg.lib()
     assert L.qg_stream_read(0, 1024, FAKE, None) == -1
