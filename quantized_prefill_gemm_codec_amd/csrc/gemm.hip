@@ -341,8 +341,10 @@ __device__ __forceinline__ void grouped_tile(int bid, int tiles_m, int tiles_n, 
 // group of WM x WN waves; each group has its own X / code / scale slice in
 // every stage, and the WK fp32 partial tiles are summed in LDS (fixed order)
 // in the epilogue.  Used for small M, where the tiles alone would leave most
-// SIMDs idle.  NSTAGE stages are in flight (loads run NSTAGE-1 steps ahead).
-template <int CODEC, int BM, int BN, int WM, int WN, int WK, int GLU, int NSTAGE>
+// SIMDs idle.  LDS holds NSTAGE stages of KS k-steps each: a stage's DMAs are
+// issued together, NSTAGE-1 stages ahead of use, and the wait + barrier that
+// make a stage visible come once per stage.
+template <int CODEC, int BM, int BN, int WM, int WN, int WK, int GLU, int NSTAGE, int KS = 1>
 __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs a)
 {
     constexpr int NWT = WM * WN;                           // waves per k-slice
@@ -363,19 +365,21 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     constexpr int X_OFF = 0, X_BYTES = BM * 128;
     constexpr int W_OFF = X_BYTES, W_BYTES = NMAT * RG * WCH;
     constexpr int S_OFF = W_OFF + W_BYTES, S_BYTES = NMAT * RG * SB;
-    constexpr int SLICE = (S_OFF + S_BYTES + 255) / 256 * 256;   // one k-slice of one stage
-    constexpr int STAGE = WK * SLICE;
-    constexpr int AHEAD = NSTAGE - 1;
+    constexpr int SLICE = (S_OFF + S_BYTES + 255) / 256 * 256;   // one k-slice of one k-step slot
+    constexpr int STAGE = WK * SLICE;                      // one k-step slot
+    constexpr int AHEAD = NSTAGE - 1;                      // stages of lead
+    constexpr int NSLOT = NSTAGE * KS;                     // k-step slots in LDS
     constexpr int PPITCH = BN * 4 + 16;                    // fp32 partial tile row pitch (WK > 1)
     constexpr int EPI_BYTES = WK == 1 ? BM * BN * 2 : WK * BM * PPITCH;
-    constexpr int LDS_BYTES = NSTAGE * STAGE > EPI_BYTES ? NSTAGE * STAGE : EPI_BYTES;
+    constexpr int LDS_BYTES = NSLOT * STAGE > EPI_BYTES ? NSLOT * STAGE : EPI_BYTES;
     constexpr int NX = X_BYTES / 1024, NWI = W_BYTES / WDMA, NSI = (S_BYTES + 255) / 256;   // DMA ops per slice
     constexpr int XPW = NX / NWT, WPW = (NWI + NWT - 1) / NWT, SPW = (NSI + NWT - 1) / NWT;
     constexpr int VMIN = XPW + NWI / NWT + NSI / NWT;       // fewest DMA ops any wave issues per stage
     constexpr int VMAX = XPW + WPW + SPW;                   // most
-    constexpr int VWAIT = (AHEAD - 1) * VMAX;               // DMA ops that may stay in flight, at most
+    constexpr int VWAIT = (AHEAD - 1) * KS * VMAX;          // DMA ops that may stay in flight, at most
     static_assert(NX % NWT == 0 && W_BYTES % 1024 == 0 && SLICE % 256 == 0, "dma tiling");
-    static_assert((FM == 1 || FM % 2 == 0) && VMIN >= 1 && NSTAGE >= 3 && VWAIT < 64 && VMAX - VMIN <= 2, "tile");
+    static_assert((FM == 1 || FM % 2 == 0) && VMIN >= 1 && NSTAGE >= 2 && NSLOT >= 3 && VWAIT < 64 &&
+                      VMAX - VMIN <= 2, "tile");
     static_assert(!(GLU && WK > 1), "the split-K epilogue sums plain GEMM partials");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
@@ -477,11 +481,11 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     nops = __builtin_amdgcn_readfirstlane(nops);
     auto wait_stage = [&]() {
         if (nops >= VMIN + 2)
-            wait_vmcnt<(AHEAD - 1) * (VMIN + 2 <= VMAX ? VMIN + 2 : VMIN)>();
+            wait_vmcnt<(AHEAD - 1) * KS * (VMIN + 2 <= VMAX ? VMIN + 2 : VMIN)>();
         else if (nops == VMIN + 1)
-            wait_vmcnt<(AHEAD - 1) * (VMIN + 1 <= VMAX ? VMIN + 1 : VMIN)>();
+            wait_vmcnt<(AHEAD - 1) * KS * (VMIN + 1 <= VMAX ? VMIN + 1 : VMIN)>();
         else
-            wait_vmcnt<(AHEAD - 1) * VMIN>();
+            wait_vmcnt<(AHEAD - 1) * KS * VMIN>();
     };
 
     // iteration i of this wave's slice = k-step kbase + i; past the end of K
@@ -594,7 +598,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
                     acc[mt][fm][fn][e] = 0.0f;
 
 #pragma unroll
-    for (int i = 0; i < AHEAD; ++i)
+    for (int i = 0; i < AHEAD * KS; ++i)
         issue_stage(min(i, kq - 1), i);
     wait_stage();
     __syncthreads();
@@ -608,11 +612,17 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     f16x8 wf[2][NMAT][FN];
     read_x(lds + slice, 0, xf[0]);
     unpack(cw, 0, wf[0]);
-    // one k-step; ST = t % NSTAGE is a compile-time constant (the loop below
-    // is unrolled by NSTAGE), so every LDS stage address folds to a constant
+    // one k-step; ST = t % NSLOT is a compile-time constant (the loop below
+    // is unrolled by NSLOT), so every LDS slot address folds to a constant.
+    // The first k-step of a stage issues the DMAs of the stage AHEAD on; the
+    // last one waits for the next stage and ends with the barrier.
     auto kstep = [&](int t, auto stc) {
         constexpr int ST = decltype(stc)::value;
-        issue_stage(min(t + AHEAD, kq - 1), (ST + AHEAD) % NSTAGE);
+        if constexpr (ST % KS == 0) {
+#pragma unroll
+            for (int h = 0; h < KS; ++h)
+                issue_stage(min(t + AHEAD * KS + h, kq - 1), (ST + AHEAD * KS + h) % NSLOT);
+        }
         const char *sp = lds + ST * STAGE + slice;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -621,14 +631,16 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
                 read_x(sp, s + 1, xf[cur ^ 1]);
                 unpack(cw, s + 1, wf[cur ^ 1]);
             } else {
-                // stage t+1 has landed once at most this wave's DMAs of the
-                // newest AHEAD-1 stages remain (wait_stage); after the
-                // barrier nobody reads stage t again.
+                // at a stage's last k-step: the next stage has landed once at
+                // most this wave's DMAs of the newest AHEAD-1 stages remain
+                // (wait_stage); after the barrier nobody reads this stage again.
                 // sched_barrier: sub-step 3's operands stay ahead of the wait.
                 __builtin_amdgcn_sched_barrier(0);
-                wait_stage();
-                __syncthreads();
-                const char *np = lds + ((ST + 1) % NSTAGE) * STAGE + slice;
+                if constexpr (ST % KS == KS - 1) {
+                    wait_stage();
+                    __syncthreads();
+                }
+                const char *np = lds + ((ST + 1) % NSLOT) * STAGE + slice;
                 read_w(np, cw);
                 read_x(np, 0, xf[cur ^ 1]);
                 unpack(cw, 0, wf[cur ^ 1]);
@@ -652,8 +664,8 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
             }
         }
     };
-    for (int t0 = 0; t0 < kq; t0 += NSTAGE)
-        static_for<NSTAGE>([&](auto u) {
+    for (int t0 = 0; t0 < kq; t0 += NSLOT)
+        static_for<NSLOT>([&](auto u) {
             if (t0 + int(decltype(u)::value) < kq)
                 kstep(t0 + int(decltype(u)::value), u);
         });
@@ -749,7 +761,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     }
 }
 
-template <int CODEC, int BM, int BN, int WM, int WN, int WK, int GLU, int NSTAGE>
+template <int CODEC, int BM, int BN, int WM, int WN, int WK, int GLU, int NSTAGE, int KS = 1>
 hipError_t launch_dma(const GemmProblem &p, hipStream_t stream)
 {
     GemmArgs a;
@@ -772,7 +784,7 @@ hipError_t launch_dma(const GemmProblem &p, hipStream_t stream)
     void *args[] = {&a};
     const dim3 grid(unsigned(a.tiles_m * a.tiles_n)), block(64 * WM * WN * WK);
     return hipLaunchKernel(
-        reinterpret_cast<const void *>(&gemm_dma_kernel<CODEC, BM, BN, WM, WN, WK, GLU, NSTAGE>), grid, block,
+        reinterpret_cast<const void *>(&gemm_dma_kernel<CODEC, BM, BN, WM, WN, WK, GLU, NSTAGE, KS>), grid, block,
         args, 0, stream);
 }
 
@@ -836,9 +848,13 @@ hipError_t launch_codec(const GemmProblem &p, int glu, hipStream_t stream)
         // 2048 x 2048 x 8192 Q4_0 prefill); 128 x 256 against 256 x 128 with
         // 2 x 4 waves took the 2048 x 4096 x 4096 Q2_0 prefill from 74.0 to
         // 67.5 us.
+        // The 128 x 256 tile's k-steps move less (25 KB), and two stages of two
+        // k-steps each -- half the barriers, the same lead -- measured faster
+        // there (Q2_0 61.4 -> 58.7 us, q-projection 65.8 -> 64.0 us), but not
+        // for 128 x 512 (57.9 -> 58.8 us) or the gated tiles.
         if (tiles(p, 128, 512) >= FILL)
             return launch_dma<CODEC, 128, 512, 1, 8, 1, 0, 3>(p, stream);
-        return launch_dma<CODEC, 128, 256, 1, 8, 1, 0, 3>(p, stream);
+        return launch_dma<CODEC, 128, 256, 1, 8, 1, 0, 2, 2>(p, stream);
     }
     // small M: 64 x 64 tiles with the k-steps split four ways inside the
     // workgroup (eight waves), so that N / 64 tiles keep the SIMDs busy
