@@ -364,13 +364,17 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     constexpr int SB = (CODEC == Q2_0 || TERN) ? 64 : (CODEC == MLX4_G32 || CODEC == Q4_K) ? 256 : 128;
     constexpr int X_OFF = 0, X_BYTES = BM * 128;
     constexpr int W_OFF = X_BYTES, W_BYTES = NMAT * RG * WCH;
-    constexpr int S_OFF = W_OFF + W_BYTES, S_BYTES = NMAT * RG * SB;
+    // each matrix's scale records take a whole number of 256-byte DMA
+    // instructions, so that no instruction (one buffer descriptor) spans both
+    // matrices of a gated tile
+    constexpr int SPM = (RG * SB + 255) / 256 * 256;       // scale bytes per matrix, padded
+    constexpr int S_OFF = W_OFF + W_BYTES, S_BYTES = NMAT * SPM;
     constexpr int SLICE = (S_OFF + S_BYTES + 255) / 256 * 256;   // one k-slice of one k-step slot
     constexpr int STAGE = WK * SLICE;                      // one k-step slot
     constexpr int AHEAD = NSTAGE - 1;                      // stages of lead
     constexpr int NSLOT = NSTAGE * KS;                     // k-step slots in LDS
     constexpr int PPITCH = BN * 4 + 16;                    // fp32 partial tile row pitch (WK > 1)
-    constexpr int EPI_BYTES = WK == 1 ? BM * BN * 2 : WK * BM * PPITCH;
+    constexpr int EPI_BYTES = WK == 1 ? BM * BN * 2 : NMAT * WK * BM * PPITCH;   // WK > 1: fp32 partials
     constexpr int LDS_BYTES = NSLOT * STAGE > EPI_BYTES ? NSLOT * STAGE : EPI_BYTES;
     constexpr int NX = X_BYTES / 1024, NWI = W_BYTES / WDMA, NSI = (S_BYTES + 255) / 256;   // DMA ops per slice
     constexpr int XPW = NX / NWT, WPW = (NWI + NWT - 1) / NWT, SPW = (NSI + NWT - 1) / NWT;
@@ -380,7 +384,6 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     static_assert(NX % NWT == 0 && W_BYTES % 1024 == 0 && SLICE % 256 == 0, "dma tiling");
     static_assert((FM == 1 || FM % 2 == 0) && VMIN >= 1 && NSTAGE >= 2 && NSLOT >= 3 && VWAIT < 64 &&
                       VMAX - VMIN <= 2, "tile");
-    static_assert(!(GLU && WK > 1), "the split-K epilogue sums plain GEMM partials");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
     __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
@@ -446,16 +449,16 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
         wv[u] = (j < NWI && rg0 + rg < a.groups) ? uint32_t(rg0 + rg) * uint32_t(a.ksteps) * WCH + lo : OOB;
     }
     // scales: dword instruction j covers bytes [256 j, 256 j + 256) of the
-    // stage's scale area, SB bytes per (matrix, row group)
+    // stage's scale area: per matrix SPM bytes, SB per row group, then padding
     uint32_t sv[SPW];
     int smat[SPW];
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
         const int j = wr + NWT * u;
         const int b = 256 * j + 4 * lane;
-        const int c = b / SB, o = b % SB;
-        const int rg = c % RG;
-        smat[u] = (256 * j / SB) / RG;              // wave-uniform: chunks never straddle matrices
+        const int bm = b % SPM;                     // byte inside the matrix's area
+        const int rg = bm / SB, o = bm % SB;
+        smat[u] = (256 * j) / SPM;                  // wave-uniform: SPM is a multiple of 256
         const uint32_t pitch = CODEC == Q2_0   ? uint32_t(a.kb128) * 64u
                              : TERN          ? uint32_t(a.ksteps >> 2) * 64u   // one record per 4 k-steps
                              : CODEC == Q4_K ? uint32_t(a.ksteps) * 160u      // 640 B per 4 k-steps
@@ -463,7 +466,8 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
         // Q4_K: bytes [0, 128) of a chunk come from the k-step's lane records
         // (+ 128 (t % 4) at issue), bytes [128, 256) from the row records at 512
         const uint32_t src = CODEC == Q4_K && o >= 128 ? uint32_t(o) - 128u + 512u : uint32_t(o);
-        sv[u] = (j < NSI && b < S_BYTES && rg0 + rg < a.groups) ? uint32_t(rg0 + rg) * pitch + src : OOB;
+        sv[u] = (j < NSI && b < S_BYTES && bm < RG * SB && rg0 + rg < a.groups) ? uint32_t(rg0 + rg) * pitch + src
+                                                                                : OOB;
     }
 
     // Waves issue different numbers of DMA ops per stage (the code and scale
@@ -547,7 +551,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
             for (int fn = 0; fn < FN; ++fn) {
                 const int c = mt * RG + wn * FN + fn;
                 const char *wp = st + W_OFF + c * WCH + lane * (CB == 32 ? 16 : CB);
-                const char *sp = st + S_OFF + c * SB;
+                const char *sp = st + S_OFF + mt * SPM + (wn * FN + fn) * SB;
                 if constexpr (TERN) {
                     const char *cp = st + W_OFF + c * WCH;
                     cw[mt][fn].a = *reinterpret_cast<const uint32_t *>(cp + lane * 4);
@@ -681,35 +685,55 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     __syncthreads();
     constexpr int CPR = BN / 8;                           // 16-byte chunks per tile row
     if constexpr (WK > 1) {
-        // fp32 partial tile of each k-slice, then the fixed-order sum
+        // fp32 partial tile of each k-slice (gated: of the gate, then of the
+        // up projection), then the fixed-order sum and, gated, the epilogue
+        constexpr int PMAT = WK * BM * PPITCH;              // bytes of one matrix's partials
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int ml = wm * TM + fm * 32 + i;
+        for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
+            for (int fm = 0; fm < FM; ++fm) {
+                const int ml = wm * TM + fm * 32 + i;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int nl = wn * TN + fn * 32 + 8 * q + 4 * g;
-                    f32x4 v = {acc[0][fm][fn][4 * q], acc[0][fm][fn][4 * q + 1], acc[0][fm][fn][4 * q + 2],
-                               acc[0][fm][fn][4 * q + 3]};
-                    *reinterpret_cast<f32x4 *>(lds + (wk * BM + ml) * PPITCH + nl * 4) = v;
-                }
-        }
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int nl = wn * TN + fn * 32 + 8 * q + 4 * g;
+                        f32x4 v = {acc[mt][fm][fn][4 * q], acc[mt][fm][fn][4 * q + 1], acc[mt][fm][fn][4 * q + 2],
+                                   acc[mt][fm][fn][4 * q + 3]};
+                        *reinterpret_cast<f32x4 *>(lds + mt * PMAT + (wk * BM + ml) * PPITCH + nl * 4) = v;
+                    }
+            }
         __syncthreads();
         for (int idx = tid; idx < BM * CPR; idx += NT) {
             const int ml = idx / CPR, c = idx % CPR;
             const int m = m0 + ml, n = n0 + c * 8;
             if (m >= a.m || n >= a.n)
                 continue;
-            f32x4 lo = *reinterpret_cast<const f32x4 *>(lds + ml * PPITCH + c * 32);
-            f32x4 hi = *reinterpret_cast<const f32x4 *>(lds + ml * PPITCH + c * 32 + 16);
+            f32x4 lo[NMAT], hi[NMAT];
 #pragma unroll
-            for (int k = 1; k < WK; ++k) {
-                lo += *reinterpret_cast<const f32x4 *>(lds + (k * BM + ml) * PPITCH + c * 32);
-                hi += *reinterpret_cast<const f32x4 *>(lds + (k * BM + ml) * PPITCH + c * 32 + 16);
+            for (int mt = 0; mt < NMAT; ++mt) {
+                const char *pp = lds + mt * PMAT + ml * PPITCH + c * 32;
+                lo[mt] = *reinterpret_cast<const f32x4 *>(pp);
+                hi[mt] = *reinterpret_cast<const f32x4 *>(pp + 16);
+#pragma unroll
+                for (int k = 1; k < WK; ++k) {
+                    lo[mt] += *reinterpret_cast<const f32x4 *>(pp + k * BM * PPITCH);
+                    hi[mt] += *reinterpret_cast<const f32x4 *>(pp + k * BM * PPITCH + 16);
+                }
             }
-            const f16x8 h = {_Float16(lo[0]), _Float16(lo[1]), _Float16(lo[2]), _Float16(lo[3]),
-                             _Float16(hi[0]), _Float16(hi[1]), _Float16(hi[2]), _Float16(hi[3])};
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (GLU != 0) {
+                    v[e] = glu_mul<GLU>(lo[0][e], lo[NMAT - 1][e]);
+                    v[4 + e] = glu_mul<GLU>(hi[0][e], hi[NMAT - 1][e]);
+                } else {
+                    v[e] = lo[0][e];
+                    v[4 + e] = hi[0][e];
+                }
+            }
+            const f16x8 h = {_Float16(v[0]), _Float16(v[1]), _Float16(v[2]), _Float16(v[3]),
+                             _Float16(v[4]), _Float16(v[5]), _Float16(v[6]), _Float16(v[7])};
             _Float16 *dst = out_at(a.y, a.ldy, a.head_dim, a.m, m, n);
             if (n + 7 < a.n) {
                 __builtin_nontemporal_store(h, reinterpret_cast<f16x8 *>(dst));
@@ -827,6 +851,12 @@ hipError_t launch_glu(const GemmProblem &p, hipStream_t stream)
 {
     if (p.m > 128)
         return launch_dma<CODEC, 128, 256, 1, 8, 1, GLU, 3>(p, stream);
+    // M <= 128: the split-k small-M tile, as for the plain GEMM (both
+    // matrices' partial tiles summed in LDS before the gated epilogue).
+    // Q8_0's two 2 KB code chunks per k-step and slice would need 198 KB of
+    // stages, so Q8_0 keeps the register-staged kernel.
+    if constexpr (CODEC != Q8_0)
+        return launch_dma<CODEC, 64, 64, 1, 2, 4, GLU, 3>(p, stream);
     return p.m > 64 ? launch_tile<CODEC, 128, 128, 2, 2, GLU>(p, stream)
                     : launch_tile<CODEC, 64, 64, 2, 2, GLU>(p, stream);
 }
@@ -856,11 +886,12 @@ hipError_t launch_codec(const GemmProblem &p, int glu, hipStream_t stream)
             return launch_dma<CODEC, 128, 512, 1, 8, 1, 0, 3>(p, stream);
         return launch_dma<CODEC, 128, 256, 1, 8, 1, 0, 2, 2>(p, stream);
     }
-    // small M: 64 x 64 tiles with the k-steps split four ways inside the
-    // workgroup (eight waves), so that N / 64 tiles keep the SIMDs busy
-    if (p.m <= 64)
-        return launch_dma<CODEC, 64, 64, 1, 2, 4, 0, 3>(p, stream);
-    return launch_tile<CODEC, 128, 128, 2, 2, 0>(p, stream);
+    // small M (up to 128, i.e. one or two 64-row tiles): 64 x 64 tiles with
+    // the k-steps split four ways inside the workgroup (eight waves), so that
+    // N / 64 tiles keep the SIMDs busy.  (The register-staged 128 x 128 kernel
+    // took 92 us for M = 65..128 on the 4096 x 14336 decode weight, this one
+    // 30-32 us.)
+    return launch_dma<CODEC, 64, 64, 1, 2, 4, 0, 3>(p, stream);
 }
 
 }  // namespace

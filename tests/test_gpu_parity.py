@@ -167,6 +167,8 @@ GEMM_SHAPES = [
     # ternary likewise, plus the register-staged class (64 < M <= 128)
     (7, 16, 256, 256), (7, 33, 200, 512), (7, 100, 136, 256), (7, 129, 136, 256), (7, 300, 264, 768),
     (7, 257, 1024, 256), (7, 48, 320, 2304), (6, 100, 264, 512),
+    # two 64-row tiles of the split-k small-M tile for the remaining codecs
+    (2, 100, 200, 256), (4, 100, 200, 256), (5, 96, 136, 288),
 ]
 
 
@@ -257,7 +259,10 @@ def test_prefill_heads_layout(torch, codec, m, n, k, d):
 SWIGLU_SHAPES = [(2, 33, 200, 192), (2, 130, 256, 128), (2, 300, 264, 256), (1, 70, 136, 96), (3, 200, 128, 256),
                  (4, 200, 128, 256), (4, 70, 136, 96), (5, 200, 128, 256), (5, 70, 136, 96),
                  (6, 300, 264, 256), (6, 70, 136, 512), (7, 300, 264, 256), (7, 70, 136, 512),
-                 (7, 40, 64, 256)]
+                 (7, 40, 64, 256),
+                 # the split-k small-M tile with both matrices: Q2_0 (64-byte scale records, two row
+                 # groups per matrix), one and two 64-row tiles, ragged N and a K tail of 128
+                 (3, 40, 72, 256), (3, 100, 136, 384), (1, 128, 200, 160)]
 
 
 @pytest.mark.parametrize("codec,m,n,k", SWIGLU_SHAPES)
