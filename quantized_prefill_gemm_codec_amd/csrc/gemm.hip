@@ -19,14 +19,14 @@
 //  * All global loads are raw buffer loads: out-of-range rows, row groups and
 //    the K tail read as zero, so tails need no branches.
 //
-// gemm_kernel (64 < M <= 128, and SwiGLU up to M = 128): codes stream from
-// memory straight into registers and the next k-step's X tile is fetched into
-// registers before the current step's MFMAs (the pages' q_next ping-pong),
-// then written to the other LDS buffer: one barrier per k-step.
+// gemm_kernel (gated Q8_0 up to M = 128): codes stream from memory straight
+// into registers and the next k-step's X tile is fetched into registers before
+// the current step's MFMAs (the pages' q_next ping-pong), then written to the
+// other LDS buffer: one barrier per k-step.
 //
-// gemm_dma_kernel (M > 128, and M <= 64 with a split k-loop): X tiles, code
-// chunks and scale records all reach LDS by hardware DMA a few k-steps ahead
-// of use; see the comment above the kernel.
+// gemm_dma_kernel (M > 128, and M <= 128 with a split k-loop, plain or gated):
+// X tiles, code chunks and scale records all reach LDS by hardware DMA a few
+// k-steps ahead of use; see the comment above the kernel.
 #include <type_traits>
 
 #include "launch.h"
