@@ -604,8 +604,12 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
 #pragma unroll
     for (int i = 0; i < AHEAD * KS; ++i)
         issue_stage(min(i, kq - 1), i);
+    // With one wave per k-slice (NWT = 1) every wave's DMA writes and LDS
+    // reads stay inside its own slice of each stage, and its own vmcnt wait
+    // is all it needs: the k-loop then runs without workgroup barriers.
     wait_stage();
-    __syncthreads();
+    if constexpr (NWT > 1)
+        __syncthreads();
     LaneCodes<CODEC> cw[NMAT][FN];
     const int slice = wk * SLICE;
     read_w(lds + slice, cw);
@@ -642,7 +646,8 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (ST % KS == KS - 1) {
                     wait_stage();
-                    __syncthreads();
+                    if constexpr (NWT > 1)
+                        __syncthreads();
                 }
                 const char *np = lds + ((ST + 1) % NSLOT) * STAGE + slice;
                 read_w(np, cw);
@@ -887,11 +892,13 @@ hipError_t launch_codec(const GemmProblem &p, int glu, hipStream_t stream)
         return launch_dma<CODEC, 128, 256, 1, 8, 1, 0, 2, 2>(p, stream);
     }
     // small M (up to 128, i.e. one or two 64-row tiles): 64 x 64 tiles with
-    // the k-steps split four ways inside the workgroup (eight waves), so that
-    // N / 64 tiles keep the SIMDs busy.  (The register-staged 128 x 128 kernel
-    // took 92 us for M = 65..128 on the 4096 x 14336 decode weight, this one
-    // 30-32 us.)
-    return launch_dma<CODEC, 64, 64, 1, 2, 4, 0, 3>(p, stream);
+    // the k-steps split four ways inside the workgroup, one wave per k-slice,
+    // so that N / 64 tiles keep the SIMDs busy and the k-loop needs no
+    // barrier.  (The register-staged 128 x 128 kernel took 92 us for M =
+    // 65..128 on the 4096 x 14336 decode weight, this one 30-32 us; at M = 64
+    // the barrier-free four waves take 15.1-15.4 us where eight waves, two per
+    // k-slice, took 15.9.)
+    return launch_dma<CODEC, 64, 64, 1, 1, 4, 0, 3>(p, stream);
 }
 
 }  // namespace
