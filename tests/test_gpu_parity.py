@@ -164,7 +164,7 @@ GEMM_SHAPES = [
     # Q4_K likewise (K a multiple of the 256-weight super-block), and a split-k shape
     (6, 16, 256, 256), (6, 33, 200, 512), (6, 129, 136, 256), (6, 300, 264, 768), (6, 257, 1024, 256),
     (6, 48, 320, 2304),
-    # ternary likewise, plus the register-staged class (64 < M <= 128)
+    # ternary likewise, plus two 64-row tiles of the split-k small-M tile (64 < M <= 128)
     (7, 16, 256, 256), (7, 33, 200, 512), (7, 100, 136, 256), (7, 129, 136, 256), (7, 300, 264, 768),
     (7, 257, 1024, 256), (7, 48, 320, 2304), (6, 100, 264, 512),
     # two 64-row tiles of the split-k small-M tile for the remaining codecs
