@@ -115,7 +115,10 @@ typedef struct {
     const void *scales;
 } qg_weight;
 
-/* Prefill projection Y[m, n] = sum_k X[m, k] * W[n, k]  (Y = X W^T).
+/* Prefill projection Y[m, n] = sum_k X[m, k] * W[n, k]  (Y = X W^T): the
+ * quantized GEMM of prompt prefill, weights dequantized inside the kernel and
+ * fed to the matrix cores (comparison page, section 2.1; project index,
+ * Pillar 1, Brick 1).
  *  w    host descriptor of W [N, K]
  *  x    device fp16 [m, ldx], rows of K used       (m >= 1, ldx >= K)
  *  y    device fp16 [m, ldy], first N columns written (ldy >= N)
@@ -157,13 +160,18 @@ qg_status qgemm_geglu(const qg_weight *wg, const qg_weight *wu, const void *x,
 /* Weight-streaming small-M projection (decode, M = 1, and speculative
  * verification of up to 64 candidate rows): Y = X W^T as for qgemm_prefill,
  * for 1 <= m <= 64 (else QG_ERR_SHAPE).  Each weight byte is read from device
- * memory once per call. */
+ * memory once per call.  (Releases page v0.3.0: the quantized linear layer
+ * takes a GEMV path for M = 1; comparison page section 2.4 and project index
+ * Pillar 4: up to 64 draft tokens verified in one pass over the weights, whose
+ * time is the weight bytes over the memory bandwidth.) */
 qg_status qgemv_decode(const qg_weight *w, const void *x, int64_t m, int64_t ldx,
                        void *y, int64_t ldy, void *stream);
 
 /* Byte sizes of the two planar planes of an [n, k] matrix of `codec` (N is
  * padded to 32 rows and K to 64 weights inside the planes; the padding decodes
- * to zero).  Either out-pointer may be NULL. */
+ * to zero).  Either out-pointer may be NULL.  (The planar split of codes and
+ * scales into separate 16-byte aligned arrays: comparison page, section 4.)
+ * Errors: QG_ERR_CODEC, QG_ERR_SHAPE (K not a multiple of the block). */
 qg_status qg_packed_sizes(int32_t codec, int64_t n, int64_t k, size_t *qs_bytes,
                           size_t *scales_bytes);
 
@@ -182,8 +190,25 @@ qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonica
 
 /* Dequantize W into fp16 w_fp16 [n, ldw] (device) with the same per-codec
  * unpack routines the GEMM kernels feed to the matrix cores; each weight is the
- * binary16 value nearest its exact codec value.  For verification. */
+ * binary16 value nearest its exact codec value.  For verification: the pages
+ * check every codec's unpack bit for bit before and after each kernel change
+ * (releases page v0.2.3, bit-exact parity suite; the shared unpack contract
+ * TCodec::unpack_column).
+ *  w_fp16  device fp16 [n, ldw], ldw >= K, a multiple of 8; 16-byte aligned
+ * Errors as for qgemm_prefill. */
 qg_status qg_dequant(const qg_weight *w, void *w_fp16, int64_t ldw, void *stream);
+
+/* Name of the kernel instantiation a call would launch, as a kernel trace
+ * prints it (host only; launches nothing).  entry: 0 qgemm_prefill,
+ * 1 qgemm_prefill_heads, 2 qgemm_swiglu, 3 qgemm_geglu, 4 qgemv_decode.  The
+ * launchers take their choice from the same function, so tests can show which
+ * instantiations a set of shapes reaches (releases page v0.2.3: every codec
+ * is checked at each boundary token count the dispatch distinguishes).
+ *  name  host buffer of cap bytes, NUL-terminated on success
+ * Errors: QG_ERR_NULL, QG_ERR_CODEC, QG_ERR_SHAPE (the entry point would reject
+ * these sizes), QG_ERR_SIZE (cap too small). */
+qg_status qg_kernel_for(int32_t entry, int32_t codec, int64_t m, int64_t n, int64_t k, char *name,
+                        size_t cap);
 
 /* Streaming-read calibration (not part of the GEMM path): reads every byte of
  * src once, with the same 128-bit non-temporal loads the GEMV uses.  It

@@ -35,9 +35,12 @@ STATUS = {0: "QG_OK", -1: "QG_ERR_NULL", -2: "QG_ERR_CODEC", -3: "QG_ERR_SHAPE",
           -5: "QG_ERR_MISMATCH", -6: "QG_ERR_LAUNCH", -7: "QG_ERR_SIZE",
           -8: "QG_ERR_CODE"}
 
-EXPORTS = ("qgemm_prefill", "qgemm_prefill_heads", "qgemm_swiglu", "qgemm_geglu", "qgemv_decode", "qg_packed_sizes", "qg_canonical_size",
-           "qg_pack_host", "qg_dequant", "qg_stream_read", "qg_status_str", "qg_version", "qattn_prefill_q8kv",
-           "qg_pack_kv_host")
+EXPORTS = ("qgemm_prefill", "qgemm_prefill_heads", "qgemm_swiglu", "qgemm_geglu", "qgemv_decode", "qg_packed_sizes",
+           "qg_canonical_size", "qg_pack_host", "qg_dequant", "qg_kernel_for", "qg_stream_read", "qg_status_str",
+           "qg_version", "qattn_prefill_q8kv", "qg_pack_kv_host")
+
+# entry ids of qg_kernel_for
+ENTRY = {"prefill": 0, "heads": 1, "swiglu": 2, "geglu": 3, "gemv": 4}
 
 
 class QGError(RuntimeError):
@@ -74,13 +77,15 @@ def lib():
         L.qg_pack_host.argtypes = [i32, i64, i64, p, sz, p, p]
         L.qg_dequant.argtypes = [W, p, i64, p]
         L.qg_stream_read.argtypes = [p, sz, p, p]
+        L.qg_kernel_for.argtypes = [i32, i32, i64, i64, i64, ctypes.c_char_p, sz]
         L.qattn_prefill_q8kv.argtypes = [p, p, i64, i64, i64, p, p, p, p, i64, i64, i32, ctypes.c_float, p]
         L.qg_pack_kv_host.argtypes = [p, sz, i64, i64, p, p]
         L.qg_status_str.argtypes = [ctypes.c_int]
         L.qg_status_str.restype = ctypes.c_char_p
         L.qg_version.restype = i32
         for f in ("qgemm_prefill", "qgemm_prefill_heads", "qgemm_swiglu", "qgemm_geglu", "qgemv_decode", "qg_packed_sizes", "qg_canonical_size",
-                  "qg_pack_host", "qg_dequant", "qg_stream_read", "qattn_prefill_q8kv", "qg_pack_kv_host"):
+                  "qg_pack_host", "qg_dequant", "qg_kernel_for", "qg_stream_read", "qattn_prefill_q8kv",
+                  "qg_pack_kv_host"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -121,6 +126,15 @@ def qg_pack_host(codec: int, n: int, k: int, canonical: np.ndarray):
     _check(lib().qg_pack_host(codec, n, k, canonical.ctypes.data, canonical.size, qs.ctypes.data, sc.ctypes.data),
            "qg_pack_host")
     return qs, sc
+
+
+def qg_kernel_for(entry, codec: int, m: int, n: int, k: int) -> str:
+    """Name of the kernel instantiation the entry point ('prefill', 'heads',
+    'swiglu', 'geglu', 'gemv' or its id) would launch for these sizes."""
+    e = ENTRY[entry] if isinstance(entry, str) else int(entry)
+    buf = ctypes.create_string_buffer(128)
+    _check(lib().qg_kernel_for(e, codec, m, n, k, buf, len(buf)), "qg_kernel_for")
+    return buf.value.decode()
 
 
 # --------------------------------------------------------------- device side --
@@ -174,12 +188,30 @@ def _as_rows(x, k: int):
     return x2, lead, ldx
 
 
+def _check_weights(device, *ws):
+    for w in ws:
+        if w.qs.device != device or w.scales.device != device:
+            raise ValueError(f"weight planes are on {w.qs.device}, activations on {device}")
+
+
+def _check_out_device(out, device):
+    torch = _torch()
+    if out.dtype != torch.float16 or not out.is_cuda or out.device != torch.device(device):
+        raise ValueError(f"out must be a float16 tensor on {device} (got {out.dtype} on {out.device})")
+
+
 def _out(m: int, n: int, device, out=None):
-    """Output rows [M, N] with a row stride that is a multiple of 8 elements."""
+    """Output rows [M, N] with a row stride that is a multiple of 8 elements.
+    A caller's `out` must be viewable as [M, N] rows of unit column stride on
+    the device of X: the kernel writes straight into it, never into a copy."""
     torch = _torch()
     if out is not None:
-        o2 = out.reshape(-1, n)
-        if out.dtype != torch.float16 or o2.stride(-1) != 1 or o2.shape[0] != m:
+        _check_out_device(out, device)
+        try:
+            o2 = out.view(-1, n)
+        except RuntimeError as e:
+            raise ValueError("out cannot be viewed as [M, N] rows without a copy") from e
+        if o2.stride(-1) != 1 or o2.shape[0] != m:
             raise ValueError("out must be float16 [..., N] with M rows and unit column stride")
         return o2, (o2.stride(0) if m > 1 else 8 * ((n + 7) // 8)), out
     ldy = 8 * ((n + 7) // 8)
@@ -190,6 +222,7 @@ def _out(m: int, n: int, device, out=None):
 def qgemm_prefill(w: QWeight, x, out=None, stream=None):
     """Y = X W^T for fp16 X [..., K]; returns fp16 [..., N]."""
     x2, lead, ldx = _as_rows(x, w.k)
+    _check_weights(x.device, w)
     m = x2.shape[0]
     ybuf, ldy, y = _out(m, w.n, x.device, out)
     _check(lib().qgemm_prefill(w.desc, x2.data_ptr(), m, ldx, ybuf.data_ptr(), ldy, _stream(stream)),
@@ -200,6 +233,7 @@ def qgemm_prefill(w: QWeight, x, out=None, stream=None):
 def qgemm_swiglu(wg: QWeight, wu: QWeight, x, out=None, stream=None):
     """SiLU(X Wg^T) * (X Wu^T) for fp16 X [..., K]; returns fp16 [..., N]."""
     x2, lead, ldx = _as_rows(x, wg.k)
+    _check_weights(x.device, wg, wu)
     m = x2.shape[0]
     ybuf, ldy, y = _out(m, wg.n, x.device, out)
     _check(lib().qgemm_swiglu(wg.desc, wu.desc, x2.data_ptr(), m, ldx, ybuf.data_ptr(), ldy, _stream(stream)),
@@ -213,10 +247,12 @@ def qgemm_prefill_heads(w: QWeight, x, head_dim: int, out=None, stream=None):
     if x.dim() != 2:
         raise ValueError("qgemm_prefill_heads takes a 2-D X [M, K]")
     x2, _, ldx = _as_rows(x, w.k)
+    _check_weights(x.device, w)
     m = x2.shape[0]
     if out is None:
         out = torch.empty((w.n // head_dim if head_dim else 0, m, head_dim), dtype=torch.float16, device=x.device)
-    if out.dtype != torch.float16 or not out.is_contiguous() or out.numel() != m * w.n:
+    _check_out_device(out, x.device)
+    if not out.is_contiguous() or out.numel() != m * w.n:
         raise ValueError("out must be a contiguous fp16 tensor of M * N elements")
     _check(lib().qgemm_prefill_heads(w.desc, x2.data_ptr(), m, ldx, out.data_ptr(), head_dim, _stream(stream)),
            "qgemm_prefill_heads")
@@ -226,6 +262,7 @@ def qgemm_prefill_heads(w: QWeight, x, head_dim: int, out=None, stream=None):
 def qgemm_geglu(wg: QWeight, wu: QWeight, x, out=None, stream=None):
     """GELU(X Wg^T) * (X Wu^T) (tanh-form GELU) for fp16 X [..., K]; returns fp16 [..., N]."""
     x2, lead, ldx = _as_rows(x, wg.k)
+    _check_weights(x.device, wg, wu)
     m = x2.shape[0]
     ybuf, ldy, y = _out(m, wg.n, x.device, out)
     _check(lib().qgemm_geglu(wg.desc, wu.desc, x2.data_ptr(), m, ldx, ybuf.data_ptr(), ldy, _stream(stream)),
@@ -236,6 +273,7 @@ def qgemm_geglu(wg: QWeight, wu: QWeight, x, out=None, stream=None):
 def qgemv_decode(w: QWeight, x, out=None, stream=None):
     """Weight-streaming Y = X W^T for 1 <= M <= 64 rows of X."""
     x2, lead, ldx = _as_rows(x, w.k)
+    _check_weights(x.device, w)
     m = x2.shape[0]
     ybuf, ldy, y = _out(m, w.n, x.device, out)
     _check(lib().qgemv_decode(w.desc, x2.data_ptr(), m, ldx, ybuf.data_ptr(), ldy, _stream(stream)),
@@ -305,11 +343,15 @@ def qattn_prefill_q8kv(q, cache: Q8KVCache, causal: bool = True, scale: float | 
     torch = _torch()
     if q.dtype != torch.float16 or not q.is_cuda or q.dim() != 3 or q.shape[2] != cache.head_dim:
         raise ValueError("q must be a float16 [H, M, D] tensor on a HIP device with D matching the cache")
+    for t in (cache.k_codes, cache.k_scales, cache.v_codes, cache.v_scales):
+        if t.device != q.device:
+            raise ValueError(f"the KV cache is on {t.device}, the queries on {q.device}")
     q = q.contiguous()
     heads, m, d = q.shape
     if out is None:
         out = torch.empty_like(q)
-    if out.shape != q.shape or out.dtype != torch.float16 or not out.is_contiguous():
+    _check_out_device(out, q.device)
+    if out.shape != q.shape or not out.is_contiguous():
         raise ValueError("out must be a contiguous float16 tensor shaped like q")
     sc = float(scale) if scale is not None else 1.0 / math.sqrt(d)
     _check(lib().qattn_prefill_q8kv(q.data_ptr(), out.data_ptr(), heads, m, d, cache.k_codes.data_ptr(),

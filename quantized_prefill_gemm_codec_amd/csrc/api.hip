@@ -80,6 +80,13 @@ qg_status launched(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ERR_LAUNC
 
 bool finite_positive(float v) { return v > 0.0f && v <= 3.4e38f; }
 
+// The kernel choose_kernel picks for the call, launched on the stream.
+hipError_t run(const GemmProblem &p, int glu, bool gemv_entry, hipStream_t stream)
+{
+    const Choice c = choose_kernel(p.codec, glu, gemv_entry, p.m, p.n, p.k);
+    return c.kern == Kern::GEMV ? launch_gemv(p, c, stream) : launch_gemm(p, c, stream);
+}
+
 qg_status check_gemm(const qg_weight *w, const void *x, int64_t m, int64_t ldx, void *y, int64_t ldy)
 {
     qg_status st = check_weight(w);
@@ -100,9 +107,7 @@ qg_status qgemm_prefill(const qg_weight *w, const void *x, int64_t m, int64_t ld
     const qg_status st = check_gemm(w, x, m, ldx, y, ldy);
     if (st != QG_OK)
         return st;
-    const GemmProblem p = problem(w, x, m, ldx, y, ldy);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    return launched(m <= 4 ? launch_gemv(p, s) : launch_gemm(p, 0, s));
+    return launched(run(problem(w, x, m, ldx, y, ldy), 0, true, static_cast<hipStream_t>(stream)));
 }
 
 qg_status qgemm_prefill_heads(const qg_weight *w, const void *x, int64_t m, int64_t ldx, void *y, int64_t head_dim,
@@ -118,8 +123,7 @@ qg_status qgemm_prefill_heads(const qg_weight *w, const void *x, int64_t m, int6
         return st;
     GemmProblem p = problem(w, x, m, ldx, y, w->n);
     p.head_dim = head_dim;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    return launched(m <= 4 ? launch_gemv(p, s) : launch_gemm(p, 0, s));
+    return launched(run(p, 0, true, static_cast<hipStream_t>(stream)));
 }
 
 // gate/up projection pair with a gated epilogue (glu 1 = SwiGLU, 2 = GeGLU)
@@ -135,7 +139,7 @@ static qg_status gated(const qg_weight *wg, const qg_weight *wu, const void *x, 
         return QG_ERR_MISMATCH;
     GemmProblem p = problem(wg, x, m, ldx, out, ldo);
     p.w1 = planes_of(wu);
-    return launched(launch_gemm(p, glu, static_cast<hipStream_t>(stream)));
+    return launched(run(p, glu, false, static_cast<hipStream_t>(stream)));
 }
 
 qg_status qgemm_swiglu(const qg_weight *wg, const qg_weight *wu, const void *x, int64_t m, int64_t ldx, void *out,
@@ -158,8 +162,7 @@ qg_status qgemv_decode(const qg_weight *w, const void *x, int64_t m, int64_t ldx
         return st;
     if (m > 64)
         return QG_ERR_SHAPE;
-    const GemmProblem p = problem(w, x, m, ldx, y, ldy);
-    return launched(launch_gemv(p, static_cast<hipStream_t>(stream)));
+    return launched(run(problem(w, x, m, ldx, y, ldy), 0, true, static_cast<hipStream_t>(stream)));
 }
 
 qg_status qg_dequant(const qg_weight *w, void *w_fp16, int64_t ldw, void *stream)
@@ -171,6 +174,21 @@ qg_status qg_dequant(const qg_weight *w, void *w_fp16, int64_t ldw, void *stream
         return st;
     const GemmProblem p = problem(w, nullptr, 1, w->k, nullptr, w->n);
     return launched(launch_dequant(p, static_cast<_Float16 *>(w_fp16), ldw, static_cast<hipStream_t>(stream)));
+}
+
+qg_status qg_kernel_for(int32_t entry, int32_t codec, int64_t m, int64_t n, int64_t k, char *name, size_t cap)
+{
+    if (!name || cap == 0)
+        return QG_ERR_NULL;
+    if (!valid_codec(codec))
+        return QG_ERR_CODEC;
+    if (entry < E_PREFILL || entry > E_GEMV || m < 1 || n < 1 || k < 1 || m >= LIMIT || n >= LIMIT || k >= LIMIT ||
+        k % block_size(codec) != 0 || (entry == E_GEMV && m > 64))
+        return QG_ERR_SHAPE;
+    const int glu = entry == E_SWIGLU ? 1 : entry == E_GEGLU ? 2 : 0;
+    const Choice c = choose_kernel(codec, glu, glu == 0, m, n, k);
+    const int len = kernel_name(c, codec, name, cap);
+    return (len > 0 && size_t(len) < cap) ? QG_OK : QG_ERR_SIZE;
 }
 
 qg_status qg_stream_read(const void *src, size_t bytes, uint32_t *out, void *stream)

@@ -627,6 +627,13 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     auto kstep = [&](int t, auto stc) {
         constexpr int ST = decltype(stc)::value;
         if constexpr (ST % KS == 0) {
+            // Without a barrier (one wave per k-slice) nothing else orders this
+            // wave's reads of the slot it refills (read in the previous k-step)
+            // before the refill's DMA writes: wait for them explicitly.  The
+            // reads still in flight here are this step's sub-step 0 operands,
+            // which its first MFMAs wait for anyway.
+            if constexpr (NWT == 1)
+                wait_lds_reads();
 #pragma unroll
             for (int h = 0; h < KS; ++h)
                 issue_stage(min(t + AHEAD * KS + h, kq - 1), (ST + AHEAD * KS + h) % NSLOT);
@@ -843,76 +850,74 @@ hipError_t launch_tile(const GemmProblem &p, hipStream_t stream)
                            block, args, 0, stream);
 }
 
-int64_t tiles(const GemmProblem &p, int bm, int bn) { return ceil_div(p.m, bm) * ceil_div(p.n, bn); }
-
-// gate/up projections with a gated epilogue (GLU 1 = SwiGLU, 2 = GeGLU).
-// M > 128: 128 x 256 tiles with the eight waves side by side along N (each
-// 128 x 32 of both matrices), so every weight is unpacked by one wave and a
-// k-step moves 25 KB by DMA; 256 x 128 tiles with 2 x 4 waves unpacked each
-// weight twice and moved 36.5 KB (424 against 399 us on the 2048 x 4096 x
-// 14336 SwiGLU).
-template <int CODEC, int GLU>
-hipError_t launch_glu(const GemmProblem &p, hipStream_t stream)
-{
-    if (p.m > 128)
-        return launch_dma<CODEC, 128, 256, 1, 8, 1, GLU, 3>(p, stream);
-    // M <= 128: the split-k small-M tile, as for the plain GEMM (both
-    // matrices' partial tiles summed in LDS before the gated epilogue).
-    // Q8_0's two 2 KB code chunks per k-step and slice would need 198 KB of
-    // stages, so Q8_0 keeps the register-staged kernel.
-    if constexpr (CODEC != Q8_0)
-        return launch_dma<CODEC, 64, 64, 1, 2, 4, GLU, 3>(p, stream);
-    return p.m > 64 ? launch_tile<CODEC, 128, 128, 2, 2, GLU>(p, stream)
-                    : launch_tile<CODEC, 64, 64, 2, 2, GLU>(p, stream);
-}
-
+// Gated kernels (glu 1 = SwiGLU, 2 = GeGLU) run with the gate and up
+// projections in one workgroup.  M > 128: 128 x 256 tiles with the eight waves
+// side by side along N (each 128 x 32 of both matrices), so every weight is
+// unpacked by one wave and a k-step moves 25 KB by DMA; 256 x 128 tiles with
+// 2 x 4 waves unpacked each weight twice and moved 36.5 KB (424 against 399 us
+// on the 2048 x 4096 x 14336 SwiGLU).  M <= 128: the split-k small-M tile, as
+// for the plain GEMM (both matrices' partial tiles summed in LDS before the
+// gated epilogue), except Q8_0, whose two 2 KB code chunks per k-step and
+// slice would need 198 KB of stages: it keeps the register-staged kernel.
+//
+// Plain kernels, M > 128: the eight waves sit side by side along N, so every
+// weight is unpacked by one wave: 128 x 512 tiles (waves of 128 x 64) while
+// they fill the chip, else 128 x 256 (waves of 128 x 32).  Per k-step a 128 x
+// 512 tile moves 34 KB by DMA where a 256 x 256 tile with 2 x 4 waves of the
+// same 128 x 64 moved 41 KB (64.1 -> 62.1 us for the 2048 x 2048 x 8192 Q4_0
+// prefill); 128 x 256 against 256 x 128 with 2 x 4 waves took the 2048 x 4096 x
+// 4096 Q2_0 prefill from 74.0 to 67.5 us.  The 128 x 256 tile's k-steps move
+// less (25 KB), and two stages of two k-steps each -- half the barriers, the
+// same lead -- measured faster there (Q2_0 61.4 -> 58.7 us, q-projection 65.8 ->
+// 64.0 us), but not for 128 x 512 (57.9 -> 58.8 us) or the gated tiles.
+// Plain kernels, M <= 128 (one or two 64-row tiles): 64 x 64 tiles with the
+// k-steps split four ways inside the workgroup, one wave per k-slice, so that
+// N / 64 tiles keep the SIMDs busy and the k-loop needs no barrier.  (The
+// register-staged 128 x 128 kernel took 92 us for M = 65..128 on the 4096 x
+// 14336 decode weight, this one 30-32 us; at M = 64 the barrier-free four waves
+// take 15.1-15.4 us where eight waves, two per k-slice, took 15.9.)
 template <int CODEC>
-hipError_t launch_codec(const GemmProblem &p, int glu, hipStream_t stream)
+hipError_t launch_codec(const GemmProblem &p, const Choice &c, hipStream_t stream)
 {
-    if (glu == 1)
-        return launch_glu<CODEC, 1>(p, stream);
-    if (glu == 2)
-        return launch_glu<CODEC, 2>(p, stream);
-    constexpr int64_t FILL = 256;   // compute units on MI355X
-    if (p.m > 128) {
-        // The eight waves sit side by side along N, so every weight is
-        // unpacked by one wave: 128 x 512 tiles (waves of 128 x 64) while they
-        // fill the chip, else 128 x 256 (waves of 128 x 32).  Per k-step a
-        // 128 x 512 tile moves 34 KB by DMA where a 256 x 256 tile with 2 x 4
-        // waves of the same 128 x 64 moved 41 KB (64.1 -> 62.1 us for the
-        // 2048 x 2048 x 8192 Q4_0 prefill); 128 x 256 against 256 x 128 with
-        // 2 x 4 waves took the 2048 x 4096 x 4096 Q2_0 prefill from 74.0 to
-        // 67.5 us.
-        // The 128 x 256 tile's k-steps move less (25 KB), and two stages of two
-        // k-steps each -- half the barriers, the same lead -- measured faster
-        // there (Q2_0 61.4 -> 58.7 us, q-projection 65.8 -> 64.0 us), but not
-        // for 128 x 512 (57.9 -> 58.8 us) or the gated tiles.
-        if (tiles(p, 128, 512) >= FILL)
-            return launch_dma<CODEC, 128, 512, 1, 8, 1, 0, 3>(p, stream);
-        return launch_dma<CODEC, 128, 256, 1, 8, 1, 0, 2, 2>(p, stream);
+    switch (c.kern) {
+    case Kern::DMA_WIDE: return launch_dma<CODEC, 128, 512, 1, 8, 1, 0, 3>(p, stream);
+    case Kern::DMA_NARROW: return launch_dma<CODEC, 128, 256, 1, 8, 1, 0, 2, 2>(p, stream);
+    case Kern::DMA_SMALL: return launch_dma<CODEC, 64, 64, 1, 1, 4, 0, 3>(p, stream);
+    case Kern::GLU_DMA:
+        return c.glu == 1 ? launch_dma<CODEC, 128, 256, 1, 8, 1, 1, 3>(p, stream)
+                          : launch_dma<CODEC, 128, 256, 1, 8, 1, 2, 3>(p, stream);
+    case Kern::GLU_DMA_SMALL:
+        if constexpr (CODEC != Q8_0)
+            return c.glu == 1 ? launch_dma<CODEC, 64, 64, 1, 2, 4, 1, 3>(p, stream)
+                              : launch_dma<CODEC, 64, 64, 1, 2, 4, 2, 3>(p, stream);
+        break;
+    case Kern::GLU_REG_64:
+        if constexpr (CODEC == Q8_0)
+            return c.glu == 1 ? launch_tile<CODEC, 64, 64, 2, 2, 1>(p, stream)
+                              : launch_tile<CODEC, 64, 64, 2, 2, 2>(p, stream);
+        break;
+    case Kern::GLU_REG_128:
+        if constexpr (CODEC == Q8_0)
+            return c.glu == 1 ? launch_tile<CODEC, 128, 128, 2, 2, 1>(p, stream)
+                              : launch_tile<CODEC, 128, 128, 2, 2, 2>(p, stream);
+        break;
+    default: break;
     }
-    // small M (up to 128, i.e. one or two 64-row tiles): 64 x 64 tiles with
-    // the k-steps split four ways inside the workgroup, one wave per k-slice,
-    // so that N / 64 tiles keep the SIMDs busy and the k-loop needs no
-    // barrier.  (The register-staged 128 x 128 kernel took 92 us for M =
-    // 65..128 on the 4096 x 14336 decode weight, this one 30-32 us; at M = 64
-    // the barrier-free four waves take 15.1-15.4 us where eight waves, two per
-    // k-slice, took 15.9.)
-    return launch_dma<CODEC, 64, 64, 1, 1, 4, 0, 3>(p, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmProblem &p, int glu, hipStream_t stream)
+hipError_t launch_gemm(const GemmProblem &p, const Choice &c, hipStream_t stream)
 {
     switch (p.codec) {
-    case Q4_0: return launch_codec<Q4_0>(p, glu, stream);
-    case MLX4_G64: return launch_codec<MLX4_G64>(p, glu, stream);
-    case MLX4_G32: return launch_codec<MLX4_G32>(p, glu, stream);
-    case Q2_0: return launch_codec<Q2_0>(p, glu, stream);
-    case Q8_0: return launch_codec<Q8_0>(p, glu, stream);
-    case Q4_K: return launch_codec<Q4_K>(p, glu, stream);
-    case TERNARY: return launch_codec<TERNARY>(p, glu, stream);
+    case Q4_0: return launch_codec<Q4_0>(p, c, stream);
+    case MLX4_G64: return launch_codec<MLX4_G64>(p, c, stream);
+    case MLX4_G32: return launch_codec<MLX4_G32>(p, c, stream);
+    case Q2_0: return launch_codec<Q2_0>(p, c, stream);
+    case Q8_0: return launch_codec<Q8_0>(p, c, stream);
+    case Q4_K: return launch_codec<Q4_K>(p, c, stream);
+    case TERNARY: return launch_codec<TERNARY>(p, c, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -36,10 +36,8 @@
 namespace qg {
 namespace {
 
-constexpr int GEMV_NW = 8;               // waves per workgroup (split of the k-steps)
 constexpr int GEMV_NT = 64 * GEMV_NW;
 constexpr int GEMV_PF = 3;               // k-steps of codes in flight per lane
-constexpr int GEMV_X_LDS_MAX = 64 * 1024; // largest staged X (M x K fp16) the GEMV takes
 
 struct GemvArgs {
     Planes w;
@@ -354,22 +352,6 @@ __global__ __launch_bounds__(256) void dequant_kernel(Planes wp, int n, int k, i
     }
 }
 
-// LDS layout of one GEMV workgroup: X, the X corrections, the wave partial sums.
-struct GemvLds {
-    int x_lds;
-    size_t bytes;
-};
-
-inline GemvLds gemv_lds(int codec, int64_t mm, int64_t ksteps)
-{
-    GemvLds l;
-    const int64_t x = (mm * ksteps * 128 + 1023) / 1024 * 1024;   // whole 1 KB DMA rows
-    l.x_lds = int(x);
-    const int64_t nc = is_mlx(codec) || codec == Q4_K ? 2 : 1;
-    l.bytes = size_t(l.x_lds + mm * ksteps * 2 * nc * 4 + GEMV_NW * mm * 32 * 4);
-    return l;
-}
-
 template <int CODEC, int MM>
 hipError_t launch_gemv_mm(const GemmProblem &p, hipStream_t stream)
 {
@@ -391,35 +373,33 @@ hipError_t launch_gemv_mm(const GemmProblem &p, hipStream_t stream)
     a.x_lds = l.x_lds;
     void *args[] = {&a};
     return hipLaunchKernel(reinterpret_cast<const void *>(&gemv_kernel<CODEC, MM>), dim3(unsigned(a.groups)),
-                           dim3(GEMV_NT), args, l.bytes, stream);
+                           dim3(GEMV_NT), args, size_t(l.bytes), stream);
 }
 
 template <int CODEC>
-hipError_t launch_gemv_codec(const GemmProblem &p, hipStream_t stream)
+hipError_t launch_gemv_codec(const GemmProblem &p, int mm, hipStream_t stream)
 {
-    if (p.m == 1)
+    if (mm == 1)
         return launch_gemv_mm<CODEC, 1>(p, stream);
-    if (p.m == 2)
+    if (mm == 2)
         return launch_gemv_mm<CODEC, 2>(p, stream);
     return launch_gemv_mm<CODEC, 4>(p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_gemv(const GemmProblem &p, hipStream_t stream)
+hipError_t launch_gemv(const GemmProblem &p, const Choice &c, hipStream_t stream)
 {
-    // beyond 4 rows, or an X too large to stage, the tiled MFMA kernel serves small M
-    const int64_t mm = p.m == 1 ? 1 : p.m == 2 ? 2 : 4;
-    if (p.m > 4 || mm * p.ksteps * 128 > GEMV_X_LDS_MAX || gemv_lds(p.codec, mm, p.ksteps).bytes > 64 * 1024)
-        return launch_gemm(p, 0, stream);
+    if (c.kern != Kern::GEMV || p.m > c.mm || !gemv_fits(p.codec, p.m, p.ksteps))
+        return hipErrorInvalidValue;
     switch (p.codec) {
-    case Q4_0: return launch_gemv_codec<Q4_0>(p, stream);
-    case MLX4_G64: return launch_gemv_codec<MLX4_G64>(p, stream);
-    case MLX4_G32: return launch_gemv_codec<MLX4_G32>(p, stream);
-    case Q2_0: return launch_gemv_codec<Q2_0>(p, stream);
-    case Q8_0: return launch_gemv_codec<Q8_0>(p, stream);
-    case Q4_K: return launch_gemv_codec<Q4_K>(p, stream);
-    case TERNARY: return launch_gemv_codec<TERNARY>(p, stream);
+    case Q4_0: return launch_gemv_codec<Q4_0>(p, c.mm, stream);
+    case MLX4_G64: return launch_gemv_codec<MLX4_G64>(p, c.mm, stream);
+    case MLX4_G32: return launch_gemv_codec<MLX4_G32>(p, c.mm, stream);
+    case Q2_0: return launch_gemv_codec<Q2_0>(p, c.mm, stream);
+    case Q8_0: return launch_gemv_codec<Q8_0>(p, c.mm, stream);
+    case Q4_K: return launch_gemv_codec<Q4_K>(p, c.mm, stream);
+    case TERNARY: return launch_gemv_codec<TERNARY>(p, c.mm, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dispatch.h"
 #include "unpack.h"
 
 namespace qg {
@@ -29,10 +30,10 @@ __device__ __forceinline__ _Float16 *out_at(_Float16 *y, int ldy, int head_dim, 
     return y + (int64_t(h) * rows + m) * head_dim + (n - h * head_dim);
 }
 
-// Tiled MFMA kernels.  Return a hipError_t of the launch.
-hipError_t launch_gemm(const GemmProblem &p, int glu, hipStream_t stream);   // glu: 0 none, 1 SwiGLU, 2 GeGLU
-// Weight-streaming small-M kernels (1 <= m <= 64).
-hipError_t launch_gemv(const GemmProblem &p, hipStream_t stream);
+// Tiled MFMA kernels (every choice but Kern::GEMV).  Return a hipError_t of the launch.
+hipError_t launch_gemm(const GemmProblem &p, const Choice &c, hipStream_t stream);
+// Weight-streaming kernel (Kern::GEMV, 1 <= m <= 4).
+hipError_t launch_gemv(const GemmProblem &p, const Choice &c, hipStream_t stream);
 // fp16 image of the weights, [n, ldw].
 hipError_t launch_dequant(const GemmProblem &p, _Float16 *out, int64_t ldw, hipStream_t stream);
 // Plain streaming read of `bytes` (a multiple of 16) bytes; XOR checksum into *out.

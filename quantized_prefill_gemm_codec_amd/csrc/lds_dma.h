@@ -47,6 +47,13 @@ template <int N> __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait until this wave's outstanding LDS reads have returned.  The DMA loads
+// above write LDS from the memory path, which the compiler does not order
+// against earlier ds_read instructions; a wave that refills a slot it has
+// just read issues this first.  (An asm statement with a memory clobber, so
+// that no LDS access is moved across it.)
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ uint32_t lds_u32(const void *p)
 {
     return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)(p)));

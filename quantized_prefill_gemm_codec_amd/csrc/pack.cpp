@@ -160,7 +160,7 @@ void pack_ternary_codes(const uint8_t *c, int64_t n, int64_t k, const Geometry &
 
 extern "C" {
 
-int32_t qg_version(void) { return 101; }
+int32_t qg_version(void) { return 102; }
 
 const char *qg_status_str(qg_status s)
 {

@@ -415,3 +415,96 @@ def test_full_workload_sampled(torch, name):
     else:
         ref = oracle.gemm_ref(wl.codec, mats[0], wl.n, wl.k, x[rows_m], rows_n=rows_n)
         assert _err(ys, ref) <= TOL
+
+
+# ------------------------------------------------------- binding guards --
+
+def test_out_that_needs_a_copy_is_rejected_before_launch(torch):
+    """A caller's out that cannot be viewed as [M, N] rows (a strided 3-D
+    slice), lives on the host, or on another device is rejected with
+    ValueError and the buffer is left untouched: nothing is launched."""
+    codec, n, k = 1, 64, 64
+    canon = synth.gen_weight(codec, n, k, 71)
+    w = _weight(torch, codec, n, k, canon)
+    x = _dev(torch, synth.gen_x(6, k, 72)).reshape(2, 3, k)
+    buf = torch.full((2, 4, n), 7.0, dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        qg.qgemm_prefill(w, x, out=buf[:, :3, :])
+    torch.cuda.synchronize()
+    assert bool((buf == 7.0).all())
+    with pytest.raises(ValueError):
+        qg.qgemm_prefill(w, x, out=torch.empty((2, 3, n), dtype=torch.float16))
+    with pytest.raises(ValueError):
+        qg.qgemm_prefill_heads(w, x.reshape(6, k), 32, out=torch.empty((2, 6, 32), dtype=torch.float16))
+    with pytest.raises(ValueError):
+        qg.qgemm_prefill(w, x, out=torch.empty((2, 3, n), dtype=torch.float32, device="cuda"))
+    good = torch.empty((2, 3, n), dtype=torch.float16, device="cuda")
+    assert qg.qgemm_prefill(w, x, out=good) is good
+    assert _err(good.reshape(6, n).cpu().numpy(), oracle.gemm_ref(codec, canon, n, k, synth.gen_x(6, k, 72))) <= TOL
+
+
+# ------------------------------------------------- non-finite tripwire --
+
+def _poison_scale(codec, canon, n, k, row, block):
+    """Canonical bytes with the fp16 scale (Q4_K: d) of one block of one row set to +Inf."""
+    c = canon.copy()
+    if codec in (2, 5):                                   # MLX: codes, then the fp16 scale plane
+        g = 64 if codec == 2 else 32
+        off = n * k // 2 + 2 * (row * (k // g) + block)
+    else:                                                 # block structs that open with fp16 d
+        size = {1: 18, 3: 34, 4: 34, 6: 144, 7: 54}[codec]
+        off = (row * (k // synth.BLOCK[codec]) + block) * size
+    c[off:off + 2] = np.array([0x7C00], np.uint16).view(np.uint8)
+    return c
+
+
+NONFINITE_CASES = [("prefill", 1, 300), ("prefill", 2, 33), ("prefill", 3, 1), ("prefill", 6, 129),
+                   ("gemv", 1, 64), ("gemv", 4, 2), ("gemv", 7, 1), ("swiglu", 2, 300), ("swiglu", 1, 33),
+                   ("geglu", 4, 40), ("geglu", 5, 129)]
+
+
+@pytest.mark.parametrize("entry,codec,m", NONFINITE_CASES)
+def test_non_finite_inputs_trip_exactly_their_rows_and_columns(torch, entry, codec, m):
+    """A NaN or Inf activation makes its output row non-finite, an Inf scale
+    makes its weight row's output column non-finite, and nothing leaks into
+    other rows or columns, which stay within the tolerance of the oracle on
+    clean data: the outputs' finite check (the pages' non-finite tripwire)
+    fires exactly where the inputs are bad."""
+    n, k, n_bad = 200, 512, 37
+    seed = 6100 + codec + m
+    x = synth.gen_x(m, k, seed)
+    xb = x.copy()
+    bad_rows = [m // 2] if m == 1 else [m // 2, m - 1]
+    xb[bad_rows[0], 17] = np.float16(np.nan)
+    if len(bad_rows) > 1:
+        xb[bad_rows[1], 300] = np.float16(np.inf)
+    gated = entry in ("swiglu", "geglu")
+    mats = [synth.gen_weight(codec, n, k, seed, t) for t in ((synth.T_WG, synth.T_WU) if gated else (synth.T_W,))]
+    bad = [_poison_scale(codec, mats[0], n, k, n_bad, 1)] + mats[1:]
+    ws = [_weight(torch, codec, n, k, c) for c in bad]
+    xd = _dev(torch, xb)
+    if entry == "prefill":
+        y = qg.qgemm_prefill(ws[0], xd)
+    elif entry == "gemv":
+        y = qg.qgemv_decode(ws[0], xd)
+    elif entry == "swiglu":
+        y = qg.qgemm_swiglu(ws[0], ws[1], xd)
+    else:
+        y = qg.qgemm_geglu(ws[0], ws[1], xd)
+    y = y.cpu().numpy().astype(np.float64)
+    want_bad = np.zeros((m, n), bool)
+    want_bad[bad_rows, :] = True
+    want_bad[:, n_bad] = True
+    assert np.array_equal(~np.isfinite(y), want_bad)
+    with pytest.raises(AssertionError, match="non-finite"):
+        _err(y, np.ones_like(y))
+    rows = np.setdiff1d(np.arange(m), bad_rows)
+    cols = np.setdiff1d(np.arange(n), [n_bad])
+    if len(rows):
+        if gated:
+            fn = oracle.swiglu_ref if entry == "swiglu" else oracle.geglu_ref
+            ref = fn(codec, mats[0], mats[1], n, k, x[rows], rows_n=cols)
+            assert _err_beyond_fp16_rounding(y[np.ix_(rows, cols)], ref) <= TOL
+        else:
+            ref = oracle.gemm_ref(codec, mats[0], n, k, x[rows], rows_n=cols)
+            assert _err(y[np.ix_(rows, cols)], ref) <= TOL

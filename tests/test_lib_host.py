@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(qg.EXPORTS)
-    assert qg.qg_version() == 101
+    assert qg.qg_version() == 102
 
 
 @pytest.mark.parametrize("codec,n,k", [(1, 8192, 2048), (1, 40, 96), (2, 14336, 4096), (3, 4096, 4096), (3, 33, 128),

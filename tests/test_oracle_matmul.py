@@ -133,3 +133,22 @@ def test_geglu_identities():
     u = rng.normal(0, 2, g.size)
     assert np.allclose(oracle.geglu(g, u), got * u, rtol=1e-15, atol=0)
 
+
+
+def test_non_finite_propagates_along_its_row_and_column():
+    """IEEE rules the oracle inherits: a NaN or Inf activation makes its whole
+    output row non-finite (x * 0 is NaN for x = Inf or NaN) and an Inf weight
+    its whole output column; every other output stays finite."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, 64)).astype(np.float16)
+    w = rng.standard_normal((5, 64))
+    w[:, 10] = 0.0
+    x[1, 10] = np.float16(np.nan)
+    x[2, 20] = np.float16(np.inf)
+    w[3, 40] = np.inf
+    ref = oracle.matmul_xwt(x, w)
+    bad = ~np.isfinite(ref)
+    want = np.zeros((4, 5), bool)
+    want[[1, 2], :] = True
+    want[:, 3] = True
+    assert np.array_equal(bad, want)
