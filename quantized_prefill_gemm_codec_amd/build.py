@@ -7,6 +7,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -24,9 +25,15 @@ HEADERS = ["planar.h", "unpack.h", "launch.h", "lds_dma.h"]
 
 # -packed-fp32-ops is switched off for all device code: the compiler then never
 # forms v_pk_{add,mul,fma}_f32 from scalar fp32 code.
-HIPCC_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+# -Werror: the sources compile without a single warning.  The resource-usage
+# remarks give every kernel's registers, scratch and LDS, checked below.
+HIPCC_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-Rpass-analysis=kernel-resource-usage",
                f"-I{os.path.join(ROOT, 'include')}"]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Werror"]
+RESOURCES = os.path.join(BUILD, "kernel_resources.txt")
+LDS_MAX = 160 * 1024   # bytes of LDS per compute unit on gfx950
 
 
 def hipcc() -> str:
@@ -43,6 +50,52 @@ def _run(cmd):
     return r
 
 
+def _demangle(names):
+    try:
+        r = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True, check=True)
+        out = r.stdout.splitlines()
+        return out if len(out) == len(names) else list(names)
+    except (OSError, subprocess.CalledProcessError):
+        return list(names)
+
+
+def kernel_resources(stderr: str):
+    """Per-kernel resource remarks of one hipcc run: {name: {field: value}}."""
+    kernels, cur = {}, None
+    for line in stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = kernels.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z][A-Za-z /\[\]]*?):\s+(\S+) \[-Rpass-analysis", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = m.group(2)
+    return kernels
+
+
+def check_resources(kernels):
+    """Every kernel runs without scratch memory (no register spills, no
+    dynamic stack) and within the LDS of one compute unit; returns the table
+    lines, raises RuntimeError listing every kernel that breaks a budget."""
+    names = sorted(kernels)
+    pretty = _demangle(names)
+    lines, bad = [], []
+    for raw, name in zip(names, pretty):
+        r = kernels[raw]
+        scratch = int(r.get("ScratchSize [bytes/lane]", "0"))
+        spills = int(r.get("VGPRs Spill", "0")) + int(r.get("SGPRs Spill", "0"))
+        lds = int(r.get("LDS Size [bytes/block]", "0"))
+        dyn = r.get("Dynamic Stack", "False") != "False"
+        lines.append(f"{name}: VGPRs={r.get('VGPRs')} AGPRs={r.get('AGPRs')} SGPRs={r.get('TotalSGPRs')} "
+                     f"scratch={scratch} spills={spills} LDS={lds} occupancy={r.get('Occupancy [waves/SIMD]')}")
+        if scratch or spills or dyn or lds > LDS_MAX:
+            bad.append(lines[-1])
+    if bad:
+        raise RuntimeError("kernels over their resource budget (scratch, spills, dynamic stack or LDS):\n" +
+                           "\n".join(bad))
+    return lines
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link libqgemm.so; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
@@ -52,14 +105,19 @@ def build(verbose: bool = False) -> str:
     for src in HIP_SOURCES + CXX_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
-        flags = HIPCC_FLAGS if src.endswith(".hip") else ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+        flags = HIPCC_FLAGS if src.endswith(".hip") else CXX_FLAGS
         compiler = cc if src.endswith(".hip") else "g++"
         jobs.append([compiler, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
     workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
+    kernels = {}
     with cf.ThreadPoolExecutor(workers) as ex:
         for r in ex.map(_run, jobs):
+            kernels.update(kernel_resources(r.stderr))
             if verbose and r.stderr:
                 sys.stderr.write(r.stderr)
+    table = check_resources(kernels)
+    with open(RESOURCES, "w") as f:
+        f.write("\n".join(table) + "\n")
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)

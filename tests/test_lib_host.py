@@ -355,3 +355,36 @@ def _attn(L, **kw):
 ])
 def test_attention_argument_errors(kw, status):
     assert _attn(qg.lib(), **kw) == status
+
+
+def test_build_guard_rejects_kernels_with_scratch_or_spills():
+    """The build parses hipcc's resource-usage remarks and refuses a library
+    whose kernels spill registers to scratch or exceed the compute unit's LDS;
+    the remark format it reads is the compiler's."""
+    from quantized_prefill_gemm_codec_amd import build as qbuild
+
+    def remarks(name, scratch, vspill, lds):
+        pre = "x.hip:1:1: remark: "
+        tail = " [-Rpass-analysis=kernel-resource-usage]"
+        return "\n".join([pre + f"Function Name: {name}" + tail, pre + "    VGPRs: 128" + tail,
+                          pre + "    AGPRs: 0" + tail, pre + f"    ScratchSize [bytes/lane]: {scratch}" + tail,
+                          pre + "    Dynamic Stack: False" + tail, pre + "    Occupancy [waves/SIMD]: 2" + tail,
+                          pre + "    SGPRs Spill: 0" + tail, pre + f"    VGPRs Spill: {vspill}" + tail,
+                          pre + f"    LDS Size [bytes/block]: {lds}" + tail])
+
+    ok = qbuild.kernel_resources(remarks("_Z2okv", 0, 0, 65536))
+    assert ok["_Z2okv"]["ScratchSize [bytes/lane]"] == "0"
+    assert len(qbuild.check_resources(ok)) == 1
+    for bad in (remarks("_Z3badv", 16, 0, 1024), remarks("_Z3badv", 0, 3, 1024), remarks("_Z3badv", 0, 0, 200000)):
+        with pytest.raises(RuntimeError, match="over their resource budget"):
+            qbuild.check_resources(qbuild.kernel_resources(bad))
+
+
+def test_built_kernels_use_no_scratch():
+    """The table the last build wrote: every kernel without scratch or spills."""
+    from quantized_prefill_gemm_codec_amd import build as qbuild
+    if not os.path.exists(qbuild.RESOURCES):
+        pytest.skip("library not built in this tree")
+    lines = open(qbuild.RESOURCES).read().splitlines()
+    assert len(lines) >= 80
+    assert all(" scratch=0 spills=0 " in ln for ln in lines), [ln for ln in lines if " scratch=0 spills=0 " not in ln]
