@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 HIP_SOURCES = ["gemm.hip", "gemv.hip", "attention.hip", "api.hip"]
 CXX_SOURCES = ["pack.cpp"]
-HEADERS = ["planar.h", "unpack.h", "launch.h", "lds_dma.h"]
+HEADERS = ["planar.h", "unpack.h", "launch.h", "lds_dma.h", "dispatch.h", "kutil.h"]
 
 # -packed-fp32-ops is switched off for all device code: the compiler then never
 # forms v_pk_{add,mul,fma}_f32 from scalar fp32 code.

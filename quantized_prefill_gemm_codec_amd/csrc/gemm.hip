@@ -27,15 +27,12 @@
 // gemm_dma_kernel (M > 128, and M <= 128 with a split k-loop, plain or gated):
 // X tiles, code chunks and scale records all reach LDS by hardware DMA a few
 // k-steps ahead of use; see the comment above the kernel.
-#include <type_traits>
-
+#include "kutil.h"
 #include "launch.h"
 #include "lds_dma.h"
 
 namespace qg {
 namespace {
-
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // Consecutive workgroup ids land on different XCDs (round-robin over 8); give
 // each XCD a contiguous run of tiles, m fastest, so the tiles of one XCD share
@@ -78,18 +75,6 @@ template <int GLU> __device__ __forceinline__ float glu_mul(float g, float u)
     else
         return sigmoid_mul(g, 1.5957691216057308f * __builtin_fmaf(0.044715f * g, g * g, g), u);
 }
-
-// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), unrolled.
-template <int N, int I = 0, class F> __device__ __forceinline__ void static_for(F &&f)
-{
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<N, I + 1>(f);
-    }
-}
-
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100, SG_DS_WR = 0x200;
 
 template <int CODEC, int BM, int BN, int WM, int WN, int GLU>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmArgs a)
@@ -557,7 +542,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
                     cw[mt][fn].a = *reinterpret_cast<const uint32_t *>(cp + lane * 4);
                     cw[mt][fn].b = *reinterpret_cast<const unsigned short *>(cp + 256 + lane * 2);
                     cw[mt][fn].tl = *reinterpret_cast<const unsigned char *>(cp + 384 + (lane >> 1));
-                    cw[mt][fn].d = *reinterpret_cast<const _Float16 *>(sp + i * 2);
+                    cw[mt][fn].d = *reinterpret_cast<const unsigned short *>(sp + i * 2);
                     prepare_lane<CODEC>(cw[mt][fn]);
                 } else if constexpr (CODEC == Q4_K) {
                     cw[mt][fn].c = *reinterpret_cast<const u32x4 *>(wp);
@@ -567,14 +552,14 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
                 } else if constexpr (CODEC == Q8_0) {
                     cw[mt][fn].lo = *reinterpret_cast<const u32x4 *>(wp);
                     cw[mt][fn].hi = *reinterpret_cast<const u32x4 *>(wp + 1024);
-                    cw[mt][fn].d = *reinterpret_cast<const _Float16 *>(sp + lane * 2);
+                    cw[mt][fn].d = *reinterpret_cast<const unsigned short *>(sp + lane * 2);
                 } else if constexpr (CODEC == Q2_0) {
                     cw[mt][fn].c = *reinterpret_cast<const u32x2 *>(wp);
-                    cw[mt][fn].d = *reinterpret_cast<const _Float16 *>(sp + i * 2);
+                    cw[mt][fn].d = *reinterpret_cast<const unsigned short *>(sp + i * 2);
                 } else {
                     cw[mt][fn].c = *reinterpret_cast<const u32x4 *>(wp);
                     if constexpr (CODEC == Q4_0)
-                        cw[mt][fn].d = *reinterpret_cast<const _Float16 *>(sp + lane * 2);
+                        cw[mt][fn].d = *reinterpret_cast<const unsigned short *>(sp + lane * 2);
                     else if constexpr (CODEC == MLX4_G32)
                         cw[mt][fn].sb = *reinterpret_cast<const uint32_t *>(sp + lane * 4);
                     else

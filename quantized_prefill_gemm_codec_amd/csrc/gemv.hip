@@ -50,9 +50,6 @@ struct GemvArgs {
     int x_lds;               // bytes of the X region
 };
 
-// memory instructions one load_lane issues
-template <int CODEC> constexpr int lane_loads() { return CODEC == TERNARY ? 4 : (CODEC == Q8_0 || CODEC == Q4_K) ? 3 : 2; }
-
 template <int CODEC> constexpr int corr_floats() { return CODEC == MLX4_G64 || CODEC == MLX4_G32 || CODEC == Q4_K ? 2 : 1; }
 
 // x_s[p] = x_{2p} + x_{2p+1} summed over the 4 sub-step chunks of the slice.
@@ -188,7 +185,7 @@ __device__ __forceinline__ float block_sum(const LaneCodes<CODEC> &lc, const flo
     else if constexpr (CODEC == Q4_K)
         sc = lc.dd;
     else
-        sc = __builtin_bit_cast(unsigned short, lc.d);
+        sc = lc.d;
     const f16x2 sb = as_f16x2(sc);
     if constexpr (CODEC == Q4_K) {
         const float dsc = float(sb[0]) * float(lc.scm & 0xFFu);

@@ -70,9 +70,12 @@ __device__ __forceinline__ Magics make_magics()
 // The codes a lane owns in one (row group, k-step) chunk, plus its scales.
 template <int CODEC> struct LaneCodes;
 
+// Scales held as raw binary16 bits in the low half of a 32-bit register (as
+// the 16-bit loads deliver them): a _Float16 field lets the compiler pack two
+// lanes' scales into one register, and the packing then waits for both loads.
 template <> struct LaneCodes<Q4_0> {
     u32x4 c;
-    _Float16 d;
+    uint32_t d;
 };
 template <> struct LaneCodes<MLX4_G64> {
     u32x4 c;
@@ -84,11 +87,11 @@ template <> struct LaneCodes<MLX4_G32> {
 };
 template <> struct LaneCodes<Q2_0> {
     u32x2 c;
-    _Float16 d;
+    uint32_t d;
 };
 template <> struct LaneCodes<Q8_0> {
     u32x4 lo, hi;    // dwords 0..3 (sub-steps 0, 1) and 4..7 (sub-steps 2, 3)
-    _Float16 d;
+    uint32_t d;
 };
 template <> struct LaneCodes<Q4_K> {
     u32x4 c;
@@ -102,7 +105,7 @@ template <> struct LaneCodes<TERNARY> {
     uint32_t a;                // bytes E0 O0 E1 O1
     uint32_t b;                // bytes E2 O2 (low 16 bits)
     uint32_t tl;               // the tail byte shared with the neighbouring lane (low 8 bits)
-    _Float16 d;
+    uint32_t d;
     uint32_t r0, r1, r2, r3;   // from prepare_lane: (E_b, O_b) one byte per 16-bit half; tail twice
     uint32_t m3;               // from prepare_lane: 16-bit digit multipliers of the lane's two tail digits
 };
@@ -247,7 +250,8 @@ __device__ __forceinline__ f16x8 unpack_substep(const LaneCodes<CODEC> &lc, int 
             const f16x2 bi = {sb[1], sb[1]};
             w = __builtin_elementwise_fma(q[p], sc, bi);
         } else if constexpr (CODEC != Q4_K) {
-            const f16x2 dd = {lc.d, lc.d};
+            const _Float16 dh = __builtin_bit_cast(_Float16, (unsigned short)lc.d);
+            const f16x2 dd = {dh, dh};
             w = q[p] * dd;
         }
         out[2 * p] = w[0];
@@ -336,6 +340,9 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int rg, int groups, int lane
     return o;
 }
 
+// memory instructions one load_lane issues
+template <int CODEC> constexpr int lane_loads() { return CODEC == TERNARY ? 4 : (CODEC == Q8_0 || CODEC == Q4_K) ? 3 : 2; }
+
 // Load the chunk (row group rg, k-step t) codes and scales a lane owns.
 // `ksteps` = padded K / 64, `kb128` = K / 128 (Q2_0 scale plane pitch).
 // rg and t are wave-uniform: the chunk part of each address is a scalar
@@ -353,11 +360,11 @@ __device__ __forceinline__ LaneCodes<CODEC> load_lane(const PlaneRsrc &w, LaneOf
         lc.a = __builtin_amdgcn_raw_buffer_load_b32(w.qs, o.q, base, AUX);
         lc.b = __builtin_amdgcn_raw_buffer_load_b16(w.qs, o.q2, base, AUX);
         lc.tl = __builtin_amdgcn_raw_buffer_load_b8(w.qs, o.q3, base, AUX);
-        lc.d = load_f16(w.sc, o.s, (uint32_t(rg) * uint32_t(ksteps >> 2) + uint32_t(t >> 2)) * 64u);
+        lc.d = __builtin_amdgcn_raw_buffer_load_b16(w.sc, o.s, (uint32_t(rg) * uint32_t(ksteps >> 2) + uint32_t(t >> 2)) * 64u, 0);
     } else if constexpr (CODEC == Q8_0) {
         lc.lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 2048, AUX));
         lc.hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 2048 + 1024, AUX));
-        lc.d = load_f16(w.sc, o.s, chunk * 128);
+        lc.d = __builtin_amdgcn_raw_buffer_load_b16(w.sc, o.s, chunk * 128, 0);
     } else if constexpr (CODEC == Q4_K) {
         // record of (row group, super-block): u16 [4 k-steps][64 lanes], then u32 [32 rows]
         lc.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 1024, AUX));
@@ -366,11 +373,11 @@ __device__ __forceinline__ LaneCodes<CODEC> load_lane(const PlaneRsrc &w, LaneOf
         lc.dd = __builtin_amdgcn_raw_buffer_load_b32(w.sc, o.s2, rec, AUX);
     } else if constexpr (CODEC == Q2_0) {
         lc.c = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(w.qs, o.q, chunk * 512, AUX));
-        lc.d = load_f16(w.sc, o.s, (uint32_t(rg) * kb128 + uint32_t(t >> 1)) * 64);
+        lc.d = __builtin_amdgcn_raw_buffer_load_b16(w.sc, o.s, (uint32_t(rg) * kb128 + uint32_t(t >> 1)) * 64, 0);
     } else {
         lc.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w.qs, o.q, chunk * 1024, AUX));
         if constexpr (CODEC == Q4_0)
-            lc.d = load_f16(w.sc, o.s, chunk * 128);
+            lc.d = __builtin_amdgcn_raw_buffer_load_b16(w.sc, o.s, chunk * 128, 0);
         else if constexpr (CODEC == MLX4_G32)
             lc.sb = __builtin_amdgcn_raw_buffer_load_b32(w.sc, o.s, chunk * 256, AUX);
         else

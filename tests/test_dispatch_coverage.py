@@ -80,6 +80,7 @@ def test_reachable_set_size():
     ("prefill", 1, 1, 14336, 4096, "gemv_kernel<1, 1>"),
     ("prefill", 1, 3, 14336, 4096, "gemv_kernel<1, 4>"),
     ("gemv", 1, 64, 14336, 4096, "gemm_dma_kernel<1, 64, 64, 1, 1, 4, 0, 3, 1>"),
+    ("prefill", 1, 65, 14336, 4096, "gemm_dma_kernel<1, 64, 64, 1, 1, 4, 0, 3, 1>"),
     ("prefill", 1, 2048, 8192, 2048, "gemm_dma_kernel<1, 128, 512, 1, 8, 1, 0, 3, 1>"),
     ("prefill", 3, 2048, 4096, 4096, "gemm_dma_kernel<3, 128, 256, 1, 8, 1, 0, 2, 2>"),
     ("swiglu", 2, 2048, 14336, 4096, "gemm_dma_kernel<2, 128, 256, 1, 8, 1, 1, 3, 1>"),
