@@ -19,9 +19,14 @@ read_ceiling (decode lines): the library's plain streaming-read kernel timed the
 same way over the same number of bytes -- what one read-only kernel sustains
 at that size on this device, beside the GEMV's fraction of 8 TB/s.
 
+parity: every line's output (the last timed launch) is compared with the fp64
+oracle on sampled rows x columns, first and last included; the headline is
+also compared on every row the CPU baseline computes.
+
 cpu_baseline: the fp64 oracle (tests' reference implementation) timed on a
-bounded sample of the same workload -- the first rows of X against all of W --
-on the host's cores; the GPU output is checked against it on the same sample.
+bounded sample of the same workload -- exact decode of all of W, then the
+first rows of X against it -- on the host's cores, decode and matmul timed
+apart; the GPU output is checked against it on the same rows.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--no-cpu] [--no-secondary] [--rotate R]
@@ -46,13 +51,16 @@ PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 MALL_BYTES = 256 << 20
 HEADLINE = "q4_0_prefill_2048x2048x8192"
-SECONDARY = ["mlx4_swiglu_2048x4096x14336", "q2_0_prefill_2048x4096x4096",
+SECONDARY = ["q4_0_tiny_16x256x256", "mlx4_swiglu_2048x4096x14336", "q2_0_prefill_2048x4096x4096",
              "q4_0_gemv_1x4096x14336", "q4_0_gemv_64x4096x14336", "q8_0_prefill_2048x2048x8192",
              "mlx4_geglu_2048x4096x14336", "q4_0_qproj_heads_2048x4096x4096", "mlx4_g32_prefill_2048x2048x8192",
              "q4_k_prefill_2048x2048x8192", "q4_k_gemv_1x4096x14336",
              "ternary_prefill_2048x2048x8192", "ternary_gemv_1x4096x14336"]
-KERNEL_SOURCES = ["gemm.hip", "gemv.hip", "unpack.h", "planar.h", "lds_dma.h"]
-ATTN_SOURCES = ["attention.hip", "unpack.h"]
+# sources whose change invalidates counter-derived traffic figures: the kernels
+# and everything that decides which kernel runs with which launch shape
+KERNEL_SOURCES = ["gemm.hip", "gemv.hip", "api.hip", "launch.h", "dispatch.h", "kutil.h", "unpack.h", "planar.h",
+                  "lds_dma.h"]
+ATTN_SOURCES = ["attention.hip", "api.hip", "launch.h", "unpack.h"]
 
 
 def kernel_source_hash(files=KERNEL_SOURCES) -> str:
@@ -112,7 +120,13 @@ class Prepared:
         st = fn(*args)
         if st != 0:
             raise RuntimeError(f"{fn.__name__} returned status {st}")
-        return self.sets[i % self.rotate][2][:, :self.wl.n]
+        self.last = i % self.rotate
+        return self.sets[self.last][2][:, :self.wl.n]
+
+    def last_out(self):
+        """Output buffer of the most recent launch ([M, N] rows; head-major data for 'heads')."""
+        y = self.sets[getattr(self, "last", 0)][2]
+        return y if self.wl.op == "heads" else y[:, :self.wl.n]
 
 
 class ReadPrepared:
@@ -208,6 +222,10 @@ class AttnPrepared:
         st = fn(*args)
         if st != 0:
             raise RuntimeError(f"{fn.__name__} returned status {st}")
+        self.last = i % self.rotate
+
+    def last_out(self):
+        return self.sets[getattr(self, "last", 0)][2]
 
 
 def time_launches(torch, prep, steps, warmup, settle_ms=SETTLE_MS):
@@ -253,42 +271,123 @@ def load_traffic(name):
     return None
 
 
+def _sample(rng, size, count):
+    """count sorted indices out of range(size), always with the first and the last."""
+    if size <= count:
+        return np.arange(size)
+    mid = rng.choice(np.arange(1, size - 1), count - 2, replace=False)
+    return np.sort(np.concatenate([[0, size - 1], mid]))
+
+
+def _rel_err(y, ref):
+    return float(np.max(np.abs(y - ref)) / np.sqrt(np.mean(ref ** 2)))
+
+
+def gemm_parity(torch, prep, y, rows=8, cols=256):
+    """The last timed launch's output against the oracle on sampled rows x
+    columns (first and last of each included), element by element."""
+    import oracle
+    wl = prep.wl
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(wl.seed)
+    rm, rn = _sample(rng, wl.m, rows), _sample(rng, wl.n, cols)
+    if wl.op == "heads":
+        full = y.reshape(-1)[:wl.m * wl.n].reshape(wl.n // wl.head_dim, wl.m, wl.head_dim)
+        ys = full.permute(1, 0, 2).reshape(wl.m, wl.n)[rm][:, rn]
+    else:
+        ys = y[rm][:, rn]
+    ys = ys.float().cpu().numpy().astype(np.float64)
+    finite = bool(np.all(np.isfinite(ys)))
+    x = prep.x_host[rm]
+    out = {"rows": len(rm), "cols": len(rn), "tol": 1e-2, "finite": finite}
+    if wl.op in synth.GATED:
+        fn = oracle.swiglu_ref if wl.op == "swiglu" else oracle.geglu_ref
+        ref = fn(wl.codec, prep.canon[0], prep.canon[1], wl.n, wl.k, x, rows_n=rn)
+        raw = _rel_err(ys, ref) if finite else float("inf")
+        beyond = float(np.max(np.maximum(np.abs(ys - ref) - 2.0 ** -11 * np.abs(ref), 0.0)) /
+                       np.sqrt(np.mean(ref ** 2))) if finite else float("inf")
+        out.update({"max_abs_err_over_rms": round(raw, 6), "beyond_fp16_output_rounding": round(beyond, 6),
+                    "ok": bool(finite and beyond <= 1e-2)})
+    else:
+        ref = oracle.gemm_ref(wl.codec, prep.canon[0], wl.n, wl.k, x, rows_n=rn)
+        err = _rel_err(ys, ref) if finite else float("inf")
+        out.update({"max_abs_err_over_rms": round(err, 6), "ok": bool(finite and err <= 1e-2)})
+    return out
+
+
+def attn_parity(torch, prep, rows=6):
+    """The last timed launch's output against the oracle on sampled query rows of every head."""
+    from oracle.attention import q8kv_attention_ref
+    aw = prep.wl
+    torch.cuda.synchronize()
+    q = aw.q()
+    kc, vc = aw.kv()
+    rm = _sample(np.random.default_rng(aw.seed), aw.m, rows)
+    got = prep.last_out()[:, rm].float().cpu().numpy().astype(np.float64)
+    scale = np.float32(1.0 / np.sqrt(aw.head_dim)).item()
+    ref = q8kv_attention_ref(q, kc, vc, aw.kv_heads, aw.s, aw.causal, scale, rows=rm)
+    finite = bool(np.all(np.isfinite(got)))
+    err = _rel_err(got, ref) if finite else float("inf")
+    return {"rows": len(rm), "heads": aw.heads, "max_abs_err_over_rms": round(err, 6), "tol": 1e-2, "finite": finite,
+            "ok": bool(finite and err <= 1e-2)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(torch, prep, target_s=12.0):
-    """Oracle timed on the first rows of X against all of W; GPU checked on them."""
+    """The oracle timed on the host on a bounded sample of the workload: exact
+    fp64 decode of all of W (each matrix), then the naive fp64 triple loop over
+    the first rows of X; the GPU output is checked against it on those rows."""
     import oracle
     wl = prep.wl
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count() or 1
-    per_row_flops = 2 * wl.n * wl.k * (2 if wl.op in synth.GATED else 1)
+    mats = len(prep.canon)
+    per_row_flops = 2 * wl.n * wl.k * mats
 
-    def run(rows):
-        t0 = time.perf_counter()
-        if wl.op in synth.GATED:
-            fn = oracle.swiglu_ref if wl.op == "swiglu" else oracle.geglu_ref
-            ref = fn(wl.codec, prep.canon[0], prep.canon[1], wl.n, wl.k, prep.x_host[:rows], threads=threads)
-        else:
-            ref = oracle.gemm_ref(wl.codec, prep.canon[0], wl.n, wl.k, prep.x_host[:rows], threads=threads)
-        return ref, time.perf_counter() - t0
+    t0 = time.perf_counter()
+    ws = [oracle.decode(wl.codec, c, wl.n, wl.k) for c in prep.canon]
+    decode_s = time.perf_counter() - t0
+
+    def matmul(rows):
+        t = time.perf_counter()
+        refs = [oracle.matmul_xwt(prep.x_host[:rows], w, threads) for w in ws]
+        return refs, time.perf_counter() - t
 
     probe = min(wl.m, max(threads, 16))
-    _, dt = run(probe)
-    rows = int(min(wl.m, max(probe, probe * target_s / max(dt, 1e-3))))
-    rows = max(1, rows)
-    ref, dt = run(rows)
+    _, dt = matmul(probe)
+    rows = max(1, int(min(wl.m, max(probe, probe * target_s / max(dt, 1e-3)))))
+    refs, matmul_s = matmul(rows)
     reps = 1
-    while rows == wl.m and reps * dt < target_s * 0.8:  # whole workload is short: repeat it for a stable figure
-        _, dt_more = run(rows)
-        dt = (dt * reps + dt_more) / (reps + 1)
+    while rows == wl.m and reps * matmul_s < target_s * 0.8:   # whole workload is short: repeat for a stable figure
+        _, more = matmul(rows)
+        matmul_s = (matmul_s * reps + more) / (reps + 1)
         reps += 1
+    if wl.op in synth.GATED:
+        ref = (oracle.swiglu if wl.op == "swiglu" else oracle.geglu)(refs[0], refs[1])
+    else:
+        ref = refs[0]
     y = prep.launch(0)
     torch.cuda.synchronize()
     yh = y[:rows].cpu().numpy().astype(np.float64)
     finite = bool(np.all(np.isfinite(yh)))
-    err = float(np.max(np.abs(yh - ref)) / np.sqrt(np.mean(ref ** 2)))
-    base = {"value": round(per_row_flops * rows / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{rows} of {wl.m} rows of X against all {wl.n} rows of W (K={wl.k}), "
-                      f"exact fp64 decode + naive k-ascending fp64 loops, {dt:.1f} s per pass, "
-                      f"mean of {reps} pass(es)"}
+    err = _rel_err(yh, ref) if finite else float("inf")
+    total_s = decode_s + matmul_s
+    base = {"value": round(per_row_flops * rows / total_s / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "cpu_model": cpu_model(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "decode_s": round(decode_s, 3), "matmul_s": round(matmul_s, 3),
+            "matmul_gflops": round(per_row_flops * rows / matmul_s / 1e9, 2),
+            "sample": f"{rows} of {wl.m} rows of X against all {wl.n} rows of W (K={wl.k}); exact fp64 decode of "
+                      f"all of W ({decode_s:.2f} s), then the naive k-ascending fp64 triple loop ({matmul_s:.2f} s"
+                      f"{f', mean of {reps} passes' if reps > 1 else ''}); value = sampled flops / (decode + matmul)"}
     parity = {"sample_rows": rows, "max_abs_err_over_rms": err, "tol": 1e-2, "finite": finite,
               "ok": bool(finite and err <= 1e-2)}
     return base, parity
@@ -352,7 +451,9 @@ def main():
         "config": {"workload": wl.name, "codec": synth.CODEC_NAMES[wl.codec], "m": wl.m, "n": wl.n, "k": wl.k,
                    "op": wl.op, "rotate": prep.rotate},
         "roofline": roofline(wl, ms, load_traffic(wl.name)),
+        "kernel": qg.qg_kernel_for(wl.op, wl.codec, wl.m, wl.n, wl.k),
         "settle": {"ms": args.settle_ms, "launches": settled},
+        "parity": gemm_parity(torch, prep, prep.last_out()),
     }
     if wl.op == "gemv":
         rec["read_ceiling"] = read_ceiling(torch, qg, wl, prep.rotate, args.steps, args.warmup, args.settle_ms, ms)
@@ -367,11 +468,14 @@ def main():
             r2 = roofline(w2, ms2, load_traffic(name))
             sec[name] = {"us_per_launch": round(ms2 * 1e3, 2), "tflops": round(w2.flops() / (ms2 * 1e-3) / 1e12, 2),
                          "gbs": round(w2.algorithmic_bytes() / (ms2 * 1e-3) / 1e9, 1), "roofline": r2,
+                         "kernel": qg.qg_kernel_for(w2.op, w2.codec, w2.m, w2.n, w2.k),
                          "rotate": p2.rotate, "settle_launches": settled2}
+            sec[name]["parity"] = gemm_parity(torch, p2, p2.last_out())
             if w2.op == "gemv":
                 sec[name]["read_ceiling"] = read_ceiling(torch, qg, w2, p2.rotate, max(10, args.steps), args.warmup,
                                                          args.settle_ms, ms2)
-            print(f"# timed {name}: {ms2 * 1e3:.1f} us/launch", file=sys.stderr, flush=True)
+            print(f"# timed {name}: {ms2 * 1e3:.1f} us/launch, parity ok={sec[name]['parity']['ok']}",
+                  file=sys.stderr, flush=True)
             del p2
             torch.cuda.empty_cache()
         for name, aw in synth.ATTN_WORKLOADS.items():
@@ -383,15 +487,19 @@ def main():
                          "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS,
                                       "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
                                       "traffic": load_traffic(name)},
+                         "kernel": f"attn_q8kv_kernel<{aw.head_dim}>",
                          "rotate": p2.rotate, "settle_launches": settled2}
-            print(f"# timed {name}: {ms2 * 1e3:.1f} us/launch", file=sys.stderr, flush=True)
+            sec[name]["parity"] = attn_parity(torch, p2)
+            print(f"# timed {name}: {ms2 * 1e3:.1f} us/launch, parity ok={sec[name]['parity']['ok']}",
+                  file=sys.stderr, flush=True)
             del p2
             torch.cuda.empty_cache()
         rec["secondary"] = sec
     if not args.no_cpu:
         base, parity = cpu_baseline(torch, prep)
         rec["cpu_baseline"] = base
-        rec["parity"] = parity
+        rec["parity_oracle_rows"] = parity
+        rec["parity"]["ok"] = bool(rec["parity"]["ok"] and parity["ok"])
     print(json.dumps(rec), flush=True)
 
 
