@@ -238,7 +238,8 @@ qg_status qg_stream_read(const void *src, size_t bytes, uint32_t *out, void *str
  *  q         device fp16 [heads, m, head_dim] (the direct-head layout of
  *            qgemm_prefill_heads), 16-byte aligned
  *  o         device fp16 [heads, m, head_dim], written; 16-byte aligned
- *  k_codes   device int8 [kv_heads * s, head_dim] (two's complement q)
+ *  k_codes   device uint8 [kv_heads * s, head_dim], q + 128 for the Q8_0 code q
+ *            (as qg_pack_kv_host writes them)
  *  k_scales  device fp16 [kv_heads * s, head_dim / 32] (d of each 32 codes)
  *  v_codes, v_scales  the same for V; all four 16-byte aligned
  *  head_dim  64 or 128;  1 <= heads <= 65535, heads % kv_heads == 0;
@@ -252,7 +253,9 @@ qg_status qattn_prefill_q8kv(const void *q, void *o, int64_t heads, int64_t m, i
 
 /* Host-side split of canonical Q8_0 rows (GGUF block_q8_0: fp16 d then 32
  * int8 codes, per 32 elements of a row) into the planar KV cache format of
- * qattn_prefill_q8kv: codes [rows, head_dim] int8 and scales [rows,
+ * qattn_prefill_q8kv: codes [rows, head_dim] as the unsigned bytes q + 128
+ * (the sign bit flipped, so the kernel places them under a binary16 exponent
+ * without a further operation) and scales [rows,
  * head_dim / 32] fp16.  Byte moves only.  head_dim a multiple of 32 (<= 4096);
  * canonical_bytes >= rows * head_dim / 32 * 34 (else QG_ERR_SIZE). */
 qg_status qg_pack_kv_host(const void *canonical, size_t canonical_bytes, int64_t rows, int64_t head_dim,

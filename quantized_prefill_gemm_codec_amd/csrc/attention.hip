@@ -8,13 +8,15 @@
 // templated on the head dimension D in {64, 128}; releases page v0.3.0,
 // grouped-query attention and causal masking in the transformer block.
 //
-// One workgroup of four wave64 handles 128 queries of one head; each wave owns
-// 32 of them for the whole key range.  Per tile of 64 keys:
-//  * the 256 threads turn the next tile's int8 codes and fp16 block scales
-//    into fp16 K [64][D] (row-major) and V^T [D][64] in the other half of a
-//    double-buffered LDS area -- each element is the correctly rounded q * d,
-//    the weights' Q8_0 rule; V is transposed in registers (8 keys x 4 d per
-//    thread) so that it is stored with 16-byte writes.  The raw codes are
+// One workgroup of eight wave64 handles 128 queries of one head.  Its waves
+// form two groups of four that take the two halves of the query tile's key
+// range at the same time; in each group, wave w owns queries 32 w .. 32 w + 31
+// for its half.  Per tile of 64 keys and group:
+//  * the group's 256 threads turn the next tile's codes and fp16 block scales
+//    into fp16 K [64][D] (row-major) and V^T [D][64] in the other half of the
+//    group's double-buffered LDS area -- each element is the correctly rounded
+//    q * d, the weights' Q8_0 rule; V is transposed in registers (8 keys x 4 d
+//    per thread) so that it is stored with 16-byte writes.  The raw codes are
 //    loaded one tile ahead of that, so one barrier per tile suffices;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_f16 (A = K rows, B = the wave's Q
 //    fragments, loaded once).  K rows are read in the order pi below, which
@@ -23,11 +25,16 @@
 //  * online softmax in fp32 on the log2 scale: the row maximum and sum are
 //    lane-local over 32 scores plus one exchange with lane l ^ 32 (the other
 //    half of the same query's keys); the O accumulators are rescaled by
-//    2^(m_old - m_new);
+//    2^(m_old - m_new) when the maximum moves;
 //  * O^T += V^T P^T (A = V^T rows from LDS, B = P as fp16).
-// The epilogue divides by the row sum and writes O [H, M, D] fp16.
-// Causal work per query tile grows linearly; workgroups are ordered so that
-// each heavy query tile is launched next to a light one (see tile_of).
+// At the end the second group hands its (maximum, sum, O^T) to the first
+// through LDS, which merges the two halves (each rescaled to the common
+// maximum), divides by the row sum and writes O [H, M, D] fp16.
+// Why two groups: one wave's per-tile chain (dequantize, QK^T, softmax, PV)
+// is a serial dependency of about 2 us that another workgroup on the same
+// compute unit barely slows, so the kernel took as long as the longest key
+// range -- the last query tile's 32 tiles.  Splitting every range in two
+// halves that chain.  Workgroups are ordered heaviest (causal) first.
 #include "launch.h"
 
 namespace qg {
@@ -35,7 +42,10 @@ namespace {
 
 constexpr int AT_BQ = 128;   // queries per workgroup
 constexpr int AT_BK = 64;    // keys per tile
-constexpr int AT_NT = 256;   // threads per workgroup
+constexpr int AT_GT = 256;   // threads per key-range group (one tile's dequantization)
+constexpr int AT_NG = 2;     // key-range groups per workgroup
+constexpr int AT_NT = AT_GT * AT_NG;   // threads per workgroup
+constexpr float RESCALE_SLACK = 8.0f;   // log2 units a row maximum may rise before the O accumulators are rescaled
 
 struct AttnArgs {
     const _Float16 *q;
@@ -46,11 +56,11 @@ struct AttnArgs {
     float scale_log2;           // softmax scale times log2(e)
 };
 
-// 16 int8 codes (two's complement) of one 32-element block half -> the fp16
-// values q * d, in order.  XOR 0x80 turns q into q + 128 in 0..255; one
-// v_perm_b32 puts two such bytes under the binary16 exponent byte 0x64 (taken
-// from the constant word e64 = 0x64646464), which reads 1024 + q + 128;
-// subtracting 1152 is exact, the multiply by d rounds once.
+// 16 codes (stored as q + 128 in 0..255) of one 32-element block half -> the
+// fp16 values q * d, in order.  One v_perm_b32 puts two code bytes under the
+// binary16 exponent byte 0x64 (taken from the constant word e64 = 0x64646464),
+// which reads 1024 + q + 128; subtracting 1152 is exact, the multiply by d
+// rounds once.
 __device__ __forceinline__ void dequant16(u32x4 c, _Float16 d, uint32_t e64, u32x4 &lo, u32x4 &hi)
 {
     const f16x2 dd = {d, d};
@@ -58,7 +68,7 @@ __device__ __forceinline__ void dequant16(u32x4 c, _Float16 d, uint32_t e64, u32
     uint32_t r[8];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        const uint32_t x = c[w] ^ 0x80808080u;
+        const uint32_t x = c[w];
         // selector bytes 0-3 pick bytes of x, 4-7 bytes of e64
         const uint32_t p01 = __builtin_amdgcn_perm(e64, x, 0x04010400u);
         const uint32_t p23 = __builtin_amdgcn_perm(e64, x, 0x04030402u);
@@ -69,33 +79,27 @@ __device__ __forceinline__ void dequant16(u32x4 c, _Float16 d, uint32_t e64, u32
     hi = u32x4{r[4], r[5], r[6], r[7]};
 }
 
-// Four codes (d .. d + 3 of one key, two's complement) -> two fp16 pairs
+// Four codes (d .. d + 3 of one key, stored as q + 128) -> two fp16 pairs
 // (d, d + 1), (d + 2, d + 3) of q * scale, in the rounding of dequant16.
 __device__ __forceinline__ void dequant4(uint32_t c, _Float16 d, uint32_t e64, uint32_t &p01, uint32_t &p23)
 {
     const f16x2 dd = {d, d};
     const f16x2 off = {_Float16(1152.0f), _Float16(1152.0f)};
-    const uint32_t x = c ^ 0x80808080u;
+    const uint32_t x = c;
     p01 = as_u32((as_f16x2(__builtin_amdgcn_perm(e64, x, 0x04010400u)) - off) * dd);
     p23 = as_u32((as_f16x2(__builtin_amdgcn_perm(e64, x, 0x04030402u)) - off) * dd);
 }
 
-// Query tile and head of workgroup `lin` (0 .. tiles_q * heads - 1).  The
-// query heads [0, H/2) take their tiles longest (causal) first, the heads
-// [H/2, H) shortest first, so that workgroups lin and lin + half -- dispatched
-// to the same compute unit when all of them are resident -- carry
-// tiles_q - 1 key-tile rows of work between them.  A bijection for any H.
-__device__ __forceinline__ void tile_of(int lin, int tiles_q, int heads, int &qt, int &h)
+// Query tile and head of workgroup `lin` (0 .. tiles_q * heads - 1): causal
+// query tiles in decreasing order of their key range (all heads of the last
+// tile first), so that the workgroups dispatched as others finish are the
+// short ones; the heads of one tile are adjacent, and every group of
+// heads / kv_heads of them reads the same KV head.
+__device__ __forceinline__ void tile_of(int lin, int tiles_q, int heads, bool causal, int &qt, int &h)
 {
-    const int hh = heads / 2, half = hh * tiles_q;
-    if (lin < half) {
-        qt = tiles_q - 1 - lin % tiles_q;
-        h = lin / tiles_q;
-    } else {
-        const int l2 = lin - half;
-        qt = l2 % tiles_q;
-        h = hh + l2 / tiles_q;
-    }
+    const int r = lin / heads;
+    qt = causal ? tiles_q - 1 - r : r;
+    h = lin - r * heads;
 }
 
 // V^T row d keeps its chunk c (keys 8 c .. 8 c + 7) at chunk position
@@ -115,32 +119,39 @@ __device__ __forceinline__ int pi_row(int r)
 }
 
 template <int D>
-__global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
+__global__ __launch_bounds__(AT_NT, 1) void attn_q8kv_kernel(AttnArgs a)
 {
     constexpr int KP = D + 8;              // K tile row pitch (halves); the pad staggers LDS banks
     constexpr int VP = AT_BK;              // V^T tile row pitch (halves): 8 chunks of 8 keys, swizzled
     constexpr int NDB = D / 32;            // 32-row blocks of O^T
     constexpr int NDD = D / 16;            // 16-deep steps over d
     constexpr int CPR = D / 16;            // 16-code chunks per key (K)
-    constexpr int IPT = AT_BK * CPR / AT_NT;   // K chunks per thread
+    constexpr int IPT = AT_BK * CPR / AT_GT;   // K chunks per thread of a group
     constexpr int VITEMS = AT_BK * D / 32;           // V items of 8 keys x 4 d per tile
-    constexpr int VIT = (VITEMS + AT_NT - 1) / AT_NT;   // per thread (D = 64: half the threads)
+    constexpr int VIT = (VITEMS + AT_GT - 1) / AT_GT;   // per thread (D = 64: half the threads)
     constexpr int VDG = D / 4;             // 4-wide d groups per key
     static_assert(D == 64 || D == 128, "head dimension");
-    static_assert(IPT >= 1 && AT_BK * CPR % AT_NT == 0 && VITEMS % 64 == 0, "tile");
+    static_assert(IPT >= 1 && AT_BK * CPR % AT_GT == 0 && VITEMS % 64 == 0, "tile");
+    constexpr int KT = AT_BK * KP, VT = D * VP;       // halves of one K tile and one V^T tile
+    // the merge area (second group's O^T, maximum and sum) reuses the tiles
+    static_assert(4 * (D / 32) * 4 * 64 * 16 + 2 * 4 * 64 * 4 <= AT_NG * 2 * (KT + VT) * 2, "merge area");
 
-    __shared__ __attribute__((aligned(16))) _Float16 ks[2][AT_BK * KP];
-    __shared__ __attribute__((aligned(16))) _Float16 vt[2][D * VP];
+    // per group: K tiles [2][KT], then V^T tiles [2][VT]
+    __shared__ __attribute__((aligned(16))) _Float16 tiles[AT_NG][2 * (KT + VT)];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, qw = wave & 3;         // key-range group, query sub-tile
+    const int gtid = tid & (AT_GT - 1);
     const int i = lane & 31, g = lane >> 5;
+    _Float16 *const ksb = &tiles[grp][0];
+    _Float16 *const vtb = &tiles[grp][2 * KT];
     int qt, h;
-    tile_of(int(blockIdx.x), a.tiles_q, a.heads, qt, h);
+    tile_of(int(blockIdx.x), a.tiles_q, a.heads, a.causal != 0, qt, h);
     const int q0 = qt * AT_BQ;
     const int kvh = h / (a.heads / a.kv_heads);
     const int off = a.s - a.m;                        // the queries are the last m positions
-    const int qrow = q0 + 32 * wave + i;
+    const int qrow = q0 + 32 * qw + i;
 
     // Q fragments (B operand): lane (i, g) holds Q[qrow][16 dd + 8 g .. + 7]
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + int64_t(h) * a.m * D, uint32_t(a.m) * D * 2u);
@@ -154,6 +165,10 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
     int t_end = (a.s + AT_BK - 1) / AT_BK;
     if (a.causal)
         t_end = min(t_end, (off + q0 + AT_BQ - 1) / AT_BK + 1);
+    // the two halves of the key range: group 0 takes tiles [0, th), group 1
+    // [th, t_end) -- one fewer when t_end is odd
+    const int th = (t_end + 1) >> 1;
+    const int tb = grp ? th : 0, tn = grp ? t_end - th : th;
 
     // raw codes and scales of one tile, AT_BK * CPR chunks per matrix:
     // chunk j = key j / CPR, 16 codes from d = 16 (j % CPR)
@@ -173,7 +188,7 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
     auto fetch = [&](int t) {
 #pragma unroll
         for (int u = 0; u < IPT; ++u) {
-            const int j = tid + AT_NT * u, kk = j / CPR, c = j % CPR;
+            const int j = gtid + AT_GT * u, kk = j / CPR, c = j % CPR;
             const uint32_t key = uint32_t(t * AT_BK + kk);
             const bool in = key < uint32_t(a.s);
             kc[u] = __builtin_bit_cast(
@@ -182,7 +197,7 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
         }
 #pragma unroll
         for (int u = 0; u < VIT; ++u) {
-            const int j = tid + AT_NT * u, k8 = j / VDG, c4 = j % VDG;
+            const int j = gtid + AT_GT * u, k8 = j / VDG, c4 = j % VDG;
             if (j >= VITEMS)
                 break;
             // keys 8 k8 .. + 7 are D (codes) and D / 16 (scale bytes) apart:
@@ -213,15 +228,15 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
     auto stage = [&](int b) {
 #pragma unroll
         for (int u = 0; u < IPT; ++u) {
-            const int j = tid + AT_NT * u, kk = j / CPR, c = j % CPR;
+            const int j = gtid + AT_GT * u, kk = j / CPR, c = j % CPR;
             u32x4 lo, hi;
             dequant16(kc[u], kd[u], e64, lo, hi);
-            *reinterpret_cast<u32x4 *>(&ks[b][kk * KP + 16 * c]) = lo;
-            *reinterpret_cast<u32x4 *>(&ks[b][kk * KP + 16 * c + 8]) = hi;
+            *reinterpret_cast<u32x4 *>(&ksb[b * KT + kk * KP + 16 * c]) = lo;
+            *reinterpret_cast<u32x4 *>(&ksb[b * KT + kk * KP + 16 * c + 8]) = hi;
         }
 #pragma unroll
         for (int u = 0; u < VIT; ++u) {
-            const int j = tid + AT_NT * u, k8 = j / VDG, c4 = j % VDG;
+            const int j = gtid + AT_GT * u, k8 = j / VDG, c4 = j % VDG;
             if (j >= VITEMS)
                 break;
             uint32_t p01[8], p23[8];
@@ -241,14 +256,16 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int d = 4 * c4 + r;
-                *reinterpret_cast<u32x4 *>(&vt[b][d * VP + 8 * (k8 ^ vswz(d))]) = rows[r];
+                *reinterpret_cast<u32x4 *>(&vtb[b * VT + d * VP + 8 * (k8 ^ vswz(d))]) = rows[r];
             }
         }
     };
-    fetch(0);
-    stage(0);
-    if (t_end > 1)
-        fetch(1);
+    if (tn > 0) {
+        fetch(tb);
+        stage(0);
+        if (tn > 1)
+            fetch(tb + 1);
+    }
     __syncthreads();
 
     f32x16 oacc[NDB];
@@ -263,13 +280,17 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
     // K rows this lane reads for the A operand, and the LDS offsets
     const int krow0 = pi_row(i), krow1 = 32 + pi_row(i);
 
-    for (int t = 0; t < t_end; ++t) {
-        const int b = t & 1;
+    // both groups step together (one barrier per step); a group whose half
+    // is one tile shorter idles through the last step
+    for (int it = 0; it < th; ++it) {
+      if (it < tn) {
+        const int t = tb + it;
+        const int b = it & 1;
         // the tile after this one goes into the other buffer: its last
         // readers finished before the barrier that ended the previous step
-        if (t + 1 < t_end) {
+        if (it + 1 < tn) {
             stage(b ^ 1);
-            if (t + 2 < t_end)
+            if (it + 2 < tn)
                 fetch(t + 2);
         }
 
@@ -280,7 +301,7 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 sacc[kb][e] = 0.0f;
-            const _Float16 *kp = &ks[b][(kb ? krow1 : krow0) * KP + 8 * g];
+            const _Float16 *kp = &ksb[b * KT + (kb ? krow1 : krow0) * KP + 8 * g];
 #pragma unroll
             for (int dd = 0; dd < NDD; ++dd) {
                 const f16x8 ka = *reinterpret_cast<const f16x8 *>(kp + 16 * dd);
@@ -292,7 +313,7 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
         // the query's own position are -inf.  Register 4 q + e of block kb
         // holds key 32 kb + 16 (q >> 1) + 8 g + 4 (q & 1) + e of the tile.
         const int kbase = t * AT_BK;
-        const bool edge = kbase + AT_BK > a.s || (a.causal && kbase + AT_BK - 1 > off + q0 + 32 * wave);
+        const bool edge = kbase + AT_BK > a.s || (a.causal && kbase + AT_BK - 1 > off + q0 + 32 * qw);
         // (the maximum is taken on the raw scores: the scale is positive)
         float tmax = -__builtin_inff();
         if (edge) {
@@ -312,19 +333,32 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
             for (int r = 0; r < 16; ++r)
                 tmax = __builtin_fmaxf(tmax, sacc[kb][r]);
         tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32)) * a.scale_log2;
-        const float mnew = __builtin_fmaxf(mrow, tmax);
+        // The running maximum moves only when a score exceeds it by more than
+        // 2^RESCALE_SLACK on the exp2 scale: until then P = 2^(s - m) stays at
+        // most 2^8 (exact range for fp16 P, and the fp32 sums and accumulators
+        // are unaffected), and the O accumulators need no rescale -- after the
+        // first tiles the maximum rarely moves that far.  Both lane halves of
+        // a row hold the same tmax and mrow, so they decide alike.
+        const bool moved = tmax > mrow + RESCALE_SLACK;
+        const float mnew = moved ? tmax : mrow;
+        // a row with no visible key yet (a whole half-range can be masked
+        // for the first queries) keeps maximum -inf: its P must be 0, not
+        // exp2(-inf + inf)
+        const float msub = mnew == -__builtin_inff() ? 0.0f : mnew;
         float lsum = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], a.scale_log2, -mnew));
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], a.scale_log2, -msub));
                 sacc[kb][r] = p;
                 lsum += p;
             }
         lsum += __shfl_xor(lsum, 32);
-        if (__builtin_amdgcn_ballot_w64(mnew != mrow) != 0) {   // some row's maximum moved: rescale
-            const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
+        if (__builtin_amdgcn_ballot_w64(moved) != 0) {   // some row's maximum moved: rescale
+            // rows whose maximum stayed keep their scale (their mrow may still
+            // be -inf, and -inf - -inf is NaN)
+            const float alpha = moved ? __builtin_amdgcn_exp2f(mrow - mnew) : 1.0f;
             lrow *= alpha;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -347,14 +381,49 @@ __global__ __launch_bounds__(AT_NT, 2) void attn_q8kv_kernel(AttnArgs a)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             const int d = 32 * db + i;
-            const _Float16 *vp = &vt[b][d * VP];
+            const _Float16 *vp = &vtb[b * VT + d * VP];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const f16x8 va = *reinterpret_cast<const f16x8 *>(vp + 8 * ((2 * k + g) ^ vswz(d)));
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[k], oacc[db], 0, 0, 0);
             }
         }
+      }
         __syncthreads();   // tile t's buffer is free; tile t + 1's is written
+    }
+
+    // merge the halves: group 1 hands its O^T, maximum and sum to group 0
+    f32x4 *mo = reinterpret_cast<f32x4 *>(&tiles[0][0]);                 // [4 qw][NDB][4 q][64 lanes]
+    float *mm = reinterpret_cast<float *>(mo + 4 * NDB * 4 * 64);         // [2][4 qw][64 lanes]: maximum, sum
+    if (grp == 1) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                mo[((qw * NDB + db) * 4 + q) * 64 + lane] =
+                    f32x4{oacc[db][4 * q], oacc[db][4 * q + 1], oacc[db][4 * q + 2], oacc[db][4 * q + 3]};
+        mm[qw * 64 + lane] = mrow;
+        mm[(4 + qw) * 64 + lane] = lrow;
+    }
+    __syncthreads();
+    if (grp == 1)
+        return;
+    {
+        const float m1 = mm[qw * 64 + lane], l1 = mm[(4 + qw) * 64 + lane];
+        const float mx = __builtin_fmaxf(mrow, m1);
+        // a half with no visible key (maximum -inf) contributes nothing
+        const float a0 = mrow == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mrow - mx);
+        const float a1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - mx);
+        lrow = lrow * a0 + l1 * a1;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 o1 = mo[((qw * NDB + db) * 4 + q) * 64 + lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    oacc[db][4 * q + e] = oacc[db][4 * q + e] * a0 + o1[e] * a1;
+            }
     }
 
     // O[h][qrow][32 db + 8 q + 4 g + e] = O^T acc / row sum

@@ -346,7 +346,8 @@ qg_status qg_pack_kv_host(const void *canonical, size_t canonical_bytes, int64_t
         for (int64_t b = 0; b < nb; ++b) {
             const uint8_t *blk = c + (r * nb + b) * 34;
             memcpy(sc + (r * nb + b) * 2, blk, 2);
-            memcpy(q + r * head_dim + b * 32, blk + 2, 32);
+            for (int j = 0; j < 32; ++j)   // q + 128: the two's-complement byte with its top bit flipped
+                q[r * head_dim + b * 32 + j] = uint8_t(blk[2 + j] ^ 0x80u);
         }
     return QG_OK;
 }

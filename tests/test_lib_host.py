@@ -331,9 +331,9 @@ def test_pack_kv_host_splits_blocks():
     assert L.qg_pack_kv_host(canon.ctypes.data, canon.size, rows, d, codes.ctypes.data, scales.ctypes.data) == 0
     blk = canon.reshape(rows, d // 32, 34)
     assert np.array_equal(scales.reshape(rows, d // 32, 2), blk[:, :, :2])
-    assert np.array_equal(codes.reshape(rows, d // 32, 32), blk[:, :, 2:])
+    assert np.array_equal(codes.reshape(rows, d // 32, 32), blk[:, :, 2:] ^ 0x80)     # q + 128
     # decoded from the planar split, the values are the oracle's Q8_0 decode
-    w = codes.view(np.int8).reshape(rows, d).astype(np.float64) * np.repeat(
+    w = (codes.reshape(rows, d).astype(np.float64) - 128.0) * np.repeat(
         scales.view(np.float16).reshape(rows, d // 32).astype(np.float64), 32, axis=1)
     assert np.array_equal(w, oracle.decode(oracle.Q8_0, canon, rows, d))
     assert L.qg_pack_kv_host(canon.ctypes.data, canon.size - 1, rows, d, codes.ctypes.data, scales.ctypes.data) == -7
