@@ -55,7 +55,8 @@ SECONDARY = ["q4_0_tiny_16x256x256", "mlx4_swiglu_2048x4096x14336", "q2_0_prefil
              "q4_0_gemv_1x4096x14336", "q4_0_gemv_64x4096x14336", "q8_0_prefill_2048x2048x8192",
              "mlx4_geglu_2048x4096x14336", "q4_0_qproj_heads_2048x4096x4096", "mlx4_g32_prefill_2048x2048x8192",
              "q4_k_prefill_2048x2048x8192", "q4_k_gemv_1x4096x14336",
-             "ternary_prefill_2048x2048x8192", "ternary_gemv_1x4096x14336"]
+             "ternary_prefill_2048x2048x8192", "ternary_gemv_1x4096x14336",
+             "ternary_q2_prefill_2048x2048x8192", "ternary_q2_gemv_1x4096x14336"]
 # sources whose change invalidates counter-derived traffic figures: the kernels
 # and everything that decides which kernel runs with which launch shape
 KERNEL_SOURCES = ["gemm.hip", "gemv.hip", "api.hip", "launch.h", "dispatch.h", "kutil.h", "unpack.h", "planar.h",

@@ -75,7 +75,15 @@ extern "C" {
  *                    above 242 (byte 53: above 2) are invalid (QG_ERR_CODE).
  *                    (BitNet ternary: releases page v0.2, router formats;
  *                    TERNARY_1_58 in the v0.3.0 registry.  The pages give no
- *                    packing; 1.6875 bits per weight.) */
+ *                    packing; 1.6875 bits per weight.)
+ *  QG_CODEC_TERNARY_1_58_Q2  the same canonical bytes as QG_CODEC_TERNARY_1_58,
+ *                    held on the device as 2-bit codes q = t with each block's
+ *                    d repeated per 128 weights -- the QG_CODEC_Q2_0 planar
+ *                    format (w = (q - 1) d), run by the Q2_0 kernels.  2.125
+ *                    bits per weight in device memory instead of 1.625 + 1/16,
+ *                    in exchange for a decode without base-3 arithmetic (the
+ *                    pages' question whether a ternary codec's byte saving
+ *                    survives its decode cost: releases page v0.2). */
 typedef enum {
     QG_CODEC_Q4_0 = 1,
     QG_CODEC_MLX4_G64 = 2,
@@ -83,7 +91,8 @@ typedef enum {
     QG_CODEC_Q8_0 = 4,
     QG_CODEC_MLX4_G32 = 5,
     QG_CODEC_Q4_K = 6,
-    QG_CODEC_TERNARY_1_58 = 7
+    QG_CODEC_TERNARY_1_58 = 7,
+    QG_CODEC_TERNARY_1_58_Q2 = 8
 } qg_codec;
 
 typedef enum {

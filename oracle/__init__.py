@@ -24,7 +24,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "qgemm_oracle.c")
 LIB = os.path.join(HERE, "libqgemm_oracle.so")
 
-Q4_0, MLX4_G64, Q2_0, Q8_0, MLX4_G32, Q4_K, TERNARY = 1, 2, 3, 4, 5, 6, 7
+Q4_0, MLX4_G64, Q2_0, Q8_0, MLX4_G32, Q4_K, TERNARY, TERNARY_Q2 = 1, 2, 3, 4, 5, 6, 7, 8
 
 _lib = None
 
@@ -159,7 +159,7 @@ def canonical_rows(codec: int, canon: np.ndarray, n: int, k: int, rows: np.ndarr
     rows = np.asarray(rows, dtype=np.int64)
     if codec == Q4_0:
         return np.ascontiguousarray(canon.reshape(n, -1)[rows]).reshape(-1)
-    if codec in (Q2_0, Q8_0, Q4_K, TERNARY):
+    if codec in (Q2_0, Q8_0, Q4_K, TERNARY, TERNARY_Q2):
         return np.ascontiguousarray(canon.reshape(n, -1)[rows]).reshape(-1)
     group = 32 if codec == MLX4_G32 else 64
     codes = canon[: n * k // 2].reshape(n, -1)[rows]

@@ -71,6 +71,9 @@
 #define ORC_MLX4_G32 5
 #define ORC_Q4_K 6
 #define ORC_TERNARY 7
+/* codec 8 reads the same canonical ternary bytes as codec 7 (the library
+ * stores them differently on the device, which the oracle never sees) */
+#define ORC_TERNARY_Q2 8
 
 /* ---------------------------------------------------------------- fp16 --- */
 
@@ -167,6 +170,7 @@ int orc_block_geometry(int codec, int64_t *weights, int64_t *bytes)
     case ORC_MLX4_G32: *weights = 32;  *bytes = 20; return 1;
     case ORC_Q4_K:     *weights = 256; *bytes = 144; return 1;
     case ORC_TERNARY:  *weights = 256; *bytes = 54; return 1;
+    case ORC_TERNARY_Q2: *weights = 256; *bytes = 54; return 1;
     default: return 0;
     }
 }
@@ -332,7 +336,7 @@ int orc_decode_rows(int codec, const uint8_t *canon, int64_t n, int64_t k,
             decode_q8_0_row(canon + nn * (k / 32) * 34, k, wr);
         else if (codec == ORC_Q4_K)
             decode_q4_k_row(canon + nn * (k / 256) * 144, k, wr);
-        else if (codec == ORC_TERNARY) {
+        else if (codec == ORC_TERNARY || codec == ORC_TERNARY_Q2) {
             if (decode_ternary_row(canon + nn * (k / 256) * 54, k, wr))
                 return -2;
         }

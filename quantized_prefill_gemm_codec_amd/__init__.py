@@ -25,10 +25,12 @@ QG_CODEC_Q8_0 = 4
 QG_CODEC_MLX4_G32 = 5
 QG_CODEC_Q4_K = 6
 QG_CODEC_TERNARY_1_58 = 7
+QG_CODEC_TERNARY_1_58_Q2 = 8
 CODECS = {"q4_0": QG_CODEC_Q4_0, "mlx4_g64": QG_CODEC_MLX4_G64, "q2_0": QG_CODEC_Q2_0, "q8_0": QG_CODEC_Q8_0,
-          "mlx4_g32": QG_CODEC_MLX4_G32, "q4_k": QG_CODEC_Q4_K, "ternary": QG_CODEC_TERNARY_1_58}
+          "mlx4_g32": QG_CODEC_MLX4_G32, "q4_k": QG_CODEC_Q4_K, "ternary": QG_CODEC_TERNARY_1_58,
+          "ternary_q2": QG_CODEC_TERNARY_1_58_Q2}
 BLOCK = {QG_CODEC_Q4_0: 32, QG_CODEC_MLX4_G64: 64, QG_CODEC_Q2_0: 128, QG_CODEC_Q8_0: 32, QG_CODEC_MLX4_G32: 32,
-         QG_CODEC_Q4_K: 256, QG_CODEC_TERNARY_1_58: 256}
+         QG_CODEC_Q4_K: 256, QG_CODEC_TERNARY_1_58: 256, QG_CODEC_TERNARY_1_58_Q2: 256}
 
 QG_OK = 0
 STATUS = {0: "QG_OK", -1: "QG_ERR_NULL", -2: "QG_ERR_CODEC", -3: "QG_ERR_SHAPE", -4: "QG_ERR_ALIGN",

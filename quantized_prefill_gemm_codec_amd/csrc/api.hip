@@ -12,7 +12,8 @@ constexpr int64_t LIMIT = int64_t(1) << 31;   // bytes per buffer, and M/N/K
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool valid_codec(int32_t c)
 {
-    return c == Q4_0 || c == MLX4_G64 || c == Q2_0 || c == Q8_0 || c == MLX4_G32 || c == Q4_K || c == TERNARY;
+    return c == Q4_0 || c == MLX4_G64 || c == Q2_0 || c == Q8_0 || c == MLX4_G32 || c == Q4_K || c == TERNARY ||
+           c == TERNARY_Q2;
 }
 
 qg_status check_weight(const qg_weight *w)
@@ -60,7 +61,7 @@ GemmProblem problem(const qg_weight *w, const void *x, int64_t m, int64_t ldx, v
 {
     const Geometry g = geometry(w->codec, w->n, w->k);
     GemmProblem p;
-    p.codec = w->codec;
+    p.codec = kernel_codec(w->codec);
     p.w0 = planes_of(w);
     p.w1 = p.w0;
     p.x = static_cast<const _Float16 *>(x);
@@ -186,8 +187,9 @@ qg_status qg_kernel_for(int32_t entry, int32_t codec, int64_t m, int64_t n, int6
         k % block_size(codec) != 0 || (entry == E_GEMV && m > 64))
         return QG_ERR_SHAPE;
     const int glu = entry == E_SWIGLU ? 1 : entry == E_GEGLU ? 2 : 0;
-    const Choice c = choose_kernel(codec, glu, glu == 0, m, n, k);
-    const int len = kernel_name(c, codec, name, cap);
+    const int kc = kernel_codec(codec);
+    const Choice c = choose_kernel(kc, glu, glu == 0, m, n, k);
+    const int len = kernel_name(c, kc, name, cap);
     return (len > 0 && size_t(len) < cap) ? QG_OK : QG_ERR_SIZE;
 }
 

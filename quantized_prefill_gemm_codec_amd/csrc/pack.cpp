@@ -13,7 +13,8 @@ namespace {
 
 bool valid_codec(int32_t c)
 {
-    return c == Q4_0 || c == MLX4_G64 || c == Q2_0 || c == Q8_0 || c == MLX4_G32 || c == Q4_K || c == TERNARY;
+    return c == Q4_0 || c == MLX4_G64 || c == Q2_0 || c == Q8_0 || c == MLX4_G32 || c == Q4_K || c == TERNARY ||
+           c == TERNARY_Q2;
 }
 
 qg_status check_shape(int32_t codec, int64_t n, int64_t k)
@@ -37,7 +38,7 @@ size_t canonical_size(int32_t codec, int64_t n, int64_t k)
         return size_t(n) * size_t(k / 32) * 34;
     if (codec == Q4_K)
         return size_t(n) * size_t(k / 256) * 144;
-    if (codec == TERNARY)
+    if (codec == TERNARY || codec == TERNARY_Q2)
         return size_t(n) * size_t(k / 256) * 54;
     const int64_t group = codec == MLX4_G32 ? 32 : 64;
     return size_t(n) * size_t(k / 2) + 2 * size_t(n) * size_t(k / group) * 2;
@@ -69,8 +70,9 @@ inline int canonical_code(int32_t codec, const uint8_t *c, int64_t row, int64_t 
         const uint8_t b = blk[16 + 32 * (w / 64) + l % 32];
         return l < 32 ? (b & 0xF) : (b >> 4);
     }
-    if (codec == TERNARY) {
-        // base-3 digit kk % 5 of byte 2 + (kk % 256) / 5 (digits 0..2)
+    if (codec == TERNARY || codec == TERNARY_Q2) {
+        // base-3 digit kk % 5 of byte 2 + (kk % 256) / 5 (digits 0..2); as a
+        // 2-bit code (TERNARY_Q2) the digit t is q with w = (q - 1) d
         static const int pw[5] = {1, 3, 9, 27, 81};
         const uint8_t *blk = c + (row * (k / 256) + kk / 256) * 54;
         const int w = int(kk % 256);
@@ -213,7 +215,7 @@ qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonica
         return QG_ERR_NULL;
     if (canonical_bytes < canonical_size(codec, n, k))
         return QG_ERR_SIZE;
-    if (codec == TERNARY && !ternary_codes_valid(static_cast<const uint8_t *>(canonical), n, k))
+    if ((codec == TERNARY || codec == TERNARY_Q2) && !ternary_codes_valid(static_cast<const uint8_t *>(canonical), n, k))
         return QG_ERR_CODE;
 
     const uint8_t *c = static_cast<const uint8_t *>(canonical);
@@ -224,7 +226,7 @@ qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonica
     const bool four_bit = codec == Q4_0 || is_mlx(codec) || codec == Q4_K;
     // zero-weight code for padding: Q4_0 q = 8, Q2_0 q = 1, Q8_0 q = 0 (stored
     // 128), MLX and Q4_K q = 0 (zero scale records)
-    const int pad_code = codec == Q4_0 ? 8 : codec == Q2_0 ? 1 : codec == Q8_0 ? 128 : 0;
+    const int pad_code = codec == Q4_0 ? 8 : (codec == Q2_0 || codec == TERNARY_Q2) ? 1 : codec == Q8_0 ? 128 : 0;
 
     memset(q, 0, size_t(g.qs_bytes));
     memset(s, 0, size_t(g.scale_bytes));
@@ -311,6 +313,11 @@ qg_status qg_pack_host(int32_t codec, int64_t n, int64_t k, const void *canonica
             const int64_t nb = k / 128;
             for (int64_t blk = 0; blk < nb; ++blk)
                 wr16(s + ((r * nb + blk) * 32 + i) * 2, rd16(c + (row * nb + blk) * 34));
+        } else if (codec == TERNARY_Q2) {
+            // the Q2_0 plane: one entry per 128 weights, each 256-weight block's d twice
+            const int64_t nb = k / 128;
+            for (int64_t blk = 0; blk < nb; ++blk)
+                wr16(s + ((r * nb + blk) * 32 + i) * 2, rd16(c + (row * (k / 256) + blk / 2) * 54));
         } else {
             const int64_t group = codec == MLX4_G32 ? 32 : 64;
             const int64_t ng = k / group;

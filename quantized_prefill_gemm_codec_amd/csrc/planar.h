@@ -72,7 +72,13 @@
 
 namespace qg {
 
-enum Codec : int32_t { Q4_0 = 1, MLX4_G64 = 2, Q2_0 = 3, Q8_0 = 4, MLX4_G32 = 5, Q4_K = 6, TERNARY = 7 };
+enum Codec : int32_t { Q4_0 = 1, MLX4_G64 = 2, Q2_0 = 3, Q8_0 = 4, MLX4_G32 = 5, Q4_K = 6, TERNARY = 7, TERNARY_Q2 = 8 };
+
+// The kernels a codec's planar format runs on.  TERNARY_Q2 is the ternary
+// canonical format repacked as 2-bit codes q = t (the digit, 0..2) with the
+// 256-weight block's scale repeated for both 128-weight halves: exactly the
+// Q2_0 planar format, w = (q - 1) d.
+QG_HD inline int kernel_codec(int codec) { return codec == TERNARY_Q2 ? int(Q2_0) : codec; }
 
 constexpr int TERNARY_CHUNK = 416;   // bytes of ternary digits per (row group, k-step)
 
@@ -83,11 +89,11 @@ QG_HD inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 QG_HD inline int block_size(int codec)
 {
     return codec == Q4_0 ? 32 : codec == MLX4_G64 ? 64 : codec == Q2_0 ? 128 : codec == Q8_0 ? 32 : codec == MLX4_G32 ? 32
-         : codec == Q4_K ? 256 : codec == TERNARY ? 256 : 0;
+         : codec == Q4_K ? 256 : codec == TERNARY ? 256 : codec == TERNARY_Q2 ? 256 : 0;
 }
 
 // bytes of codes a lane holds per chunk
-QG_HD inline int lane_code_bytes(int codec) { return codec == Q2_0 ? 8 : codec == Q8_0 ? 32 : 16; }
+QG_HD inline int lane_code_bytes(int codec) { return codec == Q2_0 || codec == TERNARY_Q2 ? 8 : codec == Q8_0 ? 32 : 16; }
 
 struct Geometry {
     int64_t groups;   // row groups (N padded to 32) / 32

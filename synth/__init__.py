@@ -68,12 +68,14 @@ CODEC_Q8_0 = 4
 CODEC_MLX4_G32 = 5
 CODEC_Q4_K = 6
 CODEC_TERNARY = 7
+CODEC_TERNARY_Q2 = 8     # the ternary canonical format, held on the device as 2-bit codes
 
 CODEC_NAMES = {CODEC_Q4_0: "q4_0", CODEC_MLX4_G64: "mlx4_g64", CODEC_Q2_0: "q2_0", CODEC_Q8_0: "q8_0",
                CODEC_MLX4_G32: "mlx4_g32", CODEC_Q4_K: "q4_k",
-               CODEC_TERNARY: "ternary"}
+               CODEC_TERNARY: "ternary", CODEC_TERNARY_Q2: "ternary_q2"}
 # weights per block (scale group) along K
-BLOCK = {CODEC_Q4_0: 32, CODEC_MLX4_G64: 64, CODEC_Q2_0: 128, CODEC_Q8_0: 32, CODEC_MLX4_G32: 32, CODEC_Q4_K: 256, CODEC_TERNARY: 256}
+BLOCK = {CODEC_Q4_0: 32, CODEC_MLX4_G64: 64, CODEC_Q2_0: 128, CODEC_Q8_0: 32, CODEC_MLX4_G32: 32, CODEC_Q4_K: 256,
+         CODEC_TERNARY: 256, CODEC_TERNARY_Q2: 256}
 
 BASE_SEED = 0x51C0DEC0
 
@@ -102,7 +104,7 @@ def canonical_bytes(codec: int, n: int, k: int) -> int:
         return n * (k // 32) * 34
     if codec == CODEC_Q4_K:
         return n * (k // 256) * 144
-    if codec == CODEC_TERNARY:
+    if codec in (CODEC_TERNARY, CODEC_TERNARY_Q2):
         return n * (k // 256) * 54
     raise ValueError(codec)
 
@@ -270,7 +272,8 @@ def gen_q4_k(n: int, k: int, seed: int, tensor_id: int = T_W,
 
 
 GEN = {CODEC_Q4_0: gen_q4_0, CODEC_MLX4_G64: gen_mlx4, CODEC_Q2_0: gen_q2_0, CODEC_Q8_0: gen_q8_0,
-       CODEC_MLX4_G32: gen_mlx4_g32, CODEC_Q4_K: gen_q4_k, CODEC_TERNARY: gen_ternary}
+       CODEC_MLX4_G32: gen_mlx4_g32, CODEC_Q4_K: gen_q4_k, CODEC_TERNARY: gen_ternary,
+       CODEC_TERNARY_Q2: gen_ternary}
 
 
 def gen_weight(codec: int, n: int, k: int, seed: int, tensor_id: int = T_W) -> np.ndarray:
@@ -336,6 +339,11 @@ WORKLOADS = {
                                                8192, BASE_SEED + 12),
     "ternary_gemv_1x4096x14336": Workload("ternary_gemv_1x4096x14336", "gemv", CODEC_TERNARY, 1, 4096, 14336,
                                           BASE_SEED + 13),
+    # the same ternary inputs held on the device as 2-bit codes (the Q2_0 planar format)
+    "ternary_q2_prefill_2048x2048x8192": Workload("ternary_q2_prefill_2048x2048x8192", "prefill", CODEC_TERNARY_Q2, 2048,
+                                                  2048, 8192, BASE_SEED + 12),
+    "ternary_q2_gemv_1x4096x14336": Workload("ternary_q2_gemv_1x4096x14336", "gemv", CODEC_TERNARY_Q2, 1, 4096, 14336,
+                                             BASE_SEED + 13),
 }
 
 

@@ -36,7 +36,7 @@ def reachable():
     ns = [1, 200, 8192, 14336, 65536]
     ks = [256, 2048, 4096, 1 << 14, 1 << 18]
     names = set()
-    for codec, entry, m, n, k in itertools.product(range(1, 8), ENTRIES, ms, ns, ks):
+    for codec, entry, m, n, k in itertools.product(range(1, 9), ENTRIES, ms, ns, ks):
         nm = _name(entry, codec, m, n, k)
         if nm:
             names.add(nm)
@@ -51,7 +51,7 @@ def covered():
     cases += [("swiglu", c, m, n, k) for c, m, n, k in par.SWIGLU_SHAPES]
     cases += [("geglu", c, m, n, k) for c, m, n, k in par.GEGLU_SHAPES]
     cases += [("gemv", c, m, n, k) for c, m, n, k in par.GEMV_SHAPES]
-    cases += [("prefill", c, 1921, 7681, 256) for c in range(1, 8)]          # test_prefill_wide_tile_ragged
+    cases += [("prefill", c, 1921, 7681, 256) for c in range(1, 9)]          # test_prefill_wide_tile_ragged
     for wl in synth.WORKLOADS.values():                                       # test_full_workload_sampled
         cases.append((wl.op, wl.codec, wl.m, wl.n, wl.k))
     cases += [("prefill", c, m, n, k) for c, m, n, k in limits.DEGENERATE]
@@ -71,7 +71,7 @@ def test_reachable_set_size():
     and 4 rows -- ten; Q8_0's gated small-M calls run the register-staged
     64 x 64 and 128 x 128 kernels instead of the split-k tile -- twelve.  A
     change to the dispatch that adds or drops an instantiation shows up here
-    first."""
+    first.  (Codec 8, the 2-bit ternary layout, runs the Q2_0 kernels.)"""
     names = reachable()
     assert len(names) == 6 * 10 + 12, sorted(names)
 

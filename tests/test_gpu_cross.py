@@ -26,7 +26,7 @@ import quantized_prefill_gemm_codec_amd as qg
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-2
-CODECS = [1, 2, 3, 4, 5, 6, 7]
+CODECS = [1, 2, 3, 4, 5, 6, 7, 8]
 ENTRIES = ["prefill", "heads", "swiglu", "geglu", "gemv"]
 MS = [1, 2, 3, 4, 33, 64, 127, 128, 129, 512]
 N, K, HEAD_DIM = 200, 512, 40

@@ -69,7 +69,7 @@ def _same_value_bits(a16, b16):
 DEQ_SHAPES = [(1, 256, 256), (1, 40, 96), (1, 1000, 544), (2, 33, 192), (2, 300, 1024),
               (3, 37, 256), (3, 520, 1152), (4, 256, 256), (4, 40, 96), (4, 300, 544),
               (5, 256, 256), (5, 33, 96), (5, 300, 544), (6, 256, 256), (6, 40, 512), (6, 300, 768),
-              (7, 256, 256), (7, 40, 512), (7, 300, 768)]
+              (7, 256, 256), (7, 40, 512), (7, 300, 768), (8, 256, 256), (8, 40, 512), (8, 300, 768)]
 
 
 @pytest.mark.parametrize("codec,n,k", DEQ_SHAPES)
@@ -136,7 +136,7 @@ def test_q4_k_single_rounding_through_kernels(torch):
         assert _same_value_bits(y, want.T[:m])
 
 
-@pytest.mark.parametrize("codec", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("codec", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_identity_probe_through_gemm(torch, codec):
     """X = I: every output is one product with 1.0, so Y = W^T exactly."""
     n = k = 256
@@ -365,7 +365,7 @@ def _sample(rng, size, count):
     return np.sort(np.concatenate([[0, size - 1], s]))
 
 
-@pytest.mark.parametrize("codec", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("codec", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_prefill_wide_tile_ragged(torch, codec):
     """M = 1921, N = 7681 is 16 x 16 tiles of 128 x 512 (the tile the prefill
     takes when those fill the chip), with a one-row m tail and a one-column n

@@ -41,14 +41,15 @@ def test_library_exports_every_declared_symbol():
 
 @pytest.mark.parametrize("codec,n,k", [(1, 8192, 2048), (1, 40, 96), (2, 14336, 4096), (3, 4096, 4096), (3, 33, 128),
                                      (4, 8192, 2048), (4, 40, 96), (5, 14336, 4096), (5, 33, 96),
-                                     (6, 8192, 2048), (6, 40, 256), (7, 8192, 2048), (7, 40, 512)])
+                                     (6, 8192, 2048), (6, 40, 256), (7, 8192, 2048), (7, 40, 512),
+                                     (8, 8192, 2048), (8, 40, 512)])
 def test_sizes(codec, n, k):
     qs, sc = qg.qg_packed_sizes(codec, n, k)
     groups, ksteps = -(-n // 32), -(-k // 64)
     if codec == 7:
         assert qs == groups * ksteps * 416                    # 1.625 bits per weight of digits
     else:
-        code_bytes = {1: 16, 2: 16, 3: 8, 4: 32, 5: 16, 6: 16}[codec]
+        code_bytes = {1: 16, 2: 16, 3: 8, 4: 32, 5: 16, 6: 16, 8: 8}[codec]
         assert qs == groups * ksteps * 64 * code_bytes
     if codec in (1, 4):
         assert sc == groups * ksteps * 64 * 2
@@ -102,7 +103,7 @@ def _read_planar(codec, n, k, qs, sc):
     if codec == 7:
         return _read_ternary_planar(n, k, qs, sc)
     groups, ksteps = -(-n // 32), -(-k // 64)
-    cb = {1: 16, 2: 16, 3: 8, 4: 32, 5: 16, 6: 16}[codec]
+    cb = {1: 16, 2: 16, 3: 8, 4: 32, 5: 16, 6: 16, 8: 8}[codec]
     if codec == 4:
         halves = qs.reshape(groups, ksteps, 2, 64, 16)
     else:
@@ -115,7 +116,7 @@ def _read_planar(codec, n, k, qs, sc):
             e4 = (j % 8) % 4
             bit = 8 * (e4 // 2) + 16 * (e4 % 2)
             q = halves[:, :, word // 4, :, (word % 4) * 4 + bit // 8].astype(np.int64) - 128
-        elif codec == 3:
+        elif codec in (3, 8):
             dw, e = divmod(j, 16)
             bit = 2 * (e // 2) + 16 * (e % 2)
             byte = lanes[..., 4 * dw + bit // 8].astype(np.int64)
@@ -164,7 +165,7 @@ def _read_planar(codec, n, k, qs, sc):
         return codes, s.astype(np.float64), b.astype(np.float64)
     d = sc.view(np.float16).reshape(groups, k // 128, 32)
     scale = d[rr[:, None] // 32, kk[None, :] // 128, rr[:, None] % 32]
-    return codes, scale.astype(np.float64), None
+    return codes, scale.astype(np.float64), None     # Q2_0 and the 2-bit ternary layout: w = (q - 1) d
 
 
 def _value(codec, codes, scale, bias):
@@ -179,7 +180,8 @@ def _value(codec, codes, scale, bias):
 
 @pytest.mark.parametrize("codec,n,k", [(1, 40, 96), (1, 64, 64), (2, 33, 192), (3, 37, 256), (3, 32, 128),
                                      (4, 40, 96), (4, 64, 128), (5, 33, 96), (5, 64, 256), (6, 40, 512),
-                                     (6, 64, 256), (7, 40, 512), (7, 64, 256), (7, 33, 768)])
+                                     (6, 64, 256), (7, 40, 512), (7, 64, 256), (7, 33, 768), (8, 40, 512),
+                                     (8, 64, 256), (8, 33, 768)])
 def test_pack_roundtrip_random(codec, n, k):
     canon = synth.gen_weight(codec, n, k, 77)
     qs, sc = qg.qg_pack_host(codec, n, k, canon)
@@ -206,6 +208,21 @@ def test_pack_padding_decodes_to_zero():
     d = sc.view(np.float16).reshape(2, 2, 2, 32)
     assert np.all(d[1, :, :, 8:] == 0)          # rows 40..63
     assert np.all(d[:, 1, 1, :] == 0)           # k 96..127 (block 3)
+
+
+def test_ternary_q2_layout_is_the_q2_0_layout():
+    """The 2-bit ternary layout is the Q2_0 planar format of codes q = t: a
+    Q2_0 matrix built from the same digits and scales packs to the same bytes
+    (each 256-weight block's d written for both of its 128-weight halves)."""
+    n, k = 45, 512
+    rng = np.random.default_rng(8)
+    t = rng.integers(0, 3, (n, k))
+    d = synth.fp16_uniform(rng, 0.01, 0.03, (n, k // 256))
+    q8 = qg.qg_pack_host(8, n, k, synth.encode_ternary((t - 1).astype(np.int8), d))
+    q3 = qg.qg_pack_host(3, n, k, synth.encode_q2_0(t.astype(np.uint8), np.repeat(d, 2, axis=1)))
+    assert np.array_equal(q8[0], q3[0]) and np.array_equal(q8[1], q3[1])
+    assert qg.qg_kernel_for("prefill", 8, 2048, 8192, 2048) == qg.qg_kernel_for("prefill", 3, 2048, 8192, 2048)
+    assert qg.qg_kernel_for("gemv", 8, 1, 14336, 4096) == "gemv_kernel<3, 1>"
 
 
 def test_pack_rejects_invalid_ternary_bytes():

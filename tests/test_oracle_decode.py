@@ -286,3 +286,11 @@ def test_generator_is_deterministic():
     c = synth.gen_q4_0(8, 64, 124)
     assert np.array_equal(a, b) and not np.array_equal(a, c)
     assert np.array_equal(synth.gen_x(4, 64, 1), synth.gen_x(4, 64, 1))
+
+
+def test_ternary_q2_reads_the_ternary_canonical_format():
+    """Codec 8 is a device layout of the ternary codec: the oracle decodes its
+    canonical bytes exactly as codec 7's (pinned above by the fixtures)."""
+    canon = synth.gen_weight(7, 33, 768, 91)
+    assert np.array_equal(oracle.decode(8, canon, 33, 768), oracle.decode(7, canon, 33, 768))
+    assert oracle.block_geometry(8) == oracle.block_geometry(7)
