@@ -35,6 +35,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -65,10 +66,16 @@ ATTN_SOURCES = ["attention.hip", "api.hip", "launch.h", "unpack.h"]
 
 
 def kernel_source_hash(files=KERNEL_SOURCES) -> str:
+    """Hash of the kernel sources' code: comments and blank lines are left out,
+    so a counter summary stays valid across edits of comments only."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "quantized_prefill_gemm_codec_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "quantized_prefill_gemm_codec_amd", "csrc", f)) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in text.splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -24,8 +24,9 @@
 //    next product: no lane exchange between the two products;
 //  * online softmax in fp32 on the log2 scale: the row maximum and sum are
 //    lane-local over 32 scores plus one exchange with lane l ^ 32 (the other
-//    half of the same query's keys); the O accumulators are rescaled by
-//    2^(m_old - m_new) when the maximum moves;
+//    half of the same query's keys); the running maximum, and with it the
+//    O accumulators (by 2^(m_old - m_new)), moves only when a tile's maximum
+//    exceeds it by more than RESCALE_SLACK;
 //  * O^T += V^T P^T (A = V^T rows from LDS, B = P as fp16).
 // At the end the second group hands its (maximum, sum, O^T) to the first
 // through LDS, which merges the two halves (each rescaled to the common
