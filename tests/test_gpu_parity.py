@@ -131,7 +131,7 @@ def test_q4_k_single_rounding_through_kernels(torch):
     w = _weight(torch, 6, n, k, canon)
     assert _same_value_bits(qg.qg_dequant(w).cpu().numpy(), want)
     eye = torch.eye(k, dtype=torch.float16, device="cuda")
-    for m in (256, 128):      # large-tile DMA kernel, register-staged kernel
+    for m in (256, 128):      # the 128-row prefill tile, the split-k 64 x 64 tile
         y = qg.qgemm_prefill(w, eye[:m].contiguous()).cpu().numpy()
         assert _same_value_bits(y, want.T[:m])
 
