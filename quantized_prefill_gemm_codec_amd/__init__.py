@@ -221,11 +221,25 @@ def _out(m: int, n: int, device, out=None):
     return buf, ldy, buf[:, :n]
 
 
+def _no_rows(lead, n: int, device, out):
+    """The result of a call with no rows of X (the C-ABI takes M >= 1): an
+    empty [..., N] tensor, or the caller's `out` once it is checked."""
+    torch = _torch()
+    if out is None:
+        return torch.empty((*lead, n), dtype=torch.float16, device=device)
+    _check_out_device(out, device)
+    if out.numel() != 0 or out.dim() < 1 or out.shape[-1] != n:
+        raise ValueError("out must be float16 [..., N] with no rows")
+    return out
+
+
 def qgemm_prefill(w: QWeight, x, out=None, stream=None):
     """Y = X W^T for fp16 X [..., K]; returns fp16 [..., N]."""
     x2, lead, ldx = _as_rows(x, w.k)
     _check_weights(x.device, w)
     m = x2.shape[0]
+    if m == 0:
+        return _no_rows(lead, w.n, x.device, out)
     ybuf, ldy, y = _out(m, w.n, x.device, out)
     _check(lib().qgemm_prefill(w.desc, x2.data_ptr(), m, ldx, ybuf.data_ptr(), ldy, _stream(stream)),
            "qgemm_prefill")
@@ -237,6 +251,8 @@ def qgemm_swiglu(wg: QWeight, wu: QWeight, x, out=None, stream=None):
     x2, lead, ldx = _as_rows(x, wg.k)
     _check_weights(x.device, wg, wu)
     m = x2.shape[0]
+    if m == 0:
+        return _no_rows(lead, wg.n, x.device, out)
     ybuf, ldy, y = _out(m, wg.n, x.device, out)
     _check(lib().qgemm_swiglu(wg.desc, wu.desc, x2.data_ptr(), m, ldx, ybuf.data_ptr(), ldy, _stream(stream)),
            "qgemm_swiglu")
@@ -251,6 +267,15 @@ def qgemm_prefill_heads(w: QWeight, x, head_dim: int, out=None, stream=None):
     x2, _, ldx = _as_rows(x, w.k)
     _check_weights(x.device, w)
     m = x2.shape[0]
+    if m == 0:
+        if head_dim < 8 or head_dim % 8 or w.n % head_dim:
+            raise ValueError("head_dim must be a multiple of 8 that divides N")
+        if out is None:
+            return torch.empty((w.n // head_dim, 0, head_dim), dtype=torch.float16, device=x.device)
+        _check_out_device(out, x.device)
+        if out.numel() != 0:
+            raise ValueError("out must be empty when X has no rows")
+        return out
     if out is None:
         out = torch.empty((w.n // head_dim if head_dim else 0, m, head_dim), dtype=torch.float16, device=x.device)
     _check_out_device(out, x.device)
@@ -266,6 +291,8 @@ def qgemm_geglu(wg: QWeight, wu: QWeight, x, out=None, stream=None):
     x2, lead, ldx = _as_rows(x, wg.k)
     _check_weights(x.device, wg, wu)
     m = x2.shape[0]
+    if m == 0:
+        return _no_rows(lead, wg.n, x.device, out)
     ybuf, ldy, y = _out(m, wg.n, x.device, out)
     _check(lib().qgemm_geglu(wg.desc, wu.desc, x2.data_ptr(), m, ldx, ybuf.data_ptr(), ldy, _stream(stream)),
            "qgemm_geglu")
@@ -277,6 +304,8 @@ def qgemv_decode(w: QWeight, x, out=None, stream=None):
     x2, lead, ldx = _as_rows(x, w.k)
     _check_weights(x.device, w)
     m = x2.shape[0]
+    if m == 0:
+        return _no_rows(lead, w.n, x.device, out)
     ybuf, ldy, y = _out(m, w.n, x.device, out)
     _check(lib().qgemv_decode(w.desc, x2.data_ptr(), m, ldx, ybuf.data_ptr(), ldy, _stream(stream)),
            "qgemv_decode")
@@ -352,6 +381,11 @@ def qattn_prefill_q8kv(q, cache: Q8KVCache, causal: bool = True, scale: float | 
     heads, m, d = q.shape
     if out is None:
         out = torch.empty_like(q)
+    if m == 0:                 # no queries: nothing to launch (the C-ABI takes M >= 1)
+        _check_out_device(out, q.device)
+        if out.shape != q.shape:
+            raise ValueError("out must be shaped like q")
+        return out
     _check_out_device(out, q.device)
     if out.shape != q.shape or not out.is_contiguous():
         raise ValueError("out must be a contiguous float16 tensor shaped like q")

@@ -508,3 +508,26 @@ def test_non_finite_inputs_trip_exactly_their_rows_and_columns(torch, entry, cod
         else:
             ref = oracle.gemm_ref(codec, mats[0], n, k, x[rows], rows_n=cols)
             assert _err(y[np.ix_(rows, cols)], ref) <= TOL
+
+
+def test_empty_batch_returns_empty_output_without_launch(torch):
+    """X with no rows (an empty batch, with or without leading dims) gives an
+    empty [..., N] result from every entry point; the C-ABI itself takes
+    M >= 1 (QG_ERR_SHAPE for M = 0, checked on the host in test_lib_host)."""
+    n, k = 64, 256
+    w = _weight(torch, 1, n, k, synth.gen_weight(1, n, k, 31))
+    wu = _weight(torch, 1, n, k, synth.gen_weight(1, n, k, 32))
+    for shape in ((0, k), (3, 0, k)):
+        x = torch.empty(shape, dtype=torch.float16, device="cuda")
+        for y in (qg.qgemm_prefill(w, x), qg.qgemv_decode(w, x), qg.qgemm_swiglu(w, wu, x), qg.qgemm_geglu(w, wu, x)):
+            assert tuple(y.shape) == shape[:-1] + (n,) and y.dtype == torch.float16 and y.is_cuda
+    y = qg.qgemm_prefill_heads(w, torch.empty((0, k), dtype=torch.float16, device="cuda"), 32)
+    assert tuple(y.shape) == (2, 0, 32)
+    with pytest.raises(ValueError):
+        qg.qgemm_prefill_heads(w, torch.empty((0, k), dtype=torch.float16, device="cuda"), 12)
+    out = torch.empty((0, n), dtype=torch.float16, device="cuda")
+    assert qg.qgemm_prefill(w, torch.empty((0, k), dtype=torch.float16, device="cuda"), out=out) is out
+    kc, vc = synth.AttnWorkload("empty", 2, 1, 1, 64, 64, True, 5).kv()
+    kv = qg.Q8KVCache.from_canonical(1, 64, 64, kc, vc)
+    q = torch.empty((2, 0, 64), dtype=torch.float16, device="cuda")
+    assert tuple(qg.qattn_prefill_q8kv(q, kv).shape) == (2, 0, 64)
