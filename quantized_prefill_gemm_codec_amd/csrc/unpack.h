@@ -22,9 +22,11 @@
 //             v_pk_mul_lo_u16, one v_pk_lshrrev_b16 and one v_pk_mad_u16 per
 //             two digits, then the or / v_pk_add_f16 / v_pk_mul_f16 of the
 //             others)
-//   Q4_K      w = d * (q sc) - dmin m      (v_pk_fma_f16 for the exact
-//             integer q sc, then v_fma_mix{lo,hi}_f16: fp16 d times fp16 q sc
-//             plus the fp32 value -dmin m, rounded once to fp16; see mix_pair)
+//   Q4_K      w = d sc q - dmin m          (no insertion: the masked field is
+//             read as the fp16 subnormal q 2^-24 (bits 0..3) or q 2^-20 (bits
+//             4..7), and v_fma_mix{lo,hi}_f16 multiply it by the fp32 value
+//             d sc 2^24 or d sc 2^20, add the fp32 value -dmin m and round
+//             once to fp16; see mix_pair)
 // (Q2_0 values are exact; Q4_0, MLX and Q4_K round once.  fp16 subnormals are
 // kept: an MLX weight with q = 0 is its bias, which may be subnormal.)
 #pragma once
@@ -97,7 +99,7 @@ template <> struct LaneCodes<Q4_K> {
     u32x4 c;
     uint32_t scm;              // the lane's sub-block: sc | m << 8 (low 16 bits)
     uint32_t dd;               // the super-block: fp16 d (low half), fp16 dmin (high half)
-    uint32_t sc2, o10, o6;     // from prepare_lane: fp16 pairs (sc, sc), (-1024 sc, ..), (-64 sc, ..)
+    float k0, k1;              // from prepare_lane: d sc 2^24 and d sc 2^20, exact in fp32
     float nm;                  // from prepare_lane: -dmin * m, exact in fp32
 };
 
@@ -123,30 +125,30 @@ template <int CODEC> __device__ __forceinline__ void prepare_lane(LaneCodes<CODE
         lc.m3 = (__lane_id() & 1) ? (9u | (27u << 16)) : (1u | (3u << 16));   // digits 2, 3 or 0, 1
     }
     if constexpr (CODEC == Q4_K) {
-        const _Float16 sc = _Float16(float(lc.scm & 0xFFu));    // 0..63, exact
-        const f16x2 s2 = {sc, sc};
-        const f16x2 k10 = {_Float16(-1024.0f), _Float16(-1024.0f)};
-        const f16x2 k6 = {_Float16(-64.0f), _Float16(-64.0f)};
-        lc.sc2 = as_u32(s2);
-        lc.o10 = as_u32(s2 * k10);    // exact: 1024 * 63 = 64512 is a binary16
-        lc.o6 = as_u32(s2 * k6);
+        // d (11 significant bits) times sc (0..63) fits fp32's 24 exactly, and
+        // so does every power-of-two scaling of it within range (at most
+        // 65504 * 63 * 2^24 < 2^47)
+        const float dsc = float(as_f16x2(lc.dd)[0]) * float(lc.scm & 0xFFu);
+        lc.k0 = dsc * 16777216.0f;    // 2^24
+        lc.k1 = dsc * 1048576.0f;     // 2^20
         lc.nm = -(float(as_f16x2(lc.dd)[1]) * float((lc.scm >> 8) & 0xFFu));
     }
 }
 
-// fp16 pair (d * qs.lo + nm, d * qs.hi + nm) with d the low half of `d`.
-// Written as fp16 -> fp32 widening, an fp32 FMA and a narrowing to fp16, which
-// the compiler selects as v_fma_mixlo_f16 / v_fma_mixhi_f16; on gfx950 those
-// take the fp16 operands and the fp32 addend as they are and round only the
-// fp16 result, so each weight is the correctly rounded value of the exact
-// d * (q sc) - dmin * m.  (Plain C rather than inline assembly, so that the
-// compiler sees the instructions and keeps its wait states against matrix
-// instructions still reading the registers they overwrite.)
-__device__ __forceinline__ uint32_t mix_pair(uint32_t d, uint32_t qs, float nm)
+// fp16 pair (k * v.lo + nm, k * v.hi + nm) for the fp16 pair v.  Written as
+// fp16 -> fp32 widening, an fp32 FMA and a narrowing to fp16, which the
+// compiler selects as v_fma_mixlo_f16 / v_fma_mixhi_f16; on gfx950 those take
+// the fp16 operand (subnormals included) and the fp32 multiplier and addend as
+// they are and round only the fp16 result.  With v = q 2^-24 (or q 2^-20) and
+// k = d sc 2^24 (or 2^20) the product is d sc q exactly, so each weight is the
+// correctly rounded value of the exact d sc q - dmin m.  (Plain C rather than
+// inline assembly, so that the compiler sees the instructions and keeps its
+// wait states against matrix instructions still reading the registers they
+// overwrite.)
+__device__ __forceinline__ uint32_t mix_pair(float k, uint32_t v, float nm)
 {
-    const float df = float(as_f16x2(d)[0]);
-    const f16x2 q = as_f16x2(qs);
-    const f16x2 r = {_Float16(__builtin_fmaf(df, float(q[0]), nm)), _Float16(__builtin_fmaf(df, float(q[1]), nm))};
+    const f16x2 q = as_f16x2(v);
+    const f16x2 r = {_Float16(__builtin_fmaf(k, float(q[0]), nm)), _Float16(__builtin_fmaf(k, float(q[1]), nm))};
     return as_u32(r);
 }
 
@@ -204,16 +206,12 @@ __device__ __forceinline__ f16x8 unpack_substep(const LaneCodes<CODEC> &lc, int 
             q[u] = factor<CODEC, 10>(ternary_digits(r, mul, p != 15 && p % 5 == 0) | 0x64006400u);
         }
     } else if constexpr (CODEC == Q4_K) {
-        // (2^E + q) sc - 2^E sc = q sc exactly (at most 15 * 63 = 945), then
-        // one rounding: d (q sc) - dmin m
+        // a field left in place under a zero exponent reads as the fp16
+        // subnormal q 2^-24 (bits 0..3 of a half) or q 2^-20 (bits 4..7);
+        // one mix FMA per weight then scales, offsets and rounds once
         const uint32_t w = lc.c[s], w8 = w >> 8;
-        const f16x2 sc2 = as_f16x2(lc.sc2), o10 = as_f16x2(lc.o10), o6 = as_f16x2(lc.o6);
-        const f16x2 qs0 = __builtin_elementwise_fma(as_f16x2((w & 0x000F000Fu) | mg.m1024), sc2, o10);
-        const f16x2 qs1 = __builtin_elementwise_fma(as_f16x2((w & 0x00F000F0u) | mg.m64), sc2, o6);
-        const f16x2 qs2 = __builtin_elementwise_fma(as_f16x2((w8 & 0x000F000Fu) | mg.m1024), sc2, o10);
-        const f16x2 qs3 = __builtin_elementwise_fma(as_f16x2((w8 & 0x00F000F0u) | mg.m64), sc2, o6);
-        const u32x4 r = {mix_pair(lc.dd, as_u32(qs0), lc.nm), mix_pair(lc.dd, as_u32(qs1), lc.nm),
-                         mix_pair(lc.dd, as_u32(qs2), lc.nm), mix_pair(lc.dd, as_u32(qs3), lc.nm)};
+        const u32x4 r = {mix_pair(lc.k0, w & 0x000F000Fu, lc.nm), mix_pair(lc.k1, w & 0x00F000F0u, lc.nm),
+                         mix_pair(lc.k0, w8 & 0x000F000Fu, lc.nm), mix_pair(lc.k1, w8 & 0x00F000F0u, lc.nm)};
         return __builtin_bit_cast(f16x8, r);
     } else if constexpr (CODEC == Q8_0) {
         // sub-step s: dwords 2s (elements 0..3) and 2s + 1 (4..7), bytes at
