@@ -405,3 +405,16 @@ def test_built_kernels_use_no_scratch():
     lines = open(qbuild.RESOURCES).read().splitlines()
     assert len(lines) >= 80
     assert all(" scratch=0 spills=0 " in ln for ln in lines), [ln for ln in lines if " scratch=0 spills=0 " not in ln]
+
+
+def test_pack_is_reentrant_across_threads():
+    """The library keeps no state: the host repack called from many threads at
+    once gives every caller the planes a lone call gives."""
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = [(codec, 64 + 32 * (codec % 3), 256 * (1 + codec % 2)) for codec in range(1, 9)] * 3
+    canon = {j: synth.gen_weight(j[0], j[1], j[2], 500 + j[0]) for j in set(jobs)}
+    alone = {j: qg.qg_pack_host(*j, canon[j]) for j in set(jobs)}
+    with ThreadPoolExecutor(8) as ex:
+        results = list(ex.map(lambda j: (j, qg.qg_pack_host(*j, canon[j])), jobs))
+    for j, (qs, sc) in results:
+        assert np.array_equal(qs, alone[j][0]) and np.array_equal(sc, alone[j][1])
