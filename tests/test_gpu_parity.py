@@ -531,3 +531,31 @@ def test_empty_batch_returns_empty_output_without_launch(torch):
     kv = qg.Q8KVCache.from_canonical(1, 64, 64, kc, vc)
     q = torch.empty((2, 0, 64), dtype=torch.float16, device="cuda")
     assert tuple(qg.qattn_prefill_q8kv(q, kv).shape) == (2, 0, 64)
+
+
+@pytest.mark.parametrize("entry,m", [("prefill", 300), ("prefill", 40), ("gemv", 1), ("gemv", 3)])
+def test_output_overflow_saturates_to_signed_infinity(torch, entry, m):
+    """Y is fp16: an exact result beyond the largest binary16 (65504; with
+    round-to-nearest-even everything from 65520 up) comes out as an infinity
+    of its sign, every smaller one as a finite value within tolerance.  The
+    rows are built far from the threshold on both sides: Q4_0 weights with
+    d = 64 and codes 15 / 0 (w = +448 / -512) in alternate rows; X rows scaled
+    so that some rows of Y reach about +-9e4 and the rest stay near 7e2."""
+    n, k = 64, 256
+    codes = np.where((np.arange(n) % 2 == 0)[:, None], 15, 0) * np.ones((n, k), np.int64)
+    d = np.full((n, k // 32), 64.0, np.float16)
+    canon = synth.encode_q4_0(codes.astype(np.uint8), d)
+    w = _weight(torch, 1, n, k, canon)
+    rng = np.random.default_rng(77)
+    x = rng.uniform(0.5, 1.0, size=(m, k)).astype(np.float16)       # positive: the row sums do not cancel
+    big = (np.arange(m) % 3 == 0)
+    x[~big] *= np.float16(1.0 / 128.0)                               # |y| ~ 512 * 0.75 * 256 / 128 ~ 800
+    ref = oracle.gemm_ref(1, canon, n, k, x)
+    assert np.all(np.abs(ref[big]) > 1.2 * 65520) and np.all(np.abs(ref[~big]) < 65520 / 8)
+    xd = torch.from_numpy(x).cuda()
+    y = (qg.qgemm_prefill(w, xd) if entry == "prefill" else qg.qgemv_decode(w, xd)).cpu().numpy().astype(np.float64)
+    assert np.all(np.isinf(y[big])) and np.array_equal(np.sign(y[big]), np.sign(ref[big]))
+    small = ref[~big]
+    if small.size:
+        assert np.all(np.isfinite(y[~big]))
+        assert float(np.max(np.abs(y[~big] - small)) / np.sqrt(np.mean(small ** 2))) <= TOL
