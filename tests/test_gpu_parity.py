@@ -559,3 +559,36 @@ def test_output_overflow_saturates_to_signed_infinity(torch, entry, m):
     if small.size:
         assert np.all(np.isfinite(y[~big]))
         assert float(np.max(np.abs(y[~big] - small)) / np.sqrt(np.mean(small ** 2))) <= TOL
+
+
+def _big_q4_0(n, k, seed, tensor_id):
+    """Q4_0 weights with d ~U(8, 16): |w| up to 128, so products with
+    subnormal activations still sum to normal binary16 outputs (also through
+    the gated product)."""
+    rng = np.random.default_rng([seed, tensor_id])
+    codes = rng.integers(0, 16, size=(n, k)).astype(np.uint8)
+    return synth.encode_q4_0(codes, synth.fp16_uniform(rng, 8.0, 16.0, (n, k // 32)))
+
+
+@pytest.mark.parametrize("entry,codec,m", [("prefill", 1, 200), ("prefill", 2, 40), ("gemv", 1, 1), ("gemv", 6, 4),
+                                           ("swiglu", 1, 130)])
+def test_subnormal_activations_are_not_flushed(torch, entry, codec, m):
+    """X made entirely of binary16 subnormals (|x| < 2^-14): every product
+    counts, so a kernel that flushed subnormal inputs to zero would return
+    zeros against the oracle's nonzero result."""
+    n, k = 96, 512
+    gen = (lambda t: _big_q4_0(n, k, 880, t)) if codec == 1 else (lambda t: synth.gen_weight(codec, n, k, 880, t))
+    canon, canon_u = gen(synth.T_W), gen(synth.T_WU)
+    x = (synth.gen_x(m, k, 882).astype(np.float64) * 2.0 ** -18).astype(np.float16)
+    assert np.all(np.abs(x.astype(np.float64)) < 2.0 ** -14) and np.count_nonzero(x) > 0.9 * x.size
+    w, wu = _weight(torch, codec, n, k, canon), _weight(torch, codec, n, k, canon_u)
+    xd = torch.from_numpy(x).cuda()
+    if entry == "swiglu":
+        y = qg.qgemm_swiglu(w, wu, xd)
+        ref = oracle.swiglu(oracle.gemm_ref(codec, canon, n, k, x), oracle.gemm_ref(codec, canon_u, n, k, x))
+    else:
+        y = qg.qgemm_prefill(w, xd) if entry == "prefill" else qg.qgemv_decode(w, xd)
+        ref = oracle.gemm_ref(codec, canon, n, k, x)
+    y = y.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(y)) and np.count_nonzero(y) > 0.5 * y.size
+    assert float(np.max(np.abs(y - ref)) / np.sqrt(np.mean(ref ** 2))) <= TOL
