@@ -25,19 +25,27 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import Q8_0, decode, f16_to_f64
+from . import Q8_0, decode, dequant_f16_bits, f16_to_f64
 
 
 def q8kv_attention_ref(q16: np.ndarray, k_canon: np.ndarray, v_canon: np.ndarray, kv_heads: int, s_len: int,
-                       causal: bool, scale: float, rows=None) -> np.ndarray:
+                       causal: bool, scale: float, rows=None, kv_f16: bool = False) -> np.ndarray:
     """O [H, len(rows), D] in fp64 for fp16 queries q16 [H, M, D] and canonical
-    Q8_0 K, V caches of kv_heads * s_len rows of D elements each."""
+    Q8_0 K, V caches of kv_heads * s_len rows of D elements each.
+
+    kv_f16: use every K and V element rounded once to binary16 (the operand
+    precision at which the cache is dequantized for the matrix unit) instead
+    of its exact value; everything after that is the same fp64 definition."""
     heads, m, d = q16.shape
     if heads % kv_heads or d % 32 or s_len < m:
         raise ValueError("shape")
     rows = np.arange(m) if rows is None else np.asarray(rows, dtype=np.int64)
-    k = decode(Q8_0, k_canon, kv_heads * s_len, d).reshape(kv_heads, s_len, d)
-    v = decode(Q8_0, v_canon, kv_heads * s_len, d).reshape(kv_heads, s_len, d)
+    if kv_f16:
+        k = f16_to_f64(dequant_f16_bits(Q8_0, k_canon, kv_heads * s_len, d)).reshape(kv_heads, s_len, d)
+        v = f16_to_f64(dequant_f16_bits(Q8_0, v_canon, kv_heads * s_len, d)).reshape(kv_heads, s_len, d)
+    else:
+        k = decode(Q8_0, k_canon, kv_heads * s_len, d).reshape(kv_heads, s_len, d)
+        v = decode(Q8_0, v_canon, kv_heads * s_len, d).reshape(kv_heads, s_len, d)
     q = f16_to_f64(np.ascontiguousarray(q16).view(np.uint16))
     group = heads // kv_heads
     offset = s_len - m

@@ -83,3 +83,52 @@ def test_attention_full_workload_sampled(torch, name):
     rows = np.sort(np.concatenate([[0, wl.m - 1], rng.choice(np.arange(1, wl.m - 1), 30, replace=False)]))
     got, ref, _ = _run(torch, wl.heads, wl.kv_heads, wl.m, wl.s, wl.head_dim, wl.causal, wl.seed, rows=rows)
     assert _err(got, ref) <= TOL
+
+
+def _run_inputs(torch, q, kc, vc, kv_heads, s, d, causal, scale, kv_f16=False):
+    cache = qg.Q8KVCache.from_canonical(kv_heads, s, d, kc, vc)
+    out = qg.qattn_prefill_q8kv(torch.from_numpy(q).cuda(), cache, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    return got, q8kv_attention_ref(q, kc, vc, kv_heads, s, causal, np.float32(scale).item(), kv_f16=kv_f16)
+
+
+@pytest.mark.parametrize("d,order", [(128, "rising"), (64, "rising"), (128, "falling"), (64, "peaked")])
+def test_attention_running_maximum_paths(torch, d, order):
+    """Scores that rise along the keys move the rows' running maximum every few
+    64-key tiles (the accumulators are rescaled each time), and with an 8x
+    scale ("peaked", a nearly one-hot softmax) in every tile; falling scores
+    never move it after the first tile.  The reference reads the cache at the
+    kernel's operand precision (every K and V element rounded once to fp16):
+    with scores this large the rounding of K alone moves a nearly one-hot
+    softmax by more than 1e-2 of rms against the exact cache, while this test
+    is about the online softmax's arithmetic."""
+    heads, kv_heads, m, s = 4, 2, 96, 640
+    wl = synth.AttnWorkload("t", heads, kv_heads, m, s, d, True, 7300 + d)
+    q = np.abs(wl.q()).astype(np.float16)                 # positive queries
+    kc, vc = wl.kv()
+    blocks = d // 32
+    k8 = kc.reshape(kv_heads * s, blocks, 34).copy()
+    codes = np.abs(k8[:, :, 2:].view(np.int8).astype(np.int16))    # positive keys: score ~ (d-scale) * key position
+    pos = np.tile(np.arange(s), kv_heads)
+    ramp = (pos + 1) / s if order != "falling" else (s - pos) / s
+    k8[:, :, 2:] = np.clip(codes * ramp[:, None, None], 0, 127).astype(np.int8).view(np.uint8)
+    kc = k8.reshape(-1)
+    scale = (8.0 if order == "peaked" else 1.0) / np.sqrt(d)
+    got, ref = _run_inputs(torch, q, kc, vc, kv_heads, s, d, True, scale, kv_f16=True)
+    assert _err(got, ref) <= TOL
+
+
+def test_attention_code_minus_128(torch):
+    """K and V codes of -128 (byte 0x80, the one code outside +-127) decode as
+    -128 d through the kernel's stored q + 128, as the oracle reads them."""
+    heads, kv_heads, m, s, d = 2, 1, 80, 80, 128
+    wl = synth.AttnWorkload("t", heads, kv_heads, m, s, d, True, 7400)
+    q = wl.q()
+    kc, vc = wl.kv()
+    kb = kc.reshape(kv_heads * s, d // 32, 34).copy()
+    vb = vc.reshape(kv_heads * s, d // 32, 34).copy()
+    kb[::3, :, 2::5] = 0x80
+    vb[1::2, :, 3::4] = 0x80
+    got, ref = _run_inputs(torch, q, kb.reshape(-1), vb.reshape(-1), kv_heads, s, d, True, 1.0 / np.sqrt(d))
+    assert _err(got, ref) <= TOL

@@ -107,3 +107,28 @@ def test_row_subset_matches_full():
     rows = np.array([0, 3, 6])
     sub = q8kv_attention_ref(q, kc, vc, 1, s, causal=True, scale=0.125, rows=rows)
     assert np.array_equal(full[:, rows], sub)
+
+
+def test_fp16_kv_option_uses_the_rounded_cache():
+    """kv_f16 reads every K and V element as its correctly rounded binary16:
+    the single visible key returns exactly numpy's fp16 rounding of the exact
+    V row (which differs from the exact row somewhere for these scales), the
+    zero-query average is the mean of the rounded rows, and on random data the
+    result stays within fp16 rounding of the exact-cache result."""
+    d = 64
+    q = synth.gen_x(1, d, 11).reshape(1, 1, d)
+    kc, vc = _q8(1, d, 12), _q8(1, d, 13)
+    exact = _kv(vc, 1, d)[0]
+    out = q8kv_attention_ref(q, kc, vc, 1, 1, causal=True, scale=0.125, kv_f16=True)
+    assert np.array_equal(out[0, 0], exact.astype(np.float16).astype(np.float64))
+    assert not np.array_equal(out[0, 0], exact)
+    h, m, s = 1, 3, 7
+    kc, vc = _q8(s, d, 14), _q8(s, d, 15)
+    z = q8kv_attention_ref(np.zeros((h, m, d), np.float16), kc, vc, 1, s, causal=False, scale=0.3, kv_f16=True)
+    v16 = _kv(vc, s, d).astype(np.float16).astype(np.float64)
+    assert np.allclose(z[0, 0], v16.mean(axis=0), rtol=0, atol=1e-14)
+    q = synth.gen_x(2 * 40, d, 16).reshape(2, 40, d)
+    kc, vc = _q8(40, d, 17), _q8(40, d, 18)
+    a = q8kv_attention_ref(q, kc, vc, 1, 40, causal=True, scale=0.125)
+    b = q8kv_attention_ref(q, kc, vc, 1, 40, causal=True, scale=0.125, kv_f16=True)
+    assert 0 < np.max(np.abs(a - b)) <= 4 * 2.0 ** -11 * np.max(np.abs(a))
