@@ -13,21 +13,23 @@
 // range at the same time; in each group, wave w owns queries 32 w .. 32 w + 31
 // for its half.  Per tile of 64 keys and group:
 //  * the group's 256 threads turn the next tile's codes and fp16 block scales
-//    into fp16 K [64][D] (row-major) and V^T [D][64] in the other half of the
-//    group's double-buffered LDS area -- each element is the correctly rounded
-//    q * d, the weights' Q8_0 rule; V is transposed in registers (8 keys x 4 d
-//    per thread) so that it is stored with 16-byte writes.  The raw codes are
-//    loaded one tile ahead of that, so one barrier per tile suffices;
+//    into fp16 K [64][D] and V [64][D] (both row-major) in the other half of
+//    the group's double-buffered LDS area -- each element is the correctly
+//    rounded q * d, the weights' Q8_0 rule.  The raw codes are loaded one tile
+//    ahead of that, so one barrier per tile suffices;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_f16 (A = K rows, B = the wave's Q
 //    fragments, loaded once).  K rows are read in the order pi below, which
 //    makes each lane's 32 scores exactly the B fragments P^T needs for the
 //    next product: no lane exchange between the two products;
 //  * online softmax in fp32 on the log2 scale: the row maximum and sum are
 //    lane-local over 32 scores plus one exchange with lane l ^ 32 (the other
-//    half of the same query's keys); the running maximum, and with it the
+//    half of the same query's keys), the sum taken over P as rounded to fp16
+//    for the product, so that numerator and denominator use the same P; the
+//    running maximum, and with it the
 //    O accumulators (by 2^(m_old - m_new)), moves only when a tile's maximum
 //    exceeds it by more than RESCALE_SLACK;
-//  * O^T += V^T P^T (A = V^T rows from LDS, B = P as fp16).
+//  * O^T += V^T P^T (A = V^T, read out of the row-major V tile by the LDS
+//    transpose load, B = P as fp16).
 // At the end the second group hands its (maximum, sum, O^T) to the first
 // through LDS, which merges the two halves (each rescaled to the common
 // maximum), divides by the row sum and writes O [H, M, D] fp16.
@@ -80,15 +82,27 @@ __device__ __forceinline__ void dequant16(u32x4 c, _Float16 d, uint32_t e64, u32
     hi = u32x4{r[4], r[5], r[6], r[7]};
 }
 
-// Four codes (d .. d + 3 of one key, stored as q + 128) -> two fp16 pairs
-// (d, d + 1), (d + 2, d + 3) of q * scale, in the rounding of dequant16.
-__device__ __forceinline__ void dequant4(uint32_t c, _Float16 d, uint32_t e64, uint32_t &p01, uint32_t &p23)
+// One fp16 scale, zero-extended into a 32-bit register.  Scales of the
+// prefetched tile stay in registers of their own until the tile is staged:
+// combining two of them into one register as they arrive would make the wave
+// wait for the whole prefetch at once.
+__device__ __forceinline__ uint16_t load_u16(__amdgpu_buffer_rsrc_t r, uint32_t voff)
 {
-    const f16x2 dd = {d, d};
-    const f16x2 off = {_Float16(1152.0f), _Float16(1152.0f)};
-    const uint32_t x = c;
-    p01 = as_u32((as_f16x2(__builtin_amdgcn_perm(e64, x, 0x04010400u)) - off) * dd);
-    p23 = as_u32((as_f16x2(__builtin_amdgcn_perm(e64, x, 0x04030402u)) - off) * dd);
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0);
+}
+
+__device__ __forceinline__ _Float16 f16_of(uint16_t x) { return __builtin_bit_cast(_Float16, x); }
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// LDS transpose load (ds_read_b64_tr_b16): in each group of 16 lanes, lane
+// 4 a + c receives element c of the four halves addressed by lanes a, a + 4,
+// a + 8 and a + 12 of the group, in that order.
+__device__ __forceinline__ f16x4 lds_read_tr16(const _Float16 *p)
+{
+    return __builtin_bit_cast(
+        f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p)));
 }
 
 // Query tile and head of workgroup `lin` (0 .. tiles_q * heads - 1): causal
@@ -102,11 +116,6 @@ __device__ __forceinline__ void tile_of(int lin, int tiles_q, int heads, bool ca
     qt = causal ? tiles_q - 1 - r : r;
     h = lin - r * heads;
 }
-
-// V^T row d keeps its chunk c (keys 8 c .. 8 c + 7) at chunk position
-// c ^ vswz(d): the MFMA reads (16 rows, one chunk each) hit distinct banks and
-// the 16-byte stores of consecutive threads (rows 4 apart) at most two-way.
-__device__ __forceinline__ int vswz(int d) { return ((d >> 1) ^ (d >> 4)) & 7; }
 
 // A-operand row r (0..31) of a 32-key block reads key pi(r): the MFMA puts
 // row 8 q + 4 g + e of the product in register 4 q + e of lane half g, and
@@ -123,21 +132,18 @@ template <int D>
 __global__ __launch_bounds__(AT_NT, 1) void attn_q8kv_kernel(AttnArgs a)
 {
     constexpr int KP = D + 8;              // K tile row pitch (halves); the pad staggers LDS banks
-    constexpr int VP = AT_BK;              // V^T tile row pitch (halves): 8 chunks of 8 keys, swizzled
+    constexpr int VP = D + 16;             // V tile row pitch (halves): 4 rows of a transpose load hit distinct banks
     constexpr int NDB = D / 32;            // 32-row blocks of O^T
     constexpr int NDD = D / 16;            // 16-deep steps over d
     constexpr int CPR = D / 16;            // 16-code chunks per key (K)
     constexpr int IPT = AT_BK * CPR / AT_GT;   // K chunks per thread of a group
-    constexpr int VITEMS = AT_BK * D / 32;           // V items of 8 keys x 4 d per tile
-    constexpr int VIT = (VITEMS + AT_GT - 1) / AT_GT;   // per thread (D = 64: half the threads)
-    constexpr int VDG = D / 4;             // 4-wide d groups per key
     static_assert(D == 64 || D == 128, "head dimension");
-    static_assert(IPT >= 1 && AT_BK * CPR % AT_GT == 0 && VITEMS % 64 == 0, "tile");
-    constexpr int KT = AT_BK * KP, VT = D * VP;       // halves of one K tile and one V^T tile
+    static_assert(IPT >= 1 && AT_BK * CPR % AT_GT == 0, "tile");
+    constexpr int KT = AT_BK * KP, VT = AT_BK * VP;   // halves of one K tile and one V tile
     // the merge area (second group's O^T, maximum and sum) reuses the tiles
     static_assert(4 * (D / 32) * 4 * 64 * 16 + 2 * 4 * 64 * 4 <= AT_NG * 2 * (KT + VT) * 2, "merge area");
 
-    // per group: K tiles [2][KT], then V^T tiles [2][VT]
+    // per group: K tiles [2][KT], then V tiles [2][VT]
     __shared__ __attribute__((aligned(16))) _Float16 tiles[AT_NG][2 * (KT + VT)];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -180,48 +186,22 @@ __global__ __launch_bounds__(AT_NT, 1) void attn_q8kv_kernel(AttnArgs a)
     const __amdgpu_buffer_rsrc_t vqr = make_rsrc(a.vq + head_row * D, uint32_t(a.s) * D);
     const __amdgpu_buffer_rsrc_t ksr = make_rsrc(a.ks + head_row * (D / 32), uint32_t(a.s) * (D / 32) * 2u);
     const __amdgpu_buffer_rsrc_t vsr = make_rsrc(a.vs + head_row * (D / 32), uint32_t(a.s) * (D / 32) * 2u);
-    // K item j: key j / CPR, codes 16 (j % CPR) .. + 15.  V item j: keys
-    // 8 (j / VDG) .. + 7, codes 4 (j % VDG) .. + 3 of each.
-    u32x4 kc[IPT];
-    _Float16 kd[IPT];
-    uint32_t vc[VIT][8];
-    _Float16 vd[VIT][8];
+    // item j of either matrix: key j / CPR, codes 16 (j % CPR) .. + 15, and
+    // the scale of their 32-element block
+    u32x4 kc[IPT], vc[IPT];
+    uint16_t kd[IPT], vd[IPT];
     auto fetch = [&](int t) {
 #pragma unroll
         for (int u = 0; u < IPT; ++u) {
             const int j = gtid + AT_GT * u, kk = j / CPR, c = j % CPR;
             const uint32_t key = uint32_t(t * AT_BK + kk);
             const bool in = key < uint32_t(a.s);
-            kc[u] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(kqr, in ? key * D + uint32_t(16 * c) : OOB, 0, 0));
-            kd[u] = load_f16(ksr, in ? (key * (D / 32) + uint32_t(c >> 1)) * 2u : OOB, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < VIT; ++u) {
-            const int j = gtid + AT_GT * u, k8 = j / VDG, c4 = j % VDG;
-            if (j >= VITEMS)
-                break;
-            // keys 8 k8 .. + 7 are D (codes) and D / 16 (scale bytes) apart:
-            // inside the sequence one vector offset serves all eight (the key
-            // goes into the instruction offset); the tile that crosses s puts
-            // each key past it out of range by its vector offset
-            const uint32_t key0 = uint32_t(t * AT_BK + 8 * k8);
-            const uint32_t cv = key0 * D + uint32_t(4 * c4);
-            const uint32_t sv = (key0 * (D / 32) + uint32_t(c4 >> 3)) * 2u;
-            if (t * AT_BK + AT_BK <= a.s) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    vc[u][e] = __builtin_amdgcn_raw_buffer_load_b32(vqr, cv + uint32_t(e * D), 0, 0);
-                    vd[u][e] = load_f16(vsr, sv + uint32_t(e * (D / 16)), 0);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const bool in = key0 + uint32_t(e) < uint32_t(a.s);
-                    vc[u][e] = __builtin_amdgcn_raw_buffer_load_b32(vqr, in ? cv + uint32_t(e * D) : OOB, 0, 0);
-                    vd[u][e] = load_f16(vsr, in ? sv + uint32_t(e * (D / 16)) : OOB, 0);
-                }
-            }
+            const uint32_t co = in ? key * D + uint32_t(16 * c) : OOB;
+            const uint32_t so = in ? (key * (D / 32) + uint32_t(c >> 1)) * 2u : OOB;
+            kc[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kqr, co, 0, 0));
+            kd[u] = load_u16(ksr, so);
+            vc[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vqr, co, 0, 0));
+            vd[u] = load_u16(vsr, so);
         }
     };
     const uint32_t e64 = 0x64646464u;
@@ -231,42 +211,26 @@ __global__ __launch_bounds__(AT_NT, 1) void attn_q8kv_kernel(AttnArgs a)
         for (int u = 0; u < IPT; ++u) {
             const int j = gtid + AT_GT * u, kk = j / CPR, c = j % CPR;
             u32x4 lo, hi;
-            dequant16(kc[u], kd[u], e64, lo, hi);
+            dequant16(kc[u], f16_of(kd[u]), e64, lo, hi);
             *reinterpret_cast<u32x4 *>(&ksb[b * KT + kk * KP + 16 * c]) = lo;
             *reinterpret_cast<u32x4 *>(&ksb[b * KT + kk * KP + 16 * c + 8]) = hi;
-        }
-#pragma unroll
-        for (int u = 0; u < VIT; ++u) {
-            const int j = gtid + AT_GT * u, k8 = j / VDG, c4 = j % VDG;
-            if (j >= VITEMS)
-                break;
-            uint32_t p01[8], p23[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                dequant4(vc[u][e], vd[u][e], e64, p01[e], p23[e]);
-            // row d = 4 c4 + r of V^T gets keys 8 k8 .. + 7: the low (r even)
-            // or high (r odd) halves of keys e, e + 1 paired by v_perm_b32
-            u32x4 rows[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                rows[0][e] = __builtin_amdgcn_perm(p01[2 * e + 1], p01[2 * e], 0x05040100u);
-                rows[1][e] = __builtin_amdgcn_perm(p01[2 * e + 1], p01[2 * e], 0x07060302u);
-                rows[2][e] = __builtin_amdgcn_perm(p23[2 * e + 1], p23[2 * e], 0x05040100u);
-                rows[3][e] = __builtin_amdgcn_perm(p23[2 * e + 1], p23[2 * e], 0x07060302u);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int d = 4 * c4 + r;
-                *reinterpret_cast<u32x4 *>(&vtb[b * VT + d * VP + 8 * (k8 ^ vswz(d))]) = rows[r];
-            }
+            dequant16(vc[u], f16_of(vd[u]), e64, lo, hi);
+            *reinterpret_cast<u32x4 *>(&vtb[b * VT + kk * VP + 16 * c]) = lo;
+            *reinterpret_cast<u32x4 *>(&vtb[b * VT + kk * VP + 16 * c + 8]) = hi;
         }
     };
     if (tn > 0) {
         fetch(tb);
         stage(0);
-        if (tn > 1)
-            fetch(tb + 1);
     }
+    // Every load so far, the Q fragments included, is in before the loop
+    // starts (after stage(0) this waits for nothing).  Without it the
+    // compiler cannot tell on every path that the Q fragments have landed,
+    // and makes each step's first MFMAs wait for the prefetch issued just
+    // before them.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    if (tn > 1)
+        fetch(tb + 1);
     __syncthreads();
 
     f32x16 oacc[NDB];
@@ -278,8 +242,13 @@ __global__ __launch_bounds__(AT_NT, 1) void attn_q8kv_kernel(AttnArgs a)
     float mrow = -__builtin_inff(), lrow = 0.0f;   // running maximum (log2 scale) and sum
     const int qpos = off + qrow;
 
-    // K rows this lane reads for the A operand, and the LDS offsets
+    // K rows this lane reads for the A operand
     const int krow0 = pi_row(i), krow1 = 32 + pi_row(i);
+    // the V element this lane addresses in a transpose load: within each 16
+    // lanes, lane 4 r + c (r, c < 4) names row r, columns 4 c .. 4 c + 3 of a
+    // 4 x 16 block (rows 8 g .., columns 16 ((lane >> 4) & 1) ..), and gets
+    // back column lane & 15 of the block's four rows
+    const int vsrc = (8 * g + ((lane >> 2) & 3)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
     // both groups step together (one barrier per step); a group whose half
     // is one tile shorter idles through the last step
@@ -346,15 +315,30 @@ __global__ __launch_bounds__(AT_NT, 1) void attn_q8kv_kernel(AttnArgs a)
         // for the first queries) keeps maximum -inf: its P must be 0, not
         // exp2(-inf + inf)
         const float msub = mnew == -__builtin_inff() ? 0.0f : mnew;
-        float lsum = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], a.scale_log2, -msub));
-                sacc[kb][r] = p;
-                lsum += p;
+            for (int r = 0; r < 16; ++r)
+                sacc[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], a.scale_log2, -msub));
+        // P as fp16 B fragments: sub-step k takes registers 8 (k & 1) .. + 7 of block k >> 1
+        f16x8 pf[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                pf[k][e] = _Float16(sacc[k >> 1][8 * (k & 1) + e]);
+        // the row sum adds the fp16 P that the product uses, two at a time
+        // (v_dot2_f32_f16 against (1, 1), fp32 accumulation)
+        const f16x2 one2 = {_Float16(1.0f), _Float16(1.0f)};
+        float ls[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const f16x2 pp = {pf[k][2 * e], pf[k][2 * e + 1]};
+                ls[e & 1] = __builtin_amdgcn_fdot2(pp, one2, ls[e & 1], false);
             }
+        float lsum = ls[0] + ls[1];
         lsum += __shfl_xor(lsum, 32);
         if (__builtin_amdgcn_ballot_w64(moved) != 0) {   // some row's maximum moved: rescale
             // rows whose maximum stayed keep their scale (their mrow may still
@@ -370,22 +354,15 @@ __global__ __launch_bounds__(AT_NT, 1) void attn_q8kv_kernel(AttnArgs a)
         lrow += lsum;
         mrow = mnew;
 
-        // P as fp16 B fragments: sub-step k takes registers 8 (k & 1) .. + 7 of block k >> 1
-        f16x8 pf[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                pf[k][e] = _Float16(sacc[k >> 1][8 * (k & 1) + e]);
-
-        // O^T += V^T P^T
+        // O^T += V^T P^T; the A fragment of sub-step k, d block db is two
+        // transpose loads: keys 16 k + 8 g + 0..3 and + 4..7 of column 32 db + i
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-            const int d = 32 * db + i;
-            const _Float16 *vp = &vtb[b * VT + d * VP];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const f16x8 va = *reinterpret_cast<const f16x8 *>(vp + 8 * ((2 * k + g) ^ vswz(d)));
+                const _Float16 *vp = &vtb[b * VT + 16 * k * VP + 32 * db + vsrc];
+                const f16x4 v0 = lds_read_tr16(vp), v1 = lds_read_tr16(vp + 4 * VP);
+                const f16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[k], oacc[db], 0, 0, 0);
             }
         }
