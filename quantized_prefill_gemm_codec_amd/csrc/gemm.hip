@@ -435,7 +435,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
     }
     // scales: dword instruction j covers bytes [256 j, 256 j + 256) of the
     // stage's scale area: per matrix SPM bytes, SB per row group, then padding
-    uint32_t sv[SPW];
+    uint32_t sv[SPW], sk[SPW];
     int smat[SPW];
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
@@ -453,6 +453,9 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
         const uint32_t src = CODEC == Q4_K && o >= 128 ? uint32_t(o) - 128u + 512u : uint32_t(o);
         sv[u] = (j < NSI && b < S_BYTES && bm < RG * SB && rg0 + rg < a.groups) ? uint32_t(rg0 + rg) * pitch + src
                                                                                 : OOB;
+        // Q4_K: the lane records move by 128 bytes per k-step inside their
+        // 4-k-step record, the row records do not
+        sk[u] = CODEC == Q4_K && o < 128 ? 128u : 0u;
     }
 
     // Waves issue different numbers of DMA ops per stage (the code and scale
@@ -507,9 +510,8 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void gemm_dma_kernel(GemmArgs
                               : TERN          ? uint32_t(t >> 2) * 64u
                               : CODEC == Q4_K ? uint32_t(t >> 2) * 640u
                                               : uint32_t(t) * uint32_t(SB);
-            uint32_t v = in ? sv[u] : OOB;
-            if constexpr (CODEC == Q4_K)
-                v = (v != OOB && lane < 32) ? v + uint32_t(t & 3) * 128u : v;
+            // (an out-of-range offset stays out of range with the record step added)
+            const uint32_t v = in ? (CODEC == Q4_K ? sv[u] + uint32_t(t & 3) * sk[u] : sv[u]) : OOB;
             if (j < NSI)
                 dma_b32(smat[u] ? s1 : s0, v, so, base + S_OFF + uint32_t(j * 256));
         }
