@@ -266,18 +266,30 @@ __global__ __launch_bounds__(AT_NT, 1) void attn_q8kv_kernel(AttnArgs a)
 
         // S^T for keys 32 kb .. 32 kb + 31 of the tile
         f32x16 sacc[2];
+        f16x8 ka[2][NDD];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const _Float16 *kp = &ksb[b * KT + (kb ? krow1 : krow0) * KP + 8 * g];
+#pragma unroll
+            for (int dd = 0; dd < NDD; ++dd)
+                ka[kb][dd] = *reinterpret_cast<const f16x8 *>(kp + 16 * dd);
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 sacc[kb][e] = 0.0f;
-            const _Float16 *kp = &ksb[b * KT + (kb ? krow1 : krow0) * KP + 8 * g];
-#pragma unroll
-            for (int dd = 0; dd < NDD; ++dd) {
-                const f16x8 ka = *reinterpret_cast<const f16x8 *>(kp + 16 * dd);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[dd], sacc[kb], 0, 0, 0);
-            }
         }
+        // all K-fragment reads issued first, then the MFMAs, both blocks interleaved
+#pragma unroll
+        for (int dd = 0; dd < NDD; ++dd)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[kb][dd], qf[dd], sacc[kb], 0, 0, 0);
+        // keep every K-fragment read ahead of the MFMAs (the scheduler would
+        // otherwise keep two in flight)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDD, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDD, 0);
 
         // scores on the log2 scale; keys past the sequence or (causal) past
         // the query's own position are -inf.  Register 4 q + e of block kb
@@ -356,14 +368,38 @@ __global__ __launch_bounds__(AT_NT, 1) void attn_q8kv_kernel(AttnArgs a)
 
         // O^T += V^T P^T; the A fragment of sub-step k, d block db is two
         // transpose loads: keys 16 k + 8 g + 0..3 and + 4..7 of column 32 db + i
+        if constexpr (D == 128) {
+            // two d blocks at a time: their 16 transpose loads first, then their
+            // MFMAs (at D = 64 the extra registers cost more than the read-ahead gains)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+            for (int d2 = 0; d2 < NDB; d2 += 2) {
+                f16x8 va[2][4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const _Float16 *vp = &vtb[b * VT + 16 * k * VP + 32 * db + vsrc];
-                const f16x4 v0 = lds_read_tr16(vp), v1 = lds_read_tr16(vp + 4 * VP);
-                const f16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[k], oacc[db], 0, 0, 0);
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const _Float16 *vp = &vtb[b * VT + 16 * k * VP + 32 * (d2 + u) + vsrc];
+                        const f16x4 v0 = lds_read_tr16(vp), v1 = lds_read_tr16(vp + 4 * VP);
+                        va[u][k] = f16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                    }
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        oacc[d2 + u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[u][k], pf[k], oacc[d2 + u], 0, 0, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            }
+        } else {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const _Float16 *vp = &vtb[b * VT + 16 * k * VP + 32 * db + vsrc];
+                    const f16x4 v0 = lds_read_tr16(vp), v1 = lds_read_tr16(vp + 4 * VP);
+                    const f16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[k], oacc[db], 0, 0, 0);
+                }
             }
         }
       }
