@@ -151,6 +151,12 @@ __global__ __launch_bounds__(AT_NT, 1) void attn_q8kv_kernel(AttnArgs a)
     const int grp = wave >> 2, qw = wave & 3;         // key-range group, query sub-tile
     const int gtid = tid & (AT_GT - 1);
     const int i = lane & 31, g = lane >> 5;
+    // The SIMD's arbiter favours the older wave of a pair, so without this the
+    // second group (waves 4..7, one per SIMD beside a first-group wave) ran
+    // behind every step and the first waited for it at the barrier; issue
+    // priority for the second group balances the pairs.
+    if (grp == 1)
+        __builtin_amdgcn_s_setprio(3);
     _Float16 *const ksb = &tiles[grp][0];
     _Float16 *const vtb = &tiles[grp][2 * KT];
     int qt, h;
