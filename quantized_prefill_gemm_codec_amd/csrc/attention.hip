@@ -21,11 +21,12 @@
 //    fragments, loaded once).  K rows are read in the order pi below, which
 //    makes each lane's 32 scores exactly the B fragments P^T needs for the
 //    next product: no lane exchange between the two products;
-//  * online softmax in fp32 on the log2 scale: the row maximum and sum are
-//    lane-local over 32 scores plus one exchange with lane l ^ 32 (the other
-//    half of the same query's keys), the sum taken over P as rounded to fp16
-//    for the product, so that numerator and denominator use the same P; the
-//    running maximum, and with it the
+//  * online softmax in fp32 on the log2 scale: each lane holds 32 scores of
+//    its query, and lane l ^ 32 the other half of that query's keys.  The
+//    halves exchange maxima only in a step where the running maximum moves,
+//    and keep their own row sums (over P as rounded to fp16 for the product,
+//    so that numerator and denominator use the same P), added once at the
+//    end.  The running maximum, and with it the
 //    O accumulators (by 2^(m_old - m_new)), moves only when a tile's maximum
 //    exceeds it by more than RESCALE_SLACK;
 //  * O^T += V^T P^T (A = V^T, read out of the row-major V tile by the LDS
@@ -315,20 +316,33 @@ __global__ __launch_bounds__(AT_NT, 1) void attn_q8kv_kernel(AttnArgs a)
                         sacc[kb][r] = -__builtin_inff();
                 }
         }
+        {
+            // four independent chains: a short dependency path to the maximum
+            float mx[4] = {tmax, tmax, tmax, tmax};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                tmax = __builtin_fmaxf(tmax, sacc[kb][r]);
-        tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32)) * a.scale_log2;
+                for (int r = 0; r < 16; ++r)
+                    mx[r & 3] = __builtin_fmaxf(mx[r & 3], sacc[kb][r]);
+            tmax = __builtin_fmaxf(__builtin_fmaxf(mx[0], mx[1]), __builtin_fmaxf(mx[2], mx[3]));
+        }
+        tmax *= a.scale_log2;
         // The running maximum moves only when a score exceeds it by more than
         // 2^RESCALE_SLACK on the exp2 scale: until then P = 2^(s - m) stays at
         // most 2^8 (exact range for fp16 P, and the fp32 sums and accumulators
         // are unaffected), and the O accumulators need no rescale -- after the
-        // first tiles the maximum rarely moves that far.  Both lane halves of
-        // a row hold the same tmax and mrow, so they decide alike.
-        const bool moved = tmax > mrow + RESCALE_SLACK;
-        const float mnew = moved ? tmax : mrow;
+        // first tiles the maximum rarely moves that far.  Each lane half sees
+        // half of a row's keys: only when some lane's half-row maximum moves
+        // does the wave exchange the halves' maxima (lane l ^ 32), so that
+        // both halves of a row take the same new maximum; otherwise no lane
+        // exchange happens in the step.
+        bool moved = tmax > mrow + RESCALE_SLACK;
+        float mnew = mrow;
+        if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+            tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+            moved = tmax > mrow + RESCALE_SLACK;
+            mnew = moved ? tmax : mrow;
+        }
         // a row with no visible key yet (a whole half-range can be masked
         // for the first queries) keeps maximum -inf: its P must be 0, not
         // exp2(-inf + inf)
@@ -356,8 +370,7 @@ __global__ __launch_bounds__(AT_NT, 1) void attn_q8kv_kernel(AttnArgs a)
                 const f16x2 pp = {pf[k][2 * e], pf[k][2 * e + 1]};
                 ls[e & 1] = __builtin_amdgcn_fdot2(pp, one2, ls[e & 1], false);
             }
-        float lsum = ls[0] + ls[1];
-        lsum += __shfl_xor(lsum, 32);
+        const float lsum = ls[0] + ls[1];   // this lane half's share; the halves add up at the end
         if (__builtin_amdgcn_ballot_w64(moved) != 0) {   // some row's maximum moved: rescale
             // rows whose maximum stayed keep their scale (their mrow may still
             // be -inf, and -inf - -inf is NaN)
@@ -412,6 +425,7 @@ __global__ __launch_bounds__(AT_NT, 1) void attn_q8kv_kernel(AttnArgs a)
         __syncthreads();   // tile t's buffer is free; tile t + 1's is written
     }
 
+    lrow += __shfl_xor(lrow, 32);   // the row sum over both lane halves' keys
     // merge the halves: group 1 hands its O^T, maximum and sum to group 0
     f32x4 *mo = reinterpret_cast<f32x4 *>(&tiles[0][0]);                 // [4 qw][NDB][4 q][64 lanes]
     float *mm = reinterpret_cast<float *>(mo + 4 * NDB * 4 * 64);         // [2][4 qw][64 lanes]: maximum, sum
