@@ -265,11 +265,15 @@ __global__ __launch_bounds__(AT_NT, 1) void attn_q8kv_kernel(AttnArgs a)
         const int b = it & 1;
         // the tile after this one goes into the other buffer: its last
         // readers finished before the barrier that ended the previous step
-        if (it + 1 < tn) {
-            stage(b ^ 1);
-            if (it + 2 < tn)
-                fetch(t + 2);
-        }
+        auto stage_next = [&]() {
+            if (it + 1 < tn) {
+                stage(b ^ 1);
+                if (it + 2 < tn)
+                    fetch(t + 2);
+            }
+        };
+        if constexpr (D != 64)
+            stage_next();
 
         // S^T for keys 32 kb .. 32 kb + 31 of the tile
         f32x16 sacc[2];
@@ -280,6 +284,15 @@ __global__ __launch_bounds__(AT_NT, 1) void attn_q8kv_kernel(AttnArgs a)
 #pragma unroll
             for (int dd = 0; dd < NDD; ++dd)
                 ka[kb][dd] = *reinterpret_cast<const f16x8 *>(kp + 16 * dd);
+        }
+        if constexpr (D == 64) {
+            // at D = 64 the next tile is staged after this tile's K-fragment
+            // reads are issued, so that they do not queue behind the tile
+            // writes (at D = 128 that measured slower: the MFMAs then wait
+            // for the staging VALU)
+            __builtin_amdgcn_sched_barrier(0);
+            stage_next();
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -295,8 +308,10 @@ __global__ __launch_bounds__(AT_NT, 1) void attn_q8kv_kernel(AttnArgs a)
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[kb][dd], qf[dd], sacc[kb], 0, 0, 0);
         // keep every K-fragment read ahead of the MFMAs (the scheduler would
         // otherwise keep two in flight)
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDD, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDD, 0);
+        if constexpr (D != 64) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDD, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDD, 0);
+        }
 
         // scores on the log2 scale; keys past the sequence or (causal) past
         // the query's own position are -inf.  Register 4 q + e of block kb
