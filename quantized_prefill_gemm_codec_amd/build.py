@@ -11,6 +11,7 @@ import re
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
@@ -33,7 +34,12 @@ HIPCC_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", 
                f"-I{os.path.join(ROOT, 'include')}"]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Werror"]
 RESOURCES = os.path.join(BUILD, "kernel_resources.txt")
+ROUNDING = os.path.join(BUILD, "q4_k_rounding.txt")
 LDS_MAX = 160 * 1024   # bytes of LDS per compute unit on gfx950
+
+# Kernels that unpack Q4_K weights to fp16 (codec 6): the GEMM tiles and the
+# dequant kernel.  The GEMV dots raw codes and rounds no weight.
+Q4_K_UNPACK = re.compile(r"(gemm_dma_kernel|gemm_kernel|dequant_kernel)ILi6E")
 
 
 def hipcc() -> str:
@@ -96,6 +102,67 @@ def check_resources(kernels):
     return lines
 
 
+def llvm_tool(name: str) -> str:
+    """An LLVM tool of the ROCm toolchain that hipcc drives."""
+    roots = [os.environ.get("ROCM_PATH"), os.path.dirname(os.path.dirname(os.path.realpath(hipcc()))), "/opt/rocm"]
+    for root in roots:
+        if root:
+            cand = os.path.join(root, "lib", "llvm", "bin", name)
+            if os.path.exists(cand):
+                return cand
+    raise RuntimeError(f"{name} not found beside hipcc")
+
+
+def device_mnemonics(obj: str) -> dict:
+    """{kernel symbol: {mnemonic: count}} of the gfx950 code object inside a
+    host object built here (its offload bundle, disassembled)."""
+    with tempfile.TemporaryDirectory() as tmp:
+        fat, co = os.path.join(tmp, "fat.bin"), os.path.join(tmp, "dev.co")
+        _run([llvm_tool("llvm-objcopy"), f"--dump-section=.hip_fatbin={fat}", obj, os.path.join(tmp, "host.o")])
+        _run([llvm_tool("clang-offload-bundler"), "--unbundle", "--type=o", f"--input={fat}",
+              f"--targets=hipv4-amdgcn-amd-amdhsa--{ARCH}", f"--output={co}"])
+        text = _run([llvm_tool("llvm-objdump"), "-d", f"--mcpu={ARCH}", co]).stdout
+    return parse_disassembly(text)
+
+
+def parse_disassembly(text: str) -> dict:
+    funcs, cur = {}, None
+    for line in text.splitlines():
+        m = re.match(r"^[0-9a-f]+ <(\S+)>:", line)
+        if m:
+            cur = funcs.setdefault(m.group(1), {})
+            continue
+        if cur is not None and line[:1].isspace():
+            tok = line.split()
+            if tok and re.match(r"^[sv]_[a-z0-9_]+$", tok[0]):
+                cur[tok[0]] = cur.get(tok[0], 0) + 1
+    return funcs
+
+
+def check_single_rounding(funcs: dict):
+    """Q4_K weights are the correctly rounded fp16 value of d sc q - dmin m.
+    The unpack writes the fused multiply-add narrowed to fp16 in plain C and
+    relies on hipcc selecting v_fma_mixlo_f16 / v_fma_mixhi_f16, which round
+    the exact result once; a lowering through v_fma_mix_f32 and a separate
+    conversion would round twice.  Every Q4_K unpacking kernel must use the
+    former and not the latter; returns the table lines, raises RuntimeError
+    naming every kernel that breaks this (or if none is found)."""
+    names = sorted(n for n in funcs if Q4_K_UNPACK.search(n))
+    lines, bad = [], []
+    for raw, name in zip(names, _demangle(names)):
+        f = funcs[raw]
+        lo, hi = f.get("v_fma_mixlo_f16", 0), f.get("v_fma_mixhi_f16", 0)
+        wide = f.get("v_fma_mix_f32", 0) + f.get("v_mad_mix_f32", 0)
+        lines.append(f"{name}: v_fma_mixlo_f16={lo} v_fma_mixhi_f16={hi} v_fma_mix_f32={wide}")
+        if lo == 0 or hi == 0 or wide:
+            bad.append(lines[-1])
+    if not names:
+        raise RuntimeError("no Q4_K unpacking kernel found in the device code")
+    if bad:
+        raise RuntimeError("Q4_K kernels whose unpack may round twice:\n" + "\n".join(bad))
+    return lines
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link libqgemm.so; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
@@ -118,6 +185,12 @@ def build(verbose: bool = False) -> str:
     table = check_resources(kernels)
     with open(RESOURCES, "w") as f:
         f.write("\n".join(table) + "\n")
+    funcs = {}
+    for src in ("gemm.hip", "gemv.hip"):
+        funcs.update(device_mnemonics(os.path.join(BUILD, src + ".o")))
+    rounding = check_single_rounding(funcs)
+    with open(ROUNDING, "w") as f:
+        f.write("\n".join(rounding) + "\n")
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)

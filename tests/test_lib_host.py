@@ -407,6 +407,40 @@ def test_built_kernels_use_no_scratch():
     assert all(" scratch=0 spills=0 " in ln for ln in lines), [ln for ln in lines if " scratch=0 spills=0 " not in ln]
 
 
+def test_build_guard_rejects_q4_k_double_rounding():
+    """The build disassembles the device code and refuses a Q4_K unpacking
+    kernel whose fused multiply-add is narrowed to fp16 by a separate
+    conversion (two roundings) instead of v_fma_mixlo/hi_f16 (one)."""
+    from quantized_prefill_gemm_codec_amd import build as qbuild
+    name = "_ZN2qg12_GLOBAL__N_115gemm_dma_kernelILi6ELi64ELi64EEEvv"
+    once = (f"0000000000001000 <{name}>:\n\tv_fma_mixlo_f16 v1, v2, v3, v4 // 000000001000: D3A10001\n"
+            "\tv_fma_mixhi_f16 v1, v2, v3, v4\n\tv_mfma_f32_32x32x16_f16 v[0:15], v[1:4], v[5:8], v[0:15]\n"
+            "0000000000002000 <_ZN2qg12_GLOBAL__N_115gemm_dma_kernelILi1ELi64ELi64EEEvv>:\n\tv_pk_mul_f16 v1, v2, v3\n")
+    funcs = qbuild.parse_disassembly(once)
+    assert funcs[name] == {"v_fma_mixlo_f16": 1, "v_fma_mixhi_f16": 1, "v_mfma_f32_32x32x16_f16": 1}
+    assert len(qbuild.check_single_rounding(funcs)) == 1        # the Q4_0 kernel is not checked
+    twice = once.replace("v_fma_mixhi_f16 v1, v2, v3, v4", "v_fma_mix_f32 v5, v2, v3, v4\n\tv_cvt_pk_f16_f32 v1, v5, v6")
+    with pytest.raises(RuntimeError, match="may round twice"):
+        qbuild.check_single_rounding(qbuild.parse_disassembly(twice))
+    with pytest.raises(RuntimeError, match="no Q4_K"):
+        qbuild.check_single_rounding({})
+
+
+def test_built_q4_k_kernels_round_once():
+    """The table the last build wrote: every Q4_K unpacking kernel (the GEMM
+    tiles and the dequant kernel) narrows with v_fma_mixlo/hi_f16 only."""
+    from quantized_prefill_gemm_codec_amd import build as qbuild
+    if not os.path.exists(qbuild.ROUNDING):
+        pytest.skip("library not built in this tree")
+    lines = open(qbuild.ROUNDING).read().splitlines()
+    assert len(lines) >= 8
+    assert any("dequant_kernel" in ln for ln in lines)
+    for ln in lines:
+        counts = dict(kv.split("=") for kv in ln.rsplit(": ", 1)[1].split())
+        assert int(counts["v_fma_mixlo_f16"]) > 0 and int(counts["v_fma_mixhi_f16"]) > 0, ln
+        assert int(counts["v_fma_mix_f32"]) == 0, ln
+
+
 def test_pack_is_reentrant_across_threads():
     """The library keeps no state: the host repack called from many threads at
     once gives every caller the planes a lone call gives."""
