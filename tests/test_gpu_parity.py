@@ -136,6 +136,20 @@ def test_q4_k_single_rounding_through_kernels(torch):
         assert _same_value_bits(y, want.T[:m])
 
 
+def test_q4_k_single_rounding_through_the_wide_tile(torch):
+    """The same tie weights through the 128 x 512 prefill tile, which only a
+    grid of 256 or more tiles reaches: X is the identity repeated 16 times."""
+    n, k, reps = 4096, 256, 16
+    assert qg.qg_kernel_for("prefill", 6, reps * k, n, k) == "gemm_dma_kernel<6, 128, 512, 1, 8, 1, 0, 3, 1>"
+    canon = _q4_k_tie_weights(n, k)
+    want = oracle.dequant_f16_bits(6, canon, n, k).view(np.float16)
+    w = _weight(torch, 6, n, k, canon)
+    eye = torch.eye(k, dtype=torch.float16, device="cuda").repeat(reps, 1).contiguous()
+    y = qg.qgemm_prefill(w, eye).cpu().numpy()
+    for r in (0, 7, reps - 1):
+        assert _same_value_bits(y[r * k:(r + 1) * k], want.T)
+
+
 @pytest.mark.parametrize("codec", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_identity_probe_through_gemm(torch, codec):
     """X = I: every output is one product with 1.0, so Y = W^T exactly."""
